@@ -1,0 +1,213 @@
+"""Benchmark of the Orthros per-layer attention step on one MI355X.
+
+A step is one orthros_prefill call (base-stream sliding-window attention
+with the fused cache write, then the output copy's split-K global
+cross-attention and its merge) over the 128K-token, batch-2, 32/8-head
+workload, with every input already resident in HBM.  value = prefill
+tokens per second (B * T / time per step).  The decode step latency
+(batch 16, lengths U[8192, 131072], 1024 steps) is reported beside it.
+
+Timing: warm-up calls, then K calls bracketed by torch.cuda.synchronize()
+and HIP events on the stream the kernels run on.  The dominant kernel's
+roofline figure comes from HIP events around orthros_swa_prefill launches
+alone (the same kernel and launch configuration), against the algorithmic
+bytes of one launch.  The fp64 CPU oracle is timed on a bounded sample of
+the same workload on this machine's host cores (cpu_baseline).
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill|swa|xattn|decode|copy]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill attn tokens/s at 128K (SWA w=128 + 1 global query); decode us/step"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def swa_bytes(B, T, Hq, Hkv, d, es=2):
+    """Algorithmic HBM bytes of one orthros_swa_prefill launch: q read, o
+    written, k and v read once, the cache written once."""
+    return B * T * (2 * Hq + 4 * Hkv) * d * es
+
+
+def swa_flops(B, T, Hq, d, w):
+    """Algorithmic flops: 4 d per (query, admissible key) (QK^T and PV)."""
+    keys = sum(min(t + 1, w) for t in range(min(T, w))) + max(0, T - w) * w
+    return 4 * d * B * Hq * keys
+
+
+def xattn_bytes(B, pos_plus_1, Hkv, d, es=2):
+    """Algorithmic bytes of the copy's global read: K and V of keys [0, P]."""
+    return B * pos_plus_1 * Hkv * d * 2 * es
+
+
+def timed(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / 1e3, wall
+
+
+def cpu_baseline(cfg, x_dev, budget_rows=1024):
+    """The fp64 oracle on a bounded sample of the workload: SWA for
+    budget_rows consecutive tokens of sequence 0 (all heads) and the global
+    query of sequence 0 (all heads, all keys); the whole workload's time is
+    extrapolated from those rates."""
+    import torch
+
+    import oracle
+    B, T, Hq = cfg["batch"], cfg["T"], cfg["n_q_heads"]
+    w = cfg["window"]
+    nthreads = oracle.default_threads()
+    t0 = T // 2
+    lo = t0 - w + 1
+    sl = slice(lo, t0 + budget_rows)
+    q = x_dev["q"][:1, sl].cpu().contiguous()
+    k = x_dev["k"][:1, sl].cpu().contiguous()
+    v = x_dev["v"][:1, sl].cpu().contiguous()
+    a, b = x_dev["alpha"].cpu(), x_dev["beta"].cpu()
+    rows = torch.tensor([(0, t - lo, h) for t in range(t0, t0 + budget_rows) for h in range(Hq)])
+    s = time.perf_counter()
+    oracle.swa_rows(q, k, v, a, b, w, rows, nthreads=nthreads)
+    t_swa = (time.perf_counter() - s) / budget_rows            # seconds per token (all heads)
+    k1 = x_dev["k"][:1].cpu().contiguous()
+    v1 = x_dev["v"][:1].cpu().contiguous()
+    s = time.perf_counter()
+    oracle.prefill(None, x_dev["q_out"][:1].cpu().contiguous(), [T - 1], k1, v1, a, b,
+                   x_dev["alpha_out"].cpu(), x_dev["beta_out"].cpu(), w, swa=False, nthreads=nthreads)
+    t_glob = time.perf_counter() - s                              # seconds per sequence
+    total = t_swa * B * T + t_glob * B
+    return {"value": B * T / total, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"fp64 oracle, {nthreads} threads: Eq. (4) rows for {budget_rows} consecutive tokens x "
+                      f"{Hq} heads of sequence 0 ({t_swa * 1e3:.2f} ms/token) plus one sequence's global "
+                      f"query over all {T} keys ({t_glob:.2f} s), extrapolated to B={B} x T={T}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", default="all", choices=["all", "prefill", "swa", "xattn", "decode", "copy"])
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the Orthros layer here runs on a single MI355X with no "
+              "sharding or collectives; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from phase_aware_swa_amd import inputs
+    from phase_aware_swa_amd.runner import Decode, Prefill
+
+    torch.cuda.set_device(0)
+    out = {}
+
+    if args.only == "copy":
+        # plain copy kernel of known size: calibrates the FETCH_SIZE / WRITE_SIZE counters
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        sec, _ = timed(lambda: dst.copy_(src), args.steps, args.warmup)
+        print(json.dumps({"copy_bytes_each_way": n, "copy_GBps": 2 * n * args.steps / sec / 1e9}), flush=True)
+        return
+
+    cfg = dict(inputs.WORKLOADS["gqa_8b_prefill_128k"])
+    B, T, Hq, Hkv, d, w = (cfg[k] for k in ("batch", "T", "n_q_heads", "n_kv_heads", "head_dim", "window"))
+    result = None
+    if args.only in ("all", "prefill", "swa", "xattn"):
+        x = inputs.prefill_inputs(seed=2, device="cuda", **cfg)
+        run = Prefill(cfg, x)
+        run.run()
+        torch.cuda.synchronize()
+        if args.only in ("all", "prefill"):
+            sec, wall = timed(run.run, args.steps, args.warmup)
+            ms = sec / args.steps * 1e3
+            result = {"metric": METRIC, "value": B * T * args.steps / sec, "unit": "tokens/s", "n_gpus": 1,
+                      "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+                      "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "gqa_8b_prefill_128k", "global_batch": B, "seq_len": T,
+                                 "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d, "window": w,
+                                 "parallelism": "single-gpu"},
+                      "wall_s_timed": wall}
+        if args.only in ("all", "prefill", "swa"):
+            sec, _ = timed(run.run_swa, args.steps, args.warmup)
+            t_swa = sec / args.steps
+            nbytes = swa_bytes(B, T, Hq, Hkv, d)
+            fl = swa_flops(B, T, Hq, d, w)
+            out["swa"] = {"kernel": "orthros_swa_prefill", "us": t_swa * 1e6, "bytes": nbytes, "flops": fl,
+                          "GBps": nbytes / t_swa / 1e9, "TFLOPs": fl / t_swa / 1e12}
+        if args.only in ("all", "prefill", "xattn"):
+            sec, _ = timed(run.run_xattn, args.steps, args.warmup)
+            t_x = sec / args.steps
+            nbytes = xattn_bytes(B, T, Hkv, d)
+            out["xattn"] = {"kernel": "orthros_global_xattn", "us": t_x * 1e6, "bytes": nbytes,
+                            "GBps": nbytes / t_x / 1e9}
+        if result is not None and not args.no_cpu_baseline:
+            result["cpu_baseline"] = cpu_baseline(cfg, x)
+        del run, x
+        torch.cuda.empty_cache()
+
+    if args.only in ("all", "decode"):
+        dcfg = dict(inputs.WORKLOADS["gqa_8b_decode_b16"])
+        nsteps = args.decode_steps
+        dcfg["steps"] = nsteps
+        xd = inputs.decode_inputs(seed=4, device="cuda", **dcfg)
+        len0 = xd["cache_len"].clone()
+        hint = int(len0.max().item()) + nsteps - 1
+        dec = Decode(dcfg, xd["k_cache"], xd["v_cache"], xd["cache_len"], hint, xd["alpha"], xd["beta"],
+                     xd["alpha_out"], xd["beta_out"])
+
+        def one_pass():
+            dec.cache_len.copy_(len0)
+            for s in range(nsteps):
+                dec.step(xd["q"][s], xd["q_out"][s], xd["k_new"][s], xd["v_new"][s])
+
+        sec, _ = timed(one_pass, 2, 1)
+        us = sec / 2 / nsteps * 1e6
+        lens = len0.double()
+        step_bytes = float(((lens + nsteps / 2).sum() * Hkv * d * 2 * 2).item())   # mean history K+V per step
+        out["decode"] = {"workload": "gqa_8b_decode_b16", "us_per_step": us, "steps": nsteps,
+                         "bytes_per_step": step_bytes, "GBps": step_bytes / (us * 1e-6) / 1e9}
+        if result is None:
+            result = {"metric": METRIC, "value": us, "unit": "us/step", "n_gpus": 1, "steps": nsteps,
+                      "warmup": 1, "ms_per_step": us / 1e3, "higher_is_better": False, "scaling": "weak",
+                      "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "gqa_8b_decode_b16", "global_batch": 16,
+                                 "parallelism": "single-gpu"}}
+
+    if result is None:
+        result = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "data": "synthetic",
+                  "dtype": "bf16", "config": {"workload": "gqa_8b_prefill_128k"}}
+    if "swa" in out:
+        s = out["swa"]
+        result["roofline"] = {"bound": "hbm", "achieved": s["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": s["GBps"] / HBM_PEAK_GBS, "traffic": None,
+                              "kernel": "orthros_swa_prefill (swa_bf16_kernel)",
+                              "mfma_algorithmic_TFLOPs": s["TFLOPs"],
+                              "mfma_algorithmic_frac": s["TFLOPs"] / BF16_PEAK_TFLOPS}
+    if "decode" in out:
+        result["decode_us_per_step"] = out["decode"]["us_per_step"]
+    result["kernels"] = out
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

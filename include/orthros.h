@@ -1,0 +1,202 @@
+/*
+ * orthros.h -- C ABI of the MI355X (gfx950) Orthros attention library.
+ *
+ * One layer of Orthros phase-aware heterogeneous attention, as described in
+ * "Orthros:阶段感知异构注意力精读笔记" (close-reading notes of arXiv
+ * 2610.13735; cited below as [N]):
+ *
+ *   - base stream: causal sliding-window attention (window w, 128 in the
+ *     pages) over every base token, [N] §2.3 Eq. (4); it writes every
+ *     position's K/V into the layer's cache, [N] §2.1 and §2.6;
+ *   - output-only stream: full-history causal cross-attention over that
+ *     cache, only at positions that predict a token, masked by the copy's
+ *     original position, [N] §2.3 Eq. (5) and §2.4;
+ *   - both streams' queries come from one shared projection followed by a
+ *     per-stream elementwise scale-offset q * alpha + beta, [N] §2.2.
+ *
+ * Modes ([N] §2.5, mode table): prefill has T_in = T-1 base-only tokens and
+ * T_out = 1 copy (the last prompt position); decode processes one new base
+ * token and one copy per step, the copy reading the whole history.
+ *
+ * Conventions shared by every call
+ *   - Positions are 0-based: the window of base row t is
+ *     [max(0, t-w+1), t]; a copy at original position P reads keys [0, P].
+ *   - Query head h reads KV head h / (n_q_heads / n_kv_heads).
+ *   - Tensors are dense, row-major, in the layouts written next to each
+ *     argument; every tensor of one call is stored in desc->dtype
+ *     (alpha/beta included).  Arithmetic is fp32 (bf16 storage: bf16 MFMA
+ *     operands with fp32 accumulation).  Outputs are written in dtype,
+ *     rounded to nearest even.
+ *   - Pointers named as device pointers must be device memory of the
+ *     current HIP device and 16-byte aligned.  Host pointers are read
+ *     before the call returns.
+ *   - Ownership: the caller owns every buffer, including the KV cache, the
+ *     lengths and the workspace.  The library allocates nothing, frees
+ *     nothing and never synchronises: work is queued on `stream` (a
+ *     hipStream_t; NULL is the null stream) and the call returns.
+ *   - Outputs must not alias inputs; k_cache/v_cache must not alias k/v.
+ *   - Errors: arguments are validated on the host before anything is
+ *     queued; a negative status means nothing was launched.  ORTHROS_E_HIP
+ *     reports a failed launch; orthros_last_error() then holds the text.
+ *   - Thread safety: calls may be made from several host threads; the only
+ *     global state is the per-thread error text.
+ */
+#ifndef ORTHROS_H
+#define ORTHROS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORTHROS_ABI_VERSION 1
+
+typedef enum {
+    ORTHROS_OK = 0,
+    ORTHROS_E_NULL = -1,      /* a required pointer is NULL                    */
+    ORTHROS_E_SHAPE = -2,     /* unsupported or inconsistent sizes             */
+    ORTHROS_E_DTYPE = -3,     /* dtype not one of orthros_dtype                */
+    ORTHROS_E_POS = -4,       /* a copy position outside [0, T)                */
+    ORTHROS_E_CAPACITY = -5,  /* cache capacity too small for the call         */
+    ORTHROS_E_WORKSPACE = -6, /* workspace missing or smaller than required    */
+    ORTHROS_E_HIP = -7,       /* a HIP launch failed                           */
+    ORTHROS_E_ALIGN = -8      /* a device pointer is not 16-byte aligned       */
+} orthros_status;
+
+typedef enum { ORTHROS_F32 = 0, ORTHROS_BF16 = 1 } orthros_dtype;
+
+/* Problem description shared by every call.
+ *   batch          B >= 1 sequences
+ *   n_q_heads      Hq >= 1, a multiple of n_kv_heads
+ *   n_kv_heads     Hkv >= 1
+ *   head_dim       d: 64 or 128
+ *   window         w >= 1 keys in the base stream's window, itself included
+ *                  ([N] §2.3: W_t = {max(1, t-w+1), ..., t}; 128 in the pages)
+ *   softmax_scale  score scale; 0 means 1/sqrt(d)
+ *   dtype          orthros_dtype of every tensor of the call               */
+typedef struct {
+    int32_t batch, n_q_heads, n_kv_heads, head_dim, window;
+    float softmax_scale;
+    int32_t dtype;
+} orthros_desc;
+
+/* ------------------------------------------------------------- prefill */
+
+/* Workspace bytes orthros_prefill and orthros_global_xattn need for a
+ * prompt of T tokens (split-K partials of the copy's query).  0 on an
+ * invalid desc or T. */
+size_t orthros_prefill_workspace_size(const orthros_desc* desc, int64_t T);
+
+/*
+ * One layer's prefill ([N] §2.5, prefill row: T_in = T-1, T_out = 1):
+ * orthros_swa_prefill followed by orthros_global_xattn on the same stream.
+ *
+ *   T          prompt length per sequence, 1 <= T <= cap
+ *   q          device [B][T][Hq][d]   base-stream projected queries x W_Q
+ *   q_out      device [B][Hq][d]      each sequence's output copy, x' W_Q
+ *              (the copy Algorithm 2 appends at the tensor tail)
+ *   out_pos    host   [B]             original position of each copy,
+ *              0 <= out_pos[b] < T (T-1 for a plain prefill)
+ *   k, v       device [B][T][Hkv][d]  this layer's base K/V
+ *   alpha, beta          device [Hq][d]  base-stream scale-offset
+ *   alpha_out, beta_out  device [Hq][d]  output-stream scale-offset
+ *   k_cache, v_cache     device [B][Hkv][cap][d]; slots [0, T) are written,
+ *              every other slot is left untouched
+ *   o          device [B][T][Hq][d]   Eq. (4) for every base row
+ *   o_out      device [B][Hq][d]      Eq. (5) for each copy
+ *   workspace  device, >= orthros_prefill_workspace_size(desc, T) bytes
+ */
+orthros_status orthros_prefill(const orthros_desc* desc, int64_t T,
+                               const void* q, const void* q_out, const int64_t* out_pos,
+                               const void* k, const void* v,
+                               const void* alpha, const void* beta,
+                               const void* alpha_out, const void* beta_out,
+                               void* k_cache, void* v_cache, int64_t cap,
+                               void* o, void* o_out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Base stream of a prefill ([N] §2.3 Eq. (4); cache write [N] §2.1, §2.6):
+ * banded sliding-window attention for every base row t of every sequence
+ * and head, and the copy of k, v into cache slots [0, T).  Arguments as in
+ * orthros_prefill.  Needs no workspace.
+ */
+orthros_status orthros_swa_prefill(const orthros_desc* desc, int64_t T,
+                                   const void* q, const void* k, const void* v,
+                                   const void* alpha, const void* beta,
+                                   void* k_cache, void* v_cache, int64_t cap,
+                                   void* o, void* stream);
+
+/*
+ * Output stream of a prefill ([N] §2.3 Eq. (5), §2.4): each sequence's copy
+ * query, scale-offset by alpha_out/beta_out, attends over cache slots
+ * [0, out_pos[b]] (its original position; 0 <= out_pos[b] < T).  Split-K
+ * over the cache, then a log-sum-exp merge in a fixed order (results are
+ * run-to-run identical).  The cache must already hold slots [0, T) (stream
+ * order after orthros_swa_prefill suffices).  Arguments as in
+ * orthros_prefill.
+ */
+orthros_status orthros_global_xattn(const orthros_desc* desc, int64_t T,
+                                    const void* q_out, const int64_t* out_pos,
+                                    const void* alpha_out, const void* beta_out,
+                                    const void* k_cache, const void* v_cache, int64_t cap,
+                                    void* o_out,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* -------------------------------------------------------------- decode */
+
+/* Workspace bytes orthros_decode_step needs when every cache length is at
+ * most max_len.  0 on an invalid desc or max_len. */
+size_t orthros_decode_workspace_size(const orthros_desc* desc, int64_t max_len);
+
+/*
+ * One decode step of one layer ([N] §2.5, decode row; §2.4 walk-through):
+ * for each sequence b with L = cache_len[b] (read on the device):
+ *   - the new base token's k_new[b], v_new[b] are written to cache slot L;
+ *   - its query q[b] attends over slots [max(0, L-w+1), L] -> o[b];
+ *   - its output copy q_out[b] attends over slots [0, L] (the whole
+ *     history, the new token included) -> o_out[b];
+ *   - cache_len[b] becomes L + 1.
+ *
+ *   q, q_out          device [B][Hq][d]   projected queries of the token and its copy
+ *   k_new, v_new      device [B][Hkv][d]
+ *   alpha..beta_out   device [Hq][d]
+ *   k_cache, v_cache  device [B][Hkv][cap][d]
+ *   cache_len         device int32 [B], lengths before the step; updated in stream order
+ *   max_len_hint      host: an upper bound of every cache_len[b]; sizes the
+ *                     grid; needs max_len_hint + 1 <= cap
+ *   o, o_out          device [B][Hq][d]
+ *   workspace         device, >= orthros_decode_workspace_size(desc, max_len_hint) bytes
+ *
+ * A sequence whose cache_len[b] is negative or above max_len_hint is not
+ * touched (no cache write, no length update) and gets NaN in o[b] and
+ * o_out[b].  Successive steps may be queued back to back with no host
+ * synchronisation; a step's workspace must not be shared with a step that
+ * can run concurrently.
+ */
+orthros_status orthros_decode_step(const orthros_desc* desc,
+                                   const void* q, const void* q_out,
+                                   const void* k_new, const void* v_new,
+                                   const void* alpha, const void* beta,
+                                   const void* alpha_out, const void* beta_out,
+                                   void* k_cache, void* v_cache, int64_t cap,
+                                   int32_t* cache_len, int64_t max_len_hint,
+                                   void* o, void* o_out,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------ utilities */
+
+/* Static text naming a status code. */
+const char* orthros_status_str(int status);
+/* Text of the last error on the calling thread ("" when none). */
+const char* orthros_last_error(void);
+/* ORTHROS_ABI_VERSION of the built library. */
+int orthros_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ORTHROS_H */

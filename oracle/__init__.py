@@ -94,17 +94,19 @@ def make_shape(batch, n_q_heads, n_kv_heads, head_dim, window, dtype, softmax_sc
 def prefill(q, q_out, out_pos, k, v, alpha, beta, alpha_out, beta_out, window,
             softmax_scale=None, k_cache=None, v_cache=None, cap=None,
             swa=True, glob=True, nthreads=None):
-    """One prefill call.  q [B,T,Hq,d], q_out [B,Hq,d], out_pos: ints [B].
+    """One prefill call.  q [B,T,Hq,d] (may be None when swa is False),
+    q_out [B,Hq,d], k/v [B,T,Hkv,d], out_pos: ints [B].
 
     k_cache / v_cache ([B,Hkv,cap,d], storage dtype) are updated in place
     when given, else created zero-filled.  Returns dict(o, o_out, k_cache,
     v_cache); o / o_out are None when swa / glob is False.
     """
-    B, T, Hq, d = q.shape
-    Hkv = k.shape[2]
-    dt = q.dtype
+    B, T, Hkv, d = k.shape
+    Hq = q_out.shape[1]
+    dt = k.dtype
+    assert q is not None or not swa, "q is needed for the base stream"
     for t in (q, q_out, k, v, alpha, beta, alpha_out, beta_out):
-        assert t.dtype == dt, "one storage type per call"
+        assert t is None or t.dtype == dt, "one storage type per call"
     cap = cap or (k_cache.shape[2] if k_cache is not None else T)
     if k_cache is None:
         k_cache = torch.zeros(B, Hkv, cap, d, dtype=dt)

@@ -1,0 +1,320 @@
+// api.hip -- the C ABI of include/orthros.h: argument validation, workspace
+// sizing, split-size choice and kernel launches.  Host code only.
+//
+// Every argument is checked before the first launch, so a negative status
+// always means that nothing was queued.  The library allocates nothing and
+// never synchronises; all work goes to the caller's stream.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <initializer_list>
+#include <string>
+
+#include "kernels.h"
+#include "orthros.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+orthros_status fail(orthros_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+orthros_status fail(orthros_status st, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+constexpr int64_t kMaxElems = int64_t(1) << 50;   // keeps every byte offset far from overflow
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+orthros_status check_desc(const orthros_desc* d)
+{
+    if (!d) return fail(ORTHROS_E_NULL, "desc is NULL");
+    if (d->dtype != ORTHROS_F32 && d->dtype != ORTHROS_BF16)
+        return fail(ORTHROS_E_DTYPE, "dtype %d is neither ORTHROS_F32 nor ORTHROS_BF16", d->dtype);
+    if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1)
+        return fail(ORTHROS_E_SHAPE, "batch, n_q_heads and n_kv_heads must be >= 1");
+    if (d->n_q_heads % d->n_kv_heads)
+        return fail(ORTHROS_E_SHAPE, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", d->n_q_heads,
+                    d->n_kv_heads);
+    if (d->n_q_heads > 65535 || d->batch > 65535)
+        return fail(ORTHROS_E_SHAPE, "batch and n_q_heads must be <= 65535");
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(ORTHROS_E_SHAPE, "head_dim %d unsupported (64 or 128)", d->head_dim);
+    if (d->window < 1) return fail(ORTHROS_E_SHAPE, "window must be >= 1");
+    if (!(d->softmax_scale >= 0.f) || std::isinf(d->softmax_scale))
+        return fail(ORTHROS_E_SHAPE, "softmax_scale must be finite and >= 0");
+    return ORTHROS_OK;
+}
+
+float qscale_of(const orthros_desc* d)
+{
+    const float s = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt((float)d->head_dim);
+    return s * 1.4426950408889634f;   // scores go to exp2: fold log2(e) into the query
+}
+
+// Smallest power-of-two key chunk >= 256 that keeps about `target` workgroups.
+int pick_chunk(int64_t keys, int64_t streams, int64_t target)
+{
+    const int64_t want = (keys * streams + target - 1) / target;
+    int64_t c = 256;
+    while (c < want && c < (int64_t(1) << 24)) c <<= 1;
+    return (int)c;
+}
+
+int64_t streams_of(const orthros_desc* d)
+{
+    const int G = d->n_q_heads / d->n_kv_heads;
+    return (int64_t)d->batch * d->n_kv_heads * (G / orthros::xattn_heads_per_wg(G));
+}
+
+constexpr int64_t kPrefillTargetWgs = 2048;
+constexpr int64_t kDecodeTargetWgs = 8192;
+constexpr size_t kLenBytesAlign = 256;
+
+size_t len_bytes(const orthros_desc* d)
+{
+    return ((size_t)d->batch * 4 + kLenBytesAlign - 1) / kLenBytesAlign * kLenBytesAlign;
+}
+
+struct Split { int chunk, n_split; size_t bytes; };
+
+Split prefill_split(const orthros_desc* d, int64_t T)
+{
+    Split s;
+    s.chunk = pick_chunk(T, streams_of(d), kPrefillTargetWgs);
+    s.n_split = (int)((T + s.chunk - 1) / s.chunk);
+    s.bytes = len_bytes(d) + (size_t)d->batch * d->n_q_heads * s.n_split * (d->head_dim + 2) * 4;
+    return s;
+}
+
+Split decode_split(const orthros_desc* d, int64_t max_len)
+{
+    Split s;
+    const int64_t keys = max_len + 1;
+    s.chunk = pick_chunk(keys, streams_of(d), kDecodeTargetWgs);
+    s.n_split = (int)((keys + s.chunk - 1) / s.chunk);
+    s.bytes = len_bytes(d) + (size_t)d->batch * d->n_q_heads * 2 * s.n_split * (d->head_dim + 2) * 4;
+    return s;
+}
+
+orthros_status check_T(const orthros_desc* d, int64_t T, int64_t cap)
+{
+    if (T < 1 || T > INT32_MAX) return fail(ORTHROS_E_SHAPE, "T = %lld outside [1, 2^31)", (long long)T);
+    if (cap < T) return fail(ORTHROS_E_CAPACITY, "cap %lld < T %lld", (long long)cap, (long long)T);
+    const int64_t rowq = (int64_t)d->n_q_heads * d->head_dim;
+    if ((int64_t)d->batch * cap > kMaxElems / rowq || (int64_t)d->batch * T > kMaxElems / rowq)
+        return fail(ORTHROS_E_SHAPE, "tensor sizes overflow the library's 2^50-element bound");
+    // bf16 SWA grid: B * Hkv * (G / HS) * ceil(T / TQ) workgroups of 256 threads, TQ >= 32
+    if ((int64_t)d->batch * d->n_q_heads * ((T + 31) / 32) >= (int64_t(1) << 24))
+        return fail(ORTHROS_E_SHAPE, "batch * n_q_heads * T / 32 exceeds the launch grid limit");
+    return ORTHROS_OK;
+}
+
+orthros_status check_ptrs(std::initializer_list<const void*> ps)
+{
+    for (const void* p : ps) {
+        if (!p) return fail(ORTHROS_E_NULL, "a required pointer is NULL");
+        if (!aligned16(p)) return fail(ORTHROS_E_ALIGN, "a device pointer is not 16-byte aligned");
+    }
+    return ORTHROS_OK;
+}
+
+orthros_status hip_status(hipError_t e, const char* what)
+{
+    if (e == hipSuccess) return ORTHROS_OK;
+    return fail(ORTHROS_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+orthros_status validate_swa(const orthros_desc* d, int64_t T, const void* q, const void* k, const void* v,
+                            const void* alpha, const void* beta, const void* k_cache, const void* v_cache,
+                            int64_t cap, const void* o)
+{
+    orthros_status st = check_desc(d);
+    if (st) return st;
+    if ((st = check_T(d, T, cap))) return st;
+    return check_ptrs({q, k, v, alpha, beta, k_cache, v_cache, o});
+}
+
+orthros_status validate_xattn(const orthros_desc* d, int64_t T, const void* q_out, const int64_t* out_pos,
+                              const void* alpha_out, const void* beta_out, const void* k_cache,
+                              const void* v_cache, int64_t cap, const void* o_out, const void* ws,
+                              size_t ws_bytes)
+{
+    orthros_status st = check_desc(d);
+    if (st) return st;
+    if ((st = check_T(d, T, cap))) return st;
+    if (!out_pos) return fail(ORTHROS_E_NULL, "out_pos is NULL");
+    for (int b = 0; b < d->batch; ++b)
+        if (out_pos[b] < 0 || out_pos[b] >= T)
+            return fail(ORTHROS_E_POS, "out_pos[%d] = %lld outside [0, T=%lld)", b, (long long)out_pos[b],
+                        (long long)T);
+    if ((st = check_ptrs({q_out, alpha_out, beta_out, k_cache, v_cache, o_out}))) return st;
+    if (!ws) return fail(ORTHROS_E_WORKSPACE, "workspace is NULL");
+    if ((st = check_ptrs({ws}))) return st;
+    const Split sp = prefill_split(d, T);
+    if (ws_bytes < sp.bytes)
+        return fail(ORTHROS_E_WORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, sp.bytes);
+    return ORTHROS_OK;
+}
+
+orthros_status run_swa(const orthros_desc* d, int64_t T, const void* q, const void* k, const void* v,
+                       const void* alpha, const void* beta, void* k_cache, void* v_cache, int64_t cap, void* o,
+                       hipStream_t s)
+{
+    orthros::SwaParams p;
+    p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
+    p.k_cache = k_cache; p.v_cache = v_cache; p.o = o;
+    p.T = T; p.cap = cap;
+    p.B = d->batch; p.Hq = d->n_q_heads; p.Hkv = d->n_kv_heads; p.D = d->head_dim; p.window = d->window;
+    p.qscale = qscale_of(d);
+    p.dt = d->dtype == ORTHROS_F32 ? orthros::Dt::F32 : orthros::Dt::BF16;
+    return hip_status(orthros::launch_swa(p, s), "sliding-window kernel launch");
+}
+
+orthros_status run_xattn(const orthros_desc* d, int64_t T, const void* q_out, const int64_t* out_pos,
+                         const void* alpha_out, const void* beta_out, const void* k_cache, const void* v_cache,
+                         int64_t cap, void* o_out, void* ws, hipStream_t s)
+{
+    const Split sp = prefill_split(d, T);
+    orthros::XattnParams p;
+    p.q_out = q_out; p.alpha_out = alpha_out; p.beta_out = beta_out;
+    p.k_cache = k_cache; p.v_cache = v_cache; p.o_out = o_out;
+    p.ws_len = (int32_t*)ws;
+    p.ws_part = (float*)((char*)ws + len_bytes(d));
+    p.pos = out_pos;
+    p.cap = cap;
+    p.B = d->batch; p.Hq = d->n_q_heads; p.Hkv = d->n_kv_heads; p.D = d->head_dim;
+    p.chunk = sp.chunk; p.n_split = sp.n_split;
+    p.qscale = qscale_of(d);
+    p.dt = d->dtype == ORTHROS_F32 ? orthros::Dt::F32 : orthros::Dt::BF16;
+    return hip_status(orthros::launch_xattn(p, s), "cross-attention kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t orthros_prefill_workspace_size(const orthros_desc* desc, int64_t T)
+{
+    if (check_desc(desc) || T < 1 || T > INT32_MAX) return 0;
+    return prefill_split(desc, T).bytes;
+}
+
+size_t orthros_decode_workspace_size(const orthros_desc* desc, int64_t max_len)
+{
+    if (check_desc(desc) || max_len < 0 || max_len >= INT32_MAX) return 0;
+    return decode_split(desc, max_len).bytes;
+}
+
+orthros_status orthros_swa_prefill(const orthros_desc* desc, int64_t T, const void* q, const void* k,
+                                   const void* v, const void* alpha, const void* beta, void* k_cache,
+                                   void* v_cache, int64_t cap, void* o, void* stream)
+{
+    g_err.clear();
+    orthros_status st = validate_swa(desc, T, q, k, v, alpha, beta, k_cache, v_cache, cap, o);
+    if (st) return st;
+    return run_swa(desc, T, q, k, v, alpha, beta, k_cache, v_cache, cap, o, (hipStream_t)stream);
+}
+
+orthros_status orthros_global_xattn(const orthros_desc* desc, int64_t T, const void* q_out,
+                                    const int64_t* out_pos, const void* alpha_out, const void* beta_out,
+                                    const void* k_cache, const void* v_cache, int64_t cap, void* o_out,
+                                    void* workspace, size_t workspace_bytes, void* stream)
+{
+    g_err.clear();
+    orthros_status st = validate_xattn(desc, T, q_out, out_pos, alpha_out, beta_out, k_cache, v_cache, cap,
+                                       o_out, workspace, workspace_bytes);
+    if (st) return st;
+    return run_xattn(desc, T, q_out, out_pos, alpha_out, beta_out, k_cache, v_cache, cap, o_out, workspace,
+                     (hipStream_t)stream);
+}
+
+orthros_status orthros_prefill(const orthros_desc* desc, int64_t T, const void* q, const void* q_out,
+                               const int64_t* out_pos, const void* k, const void* v, const void* alpha,
+                               const void* beta, const void* alpha_out, const void* beta_out, void* k_cache,
+                               void* v_cache, int64_t cap, void* o, void* o_out, void* workspace,
+                               size_t workspace_bytes, void* stream)
+{
+    g_err.clear();
+    orthros_status st = validate_swa(desc, T, q, k, v, alpha, beta, k_cache, v_cache, cap, o);
+    if (st) return st;
+    st = validate_xattn(desc, T, q_out, out_pos, alpha_out, beta_out, k_cache, v_cache, cap, o_out, workspace,
+                        workspace_bytes);
+    if (st) return st;
+    st = run_swa(desc, T, q, k, v, alpha, beta, k_cache, v_cache, cap, o, (hipStream_t)stream);
+    if (st) return st;
+    return run_xattn(desc, T, q_out, out_pos, alpha_out, beta_out, k_cache, v_cache, cap, o_out, workspace,
+                     (hipStream_t)stream);
+}
+
+orthros_status orthros_decode_step(const orthros_desc* desc, const void* q, const void* q_out,
+                                   const void* k_new, const void* v_new, const void* alpha, const void* beta,
+                                   const void* alpha_out, const void* beta_out, void* k_cache, void* v_cache,
+                                   int64_t cap, int32_t* cache_len, int64_t max_len_hint, void* o, void* o_out,
+                                   void* workspace, size_t workspace_bytes, void* stream)
+{
+    g_err.clear();
+    orthros_status st = check_desc(desc);
+    if (st) return st;
+    if (max_len_hint < 0 || max_len_hint >= INT32_MAX)
+        return fail(ORTHROS_E_SHAPE, "max_len_hint %lld outside [0, 2^31 - 1)", (long long)max_len_hint);
+    if (cap < max_len_hint + 1)
+        return fail(ORTHROS_E_CAPACITY, "cap %lld < max_len_hint + 1 = %lld", (long long)cap,
+                    (long long)max_len_hint + 1);
+    const int64_t rowq = (int64_t)desc->n_q_heads * desc->head_dim;
+    if ((int64_t)desc->batch * cap > kMaxElems / rowq)
+        return fail(ORTHROS_E_SHAPE, "cache size overflows the library's 2^50-element bound");
+    if (!workspace) return fail(ORTHROS_E_WORKSPACE, "workspace is NULL");
+    if ((st = check_ptrs({q, q_out, k_new, v_new, alpha, beta, alpha_out, beta_out, k_cache, v_cache,
+                          cache_len, o, o_out, workspace})))
+        return st;
+    const Split sp = decode_split(desc, max_len_hint);
+    if (workspace_bytes < sp.bytes)
+        return fail(ORTHROS_E_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, sp.bytes);
+
+    orthros::DecodeParams p;
+    p.q = q; p.q_out = q_out; p.k_new = k_new; p.v_new = v_new;
+    p.alpha = alpha; p.beta = beta; p.alpha_out = alpha_out; p.beta_out = beta_out;
+    p.k_cache = k_cache; p.v_cache = v_cache; p.cache_len = cache_len; p.o = o; p.o_out = o_out;
+    p.ws_len = (int32_t*)workspace;
+    p.ws_part = (float*)((char*)workspace + len_bytes(desc));
+    p.cap = cap; p.max_len = max_len_hint;
+    p.B = desc->batch; p.Hq = desc->n_q_heads; p.Hkv = desc->n_kv_heads; p.D = desc->head_dim;
+    p.window = desc->window;
+    p.chunk = sp.chunk; p.n_split = sp.n_split;
+    p.qscale = qscale_of(desc);
+    p.dt = desc->dtype == ORTHROS_F32 ? orthros::Dt::F32 : orthros::Dt::BF16;
+    return hip_status(orthros::launch_decode(p, (hipStream_t)stream), "decode kernel launch");
+}
+
+const char* orthros_status_str(int status)
+{
+    switch (status) {
+    case ORTHROS_OK: return "ORTHROS_OK";
+    case ORTHROS_E_NULL: return "ORTHROS_E_NULL";
+    case ORTHROS_E_SHAPE: return "ORTHROS_E_SHAPE";
+    case ORTHROS_E_DTYPE: return "ORTHROS_E_DTYPE";
+    case ORTHROS_E_POS: return "ORTHROS_E_POS";
+    case ORTHROS_E_CAPACITY: return "ORTHROS_E_CAPACITY";
+    case ORTHROS_E_WORKSPACE: return "ORTHROS_E_WORKSPACE";
+    case ORTHROS_E_HIP: return "ORTHROS_E_HIP";
+    case ORTHROS_E_ALIGN: return "ORTHROS_E_ALIGN";
+    default: return "ORTHROS_E_UNKNOWN";
+    }
+}
+
+const char* orthros_last_error(void) { return g_err.c_str(); }
+
+int orthros_abi_version(void) { return ORTHROS_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// device.h -- small gfx950 device helpers shared by the library's kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace orthros {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+// Finite "minus infinity" for running maxima: exp2(x - kNegBig) never
+// produces NaN, and exp2(kNegBig - m) underflows to 0 for any real m.
+constexpr float kNegBig = -1.0e30f;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16)
+{
+    return __uint_as_float(bits16 << 16);
+}
+
+// Low / high bf16 of a packed 32-bit pair, as fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 with round-to-nearest-even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// DPP lane movement inside a row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- 7-i inside each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <- 15-i inside each 16 lanes
+
+// Sum over aligned groups of N lanes (N = 8 or 16); every lane of a group
+// ends with the same bits (each step adds a pair in both orders, and fp32
+// addition is commutative).
+template <int N>
+__device__ __forceinline__ float group_sum(float x)
+{
+    x += dpp_mov<kDppXor1>(x);
+    x += dpp_mov<kDppXor2>(x);
+    x += dpp_mov<kDppHalfMirror>(x);
+    if constexpr (N == 16) x += dpp_mov<kDppMirror>(x);
+    return x;
+}
+
+// Maps a launch-order workgroup id to a logical id so that the round-robin
+// dispatch over the 8 XCDs hands each XCD one contiguous run of logical ids
+// (neighbouring tiles then share that XCD's L2).  Ids past the last whole
+// multiple of 8 keep their order.
+__device__ __forceinline__ int64_t xcd_contiguous_id(int64_t i, int64_t n)
+{
+    int64_t n8 = n - (n & 7);
+    if (i >= n8) return i;
+    return (i & 7) * (n8 >> 3) + (i >> 3);
+}
+
+}  // namespace orthros

@@ -1,0 +1,377 @@
+// global_xattn.hip -- the output-only stream's full-history causal
+// cross-attention (prefill and decode) and the decode step, for gfx950.
+//
+// "Orthros:阶段感知异构注意力精读笔记" §2.3 Eq. (5): the output copy at
+// original position P attends over every cached key j <= P (§2.4: the mask
+// follows the original position, never the copy's slot at the tensor tail).
+// Its query is q_out * alpha_out + beta_out (§2.2).  In decode (§2.5 decode
+// row, §2.4 walk-through) the step also appends the new base token's K/V at
+// slot L = cache_len[b], runs the base token's window [L-w+1, L], and the
+// copy reads [0, L], the new token included.
+//
+// One query per (sequence, head) over up to a million keys is a
+// memory-bound stream (about 2 flop per cache byte per head), so the work is
+// split along the keys (split-K):
+//   - a workgroup owns one key chunk of one KV head and serves the HG query
+//     heads of that group at once, so each K/V byte is read from HBM once;
+//   - inside a wave, D/8 lanes hold one key row (8 head-dim values each, a
+//     16-byte load), so a wave reads 4 (d=128) or 8 (d=64) whole 256-byte or
+//     128-byte rows per load instruction; the dot product is finished with
+//     DPP row moves (no LDS);
+//   - each lane keeps an fp32 online-softmax state per head for the keys
+//     it saw; the states of a workgroup are merged by lane shuffles, then
+//     through LDS, into one (max, sum, unnormalised output) partial per head;
+//   - a second kernel merges the partials of a (sequence, head) by
+//     log-sum-exp in a fixed split order, so results are run-to-run
+//     identical.
+// The decode step uses the same chunk worker for the copy (range [0, L])
+// and the base token (range [L-w+1, L]); the new token's key L is read from
+// k_new/v_new, never from the cache slot the same launch is writing.
+
+#include "device.h"
+#include "kernels.h"
+
+namespace orthros {
+namespace {
+
+constexpr int kUnroll = 4;   // key rows per lane per softmax update
+
+// 8 consecutive head-dim values of one row, kept in storage form until used.
+template <typename E> struct Row8;
+template <> struct Row8<uint16_t> {
+    u32x4 w;
+    __device__ void zero() { w = u32x4{0u, 0u, 0u, 0u}; }
+    __device__ void load(const uint16_t* p) { w = *(const u32x4*)p; }
+    __device__ float operator[](int e) const { return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]); }
+};
+template <> struct Row8<float> {
+    float4 a, b;
+    __device__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ void load(const float* p) { a = *(const float4*)p; b = *(const float4*)(p + 4); }
+    __device__ float operator[](int e) const
+    {
+        const float4& x = e < 4 ? a : b;
+        switch (e & 3) { case 0: return x.x; case 1: return x.y; case 2: return x.z; default: return x.w; }
+    }
+};
+
+__device__ __forceinline__ float ld_elem(const uint16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+__device__ __forceinline__ float ld_elem(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ void st_elem(uint16_t* p, int64_t i, float x) { p[i] = (uint16_t)f32_to_bf16_bits(x); }
+__device__ __forceinline__ void st_elem(float* p, int64_t i, float x) { p[i] = x; }
+
+// Scale-offset queries of HG heads into LDS: qs[hh][d] = (q*alpha+beta)*qscale.
+template <typename E, int D, int HG>
+__device__ __forceinline__ void load_queries(float (*qs)[D], const E* q, const E* alpha, const E* beta,
+                             int64_t qrow0, int h0, float qscale)
+{
+    for (int idx = threadIdx.x; idx < HG * D; idx += blockDim.x) {
+        const int hh = idx / D, d = idx % D;
+        const int64_t hd = (int64_t)(h0 + hh) * D + d;
+        qs[hh][d] = (ld_elem(q, qrow0 + hd) * ld_elem(alpha, hd) + ld_elem(beta, hd)) * qscale;
+    }
+}
+
+// Online softmax over keys [lo, hi] of one KV head for HG queries; writes
+// one partial (max, sum, sum of weighted values) per query head to
+// out[hh * out_stride + {0, 1, 2 + d}].  Key rows start at kc + j * D; key
+// `lnew` (if >= 0) is read from knew/vnew instead.  256 threads.
+template <typename E, int D, int HG>
+__device__ __forceinline__ void attend_chunk(const float (*qs)[D], const E* kc, const E* vc,
+                             int64_t lnew, const E* knew, const E* vnew,
+                             int64_t lo, int64_t hi, float (*red)[HG][D + 2],
+                             float* out, int64_t out_stride)
+{
+    constexpr int LPK = D / 8;        // lanes per key row
+    constexpr int KPW = 64 / LPK;     // key rows per wave per step
+    constexpr int KPS = 4 * KPW;      // key rows per workgroup per step
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int c = lane % LPK, kg = lane / LPK;
+
+    float qr[HG][8];
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qr[hh][e] = qs[hh][8 * c + e];
+
+    float m[HG], l[HG], acc[HG][8];
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+        m[hh] = kNegBig;
+        l[hh] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+    }
+
+    for (int64_t base = lo; base <= hi; base += (int64_t)KPS * kUnroll) {
+        Row8<E> kx[kUnroll], vx[kUnroll];
+        bool ok[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t j = base + (int64_t)u * KPS + wv * KPW + kg;
+            ok[u] = j <= hi;
+            kx[u].zero();
+            vx[u].zero();
+            if (ok[u]) {
+                const E* kr = (j == lnew) ? knew : kc + j * D;
+                const E* vr = (j == lnew) ? vnew : vc + j * D;
+                kx[u].load(kr + 8 * c);
+                vx[u].load(vr + 8 * c);
+            }
+        }
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh) {
+            float s[kUnroll];
+            float mx = m[hh];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                float dot = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dot += qr[hh][e] * kx[u][e];
+                dot = group_sum<LPK>(dot);
+                s[u] = ok[u] ? dot : -INFINITY;
+                mx = fmaxf(mx, s[u]);
+            }
+            const float corr = fast_exp2(m[hh] - mx);
+            m[hh] = mx;
+            l[hh] *= corr;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[hh][e] *= corr;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const float p = fast_exp2(s[u] - mx);
+                l[hh] += p;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[hh][e] += p * vx[u][e];
+            }
+        }
+    }
+
+    // merge the KPW key slots of a wave (lanes differing in kg)
+#pragma unroll
+    for (int x = LPK; x < 64; x <<= 1) {
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh) {
+            const float mo = __shfl_xor(m[hh], x);
+            const float lo_ = __shfl_xor(l[hh], x);
+            const float mx = fmaxf(m[hh], mo);
+            const float f = fast_exp2(m[hh] - mx), fo = fast_exp2(mo - mx);
+            l[hh] = l[hh] * f + lo_ * fo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[hh][e] = acc[hh][e] * f + __shfl_xor(acc[hh][e], x) * fo;
+            m[hh] = mx;
+        }
+    }
+    if (kg == 0) {
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[wv][hh][2 + 8 * c + e] = acc[hh][e];
+            if (c == 0) { red[wv][hh][0] = m[hh]; red[wv][hh][1] = l[hh]; }
+        }
+    }
+    __syncthreads();
+    // merge the 4 waves in a fixed order
+    for (int idx = threadIdx.x; idx < HG * (D + 1); idx += blockDim.x) {
+        const int hh = idx / (D + 1), d = idx % (D + 1);   // d == D: the (max, sum) pair
+        float M = red[0][hh][0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) M = fmaxf(M, red[w][hh][0]);
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float f = fast_exp2(red[w][hh][0] - M);
+            sum += f * (d < D ? red[w][hh][2 + d] : red[w][hh][1]);
+        }
+        float* o = out + hh * out_stride;
+        if (d < D) {
+            o[2 + d] = sum;
+        } else {
+            o[0] = M;
+            o[1] = sum;
+        }
+    }
+    __syncthreads();
+}
+
+// ------------------------------------------------------ prefill: split-K
+
+template <typename E, int D, int HG>
+__global__ __launch_bounds__(256) void xattn_split_kernel(XattnParams p, int b0, int nb, PosBlock pos)
+{
+    __shared__ float qs[HG][D];
+    __shared__ float red[4][HG][D + 2];
+    const int s = blockIdx.x;
+    const int G = p.Hq / p.Hkv, hblocks = G / HG;
+    const int g = blockIdx.y / hblocks, hb = blockIdx.y % hblocks;
+    const int bi = blockIdx.z, b = b0 + bi;
+    const int64_t P = pos.v[bi];
+    if (s == 0 && blockIdx.y == 0 && threadIdx.x == 0) p.ws_len[b] = (int32_t)P;
+    const int64_t lo = (int64_t)s * p.chunk;
+    if (lo > P) return;
+    const int64_t hi = lo + p.chunk - 1 < P ? lo + p.chunk - 1 : P;
+    const int h0 = g * G + hb * HG;
+    load_queries<E, D, HG>(qs, (const E*)p.q_out, (const E*)p.alpha_out, (const E*)p.beta_out,
+                           (int64_t)b * p.Hq * D, h0, p.qscale);
+    __syncthreads();
+    const int64_t crow = ((int64_t)b * p.Hkv + g) * p.cap * D;
+    const int64_t part_stride = (int64_t)p.n_split * (D + 2);
+    float* out = p.ws_part + ((int64_t)b * p.Hq + h0) * part_stride + (int64_t)s * (D + 2);
+    attend_chunk<E, D, HG>(qs, (const E*)p.k_cache + crow, (const E*)p.v_cache + crow, -1, nullptr,
+                           nullptr, lo, hi, red, out, part_stride);
+}
+
+// ----------------------------------------------------------- decode: split
+
+template <typename E, int D, int HG>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p)
+{
+    __shared__ float qs[2][HG][D];
+    __shared__ float red[4][HG][D + 2];
+    const int s = blockIdx.x;
+    const int G = p.Hq / p.Hkv, hblocks = G / HG;
+    const int g = blockIdx.y / hblocks, hb = blockIdx.y % hblocks;
+    const int b = blockIdx.z;
+    const int64_t L = p.cache_len[b];
+    if (s == 0 && blockIdx.y == 0 && threadIdx.x == 0) p.ws_len[b] = (int32_t)L;
+    if (L < 0 || L > p.max_len) return;
+
+    const int64_t crow = ((int64_t)b * p.Hkv + g) * p.cap * D;
+    const E* knew = (const E*)p.k_new + ((int64_t)b * p.Hkv + g) * D;
+    const E* vnew = (const E*)p.v_new + ((int64_t)b * p.Hkv + g) * D;
+    if (s == 0 && hb == 0) {
+        // append the new base token's K/V at slot L (nobody reads slot L from
+        // the cache in this launch: readers take key L from k_new / v_new)
+        for (int d = threadIdx.x; d < D; d += blockDim.x) {
+            ((E*)p.k_cache)[crow + L * D + d] = knew[d];
+            ((E*)p.v_cache)[crow + L * D + d] = vnew[d];
+        }
+    }
+    const int64_t lo = (int64_t)s * p.chunk;
+    if (lo > L) return;
+    const int64_t hi = lo + p.chunk - 1 < L ? lo + p.chunk - 1 : L;
+    const int h0 = g * G + hb * HG;
+    load_queries<E, D, HG>(qs[0], (const E*)p.q_out, (const E*)p.alpha_out, (const E*)p.beta_out,
+                           (int64_t)b * p.Hq * D, h0, p.qscale);
+    load_queries<E, D, HG>(qs[1], (const E*)p.q, (const E*)p.alpha, (const E*)p.beta,
+                           (int64_t)b * p.Hq * D, h0, p.qscale);
+    __syncthreads();
+    const int64_t kind_stride = (int64_t)p.n_split * (D + 2);
+    const int64_t head_stride = 2 * kind_stride;
+    float* out = p.ws_part + ((int64_t)b * p.Hq + h0) * head_stride + (int64_t)s * (D + 2);
+    // the output copy: whole history [0, L]
+    attend_chunk<E, D, HG>(qs[0], (const E*)p.k_cache + crow, (const E*)p.v_cache + crow, L, knew, vnew,
+                           lo, hi, red, out, head_stride);
+    // the base token: its window [L - w + 1, L]
+    const int64_t wlo = L - p.window + 1 > lo ? L - p.window + 1 : lo;
+    if (wlo <= hi)
+        attend_chunk<E, D, HG>(qs[1], (const E*)p.k_cache + crow, (const E*)p.v_cache + crow, L, knew,
+                               vnew, wlo, hi, red, out + kind_stride, head_stride);
+}
+
+// --------------------------------------------------------------- LSE merge
+
+// One workgroup per (sequence, query head); thread d owns output element d.
+// kinds = 1: the copy only (prefill); kinds = 2: copy and base token (decode).
+template <typename E, int D>
+__global__ __launch_bounds__(D) void merge_kernel(const float* ws_part, const int32_t* ws_len,
+                                                  int32_t* cache_len, int64_t max_len, int window,
+                                                  int Hq, int chunk, int n_split, int kinds,
+                                                  E* o_out, E* o)
+{
+    const int b = blockIdx.x / Hq, h = blockIdx.x % Hq, d = threadIdx.x;
+    const int64_t L = ws_len[b];
+    const int64_t kind_stride = (int64_t)n_split * (D + 2);
+    const float* part = ws_part + ((int64_t)b * Hq + h) * kinds * kind_stride;
+    const int64_t row = ((int64_t)b * Hq + h) * D + d;
+    if (L < 0 || L > max_len) {
+        st_elem(o_out, row, __builtin_nanf(""));
+        if (kinds == 2) st_elem(o, row, __builtin_nanf(""));
+        return;
+    }
+    for (int kind = 0; kind < kinds; ++kind) {
+        const int64_t lo = kind == 0 ? 0 : (L - window + 1 > 0 ? L - window + 1 : 0);
+        const int s0 = (int)(lo / chunk), s1 = (int)(L / chunk);
+        const float* pk = part + kind * kind_stride;
+        float M = kNegBig;
+        for (int s = s0; s <= s1; ++s) M = fmaxf(M, pk[(int64_t)s * (D + 2)]);
+        float num = 0.f, den = 0.f;
+        for (int s = s0; s <= s1; ++s) {
+            const float* ps = pk + (int64_t)s * (D + 2);
+            const float f = fast_exp2(ps[0] - M);
+            den += f * ps[1];
+            num += f * ps[2 + d];
+        }
+        st_elem(kind == 0 ? o_out : o, row, num / den);
+    }
+    if (cache_len && h == 0 && d == 0) cache_len[b] = (int32_t)(L + 1);
+}
+
+template <typename E, int D, int HG>
+hipError_t launch_xattn_t(const XattnParams& p, hipStream_t st)
+{
+    const int hblocks = (p.Hq / p.Hkv) / HG;
+    for (int b0 = 0; b0 < p.B; b0 += kPosPerLaunch) {
+        const int nb = p.B - b0 < kPosPerLaunch ? p.B - b0 : kPosPerLaunch;
+        PosBlock pos;
+        for (int i = 0; i < nb; ++i) pos.v[i] = p.pos[b0 + i];
+        hipLaunchKernelGGL((xattn_split_kernel<E, D, HG>), dim3(p.n_split, p.Hkv * hblocks, nb), dim3(256),
+                           0, st, p, b0, nb, pos);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    int64_t max_len = 0;
+    for (int b = 0; b < p.B; ++b) max_len = p.pos[b] > max_len ? p.pos[b] : max_len;
+    hipLaunchKernelGGL((merge_kernel<E, D>), dim3(p.B * p.Hq), dim3(D), 0, st, p.ws_part, p.ws_len,
+                       (int32_t*)nullptr, max_len, 0, p.Hq, p.chunk, p.n_split, 1, (E*)p.o_out, (E*)nullptr);
+    return hipGetLastError();
+}
+
+template <typename E, int D, int HG>
+hipError_t launch_decode_t(const DecodeParams& p, hipStream_t st)
+{
+    const int hblocks = (p.Hq / p.Hkv) / HG;
+    hipLaunchKernelGGL((decode_split_kernel<E, D, HG>), dim3(p.n_split, p.Hkv * hblocks, p.B), dim3(256), 0,
+                       st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((merge_kernel<E, D>), dim3(p.B * p.Hq), dim3(D), 0, st, p.ws_part, p.ws_len,
+                       p.cache_len, p.max_len, p.window, p.Hq, p.chunk, p.n_split, 2, (E*)p.o_out, (E*)p.o);
+    return hipGetLastError();
+}
+
+template <typename E, int D>
+hipError_t xattn_by_hg(const XattnParams& p, hipStream_t st)
+{
+    switch (xattn_heads_per_wg(p.Hq / p.Hkv)) {
+    case 4: return launch_xattn_t<E, D, 4>(p, st);
+    case 2: return launch_xattn_t<E, D, 2>(p, st);
+    default: return launch_xattn_t<E, D, 1>(p, st);
+    }
+}
+
+template <typename E, int D>
+hipError_t decode_by_hg(const DecodeParams& p, hipStream_t st)
+{
+    switch (xattn_heads_per_wg(p.Hq / p.Hkv)) {
+    case 4: return launch_decode_t<E, D, 4>(p, st);
+    case 2: return launch_decode_t<E, D, 2>(p, st);
+    default: return launch_decode_t<E, D, 1>(p, st);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_xattn(const XattnParams& p, hipStream_t st)
+{
+    if (p.dt == Dt::F32) return p.D == 64 ? xattn_by_hg<float, 64>(p, st) : xattn_by_hg<float, 128>(p, st);
+    return p.D == 64 ? xattn_by_hg<uint16_t, 64>(p, st) : xattn_by_hg<uint16_t, 128>(p, st);
+}
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t st)
+{
+    if (p.dt == Dt::F32) return p.D == 64 ? decode_by_hg<float, 64>(p, st) : decode_by_hg<float, 128>(p, st);
+    return p.D == 64 ? decode_by_hg<uint16_t, 64>(p, st) : decode_by_hg<uint16_t, 128>(p, st);
+}
+
+}  // namespace orthros

@@ -1,0 +1,81 @@
+// kernels.h -- internal interface between the C-ABI host code (api.hip) and
+// the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace orthros {
+
+// Storage type of every tensor of a call.
+enum class Dt : int32_t { F32 = 0, BF16 = 1 };
+
+// Base-stream sliding-window attention + cache write (prefill).
+struct SwaParams {
+    const void* q;        // [B][T][Hq][D]
+    const void* k;        // [B][T][Hkv][D]
+    const void* v;
+    const void* alpha;    // [Hq][D]
+    const void* beta;
+    void* k_cache;        // [B][Hkv][cap][D]
+    void* v_cache;
+    void* o;              // [B][T][Hq][D]
+    int64_t T, cap;
+    int32_t B, Hq, Hkv, D, window;
+    float qscale;         // softmax_scale * log2(e)
+    Dt dt;
+};
+
+// Chunked single-query attention over the cache (the output copy, and in
+// decode also the base token's window), followed by the LSE merge.
+constexpr int kPosPerLaunch = 64;   // batch rows whose copy positions travel in one launch
+struct PosBlock { int64_t v[kPosPerLaunch]; };   // passed by value as a kernel argument
+
+struct XattnParams {
+    const void* q_out;    // [B][Hq][D]
+    const void* alpha_out;
+    const void* beta_out;
+    const void* k_cache;  // [B][Hkv][cap][D]
+    const void* v_cache;
+    void* o_out;          // [B][Hq][D]
+    int32_t* ws_len;      // workspace: per-sequence last key index
+    float* ws_part;       // workspace: partials [B][Hq][1][n_split][D+2]
+    const int64_t* pos;   // host [B]: copy positions
+    int64_t cap;
+    int32_t B, Hq, Hkv, D;
+    int32_t chunk, n_split;
+    float qscale;
+    Dt dt;
+};
+
+struct DecodeParams {
+    const void* q;        // [B][Hq][D]
+    const void* q_out;
+    const void* k_new;    // [B][Hkv][D]
+    const void* v_new;
+    const void* alpha;
+    const void* beta;
+    const void* alpha_out;
+    const void* beta_out;
+    void* k_cache;        // [B][Hkv][cap][D]
+    void* v_cache;
+    int32_t* cache_len;   // device [B]
+    void* o;              // [B][Hq][D]
+    void* o_out;
+    int32_t* ws_len;      // workspace: per-sequence length seen by this step
+    float* ws_part;       // workspace: partials [B][Hq][2][n_split][D+2]
+    int64_t cap, max_len;
+    int32_t B, Hq, Hkv, D, window;
+    int32_t chunk, n_split;
+    float qscale;
+    Dt dt;
+};
+
+// Heads of one KV group that one workgroup of the chunked kernels serves.
+inline int xattn_heads_per_wg(int G) { return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
+
+hipError_t launch_swa(const SwaParams& p, hipStream_t s);
+hipError_t launch_xattn(const XattnParams& p, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+
+}  // namespace orthros

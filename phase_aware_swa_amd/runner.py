@@ -1,0 +1,81 @@
+"""Device-buffer plumbing around the binding: allocates outputs, caches and
+workspaces with torch (device memory only) and calls the C ABI.
+
+Nothing here computes: every step of the attention runs in liborthros.so.
+"""
+import torch
+
+from . import binding
+from .inputs import empty_cache
+
+
+def desc_for(cfg, softmax_scale=0.0):
+    return binding.make_desc(cfg["batch"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"],
+                             cfg["window"], cfg["dtype"], softmax_scale)
+
+
+class Prefill:
+    """Buffers for repeated prefill calls of one shape on one device.
+
+    x: the input dict of inputs.prefill_inputs (tensors already on `device`).
+    cap: cache capacity (>= T); slots [T, cap) hold the sentinel and must
+    stay untouched.
+    """
+
+    def __init__(self, cfg, x, device="cuda", cap=None, softmax_scale=0.0):
+        self.cfg = cfg
+        self.x = x
+        B, T = cfg["batch"], x["q"].shape[1]
+        Hq, Hkv, d, dt = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["dtype"]
+        self.T = T
+        self.desc = desc_for(cfg, softmax_scale)
+        self.cap = cap or T
+        self.k_cache = empty_cache(B, Hkv, self.cap, d, dt, device)
+        self.v_cache = empty_cache(B, Hkv, self.cap, d, dt, device)
+        self.o = torch.empty(B, T, Hq, d, dtype=dt, device=device)
+        self.o_out = torch.empty(B, Hq, d, dtype=dt, device=device)
+        ws = binding.prefill_workspace_size(self.desc, T)
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
+
+    def run(self, stream=None):
+        x = self.x
+        binding.prefill(self.desc, self.T, x["q"], x["q_out"], x["out_pos"], x["k"], x["v"], x["alpha"],
+                        x["beta"], x["alpha_out"], x["beta_out"], self.k_cache, self.v_cache, self.o,
+                        self.o_out, self.workspace, stream)
+
+    def run_swa(self, stream=None):
+        x = self.x
+        binding.swa_prefill(self.desc, self.T, x["q"], x["k"], x["v"], x["alpha"], x["beta"], self.k_cache,
+                            self.v_cache, self.o, stream)
+
+    def run_xattn(self, stream=None):
+        x = self.x
+        binding.global_xattn(self.desc, self.T, x["q_out"], x["out_pos"], x["alpha_out"], x["beta_out"],
+                             self.k_cache, self.v_cache, self.o_out, self.workspace, stream)
+
+
+class Decode:
+    """Buffers for a run of decode steps over caches the caller owns.
+
+    k_cache, v_cache, cache_len: device tensors, updated in place by step().
+    max_len_hint: host bound of every cache length for the whole run.
+    """
+
+    def __init__(self, cfg, k_cache, v_cache, cache_len, max_len_hint, alpha, beta, alpha_out, beta_out,
+                 softmax_scale=0.0):
+        B, Hq, d, dt = cfg["batch"], cfg["n_q_heads"], cfg["head_dim"], cfg["dtype"]
+        dev = k_cache.device
+        self.desc = desc_for(cfg, softmax_scale)
+        self.k_cache, self.v_cache, self.cache_len = k_cache, v_cache, cache_len
+        self.max_len_hint = max_len_hint
+        self.alpha, self.beta, self.alpha_out, self.beta_out = alpha, beta, alpha_out, beta_out
+        self.o = torch.empty(B, Hq, d, dtype=dt, device=dev)
+        self.o_out = torch.empty(B, Hq, d, dtype=dt, device=dev)
+        ws = binding.decode_workspace_size(self.desc, max_len_hint)
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+
+    def step(self, q, q_out, k_new, v_new, o=None, o_out=None, stream=None):
+        binding.decode_step(self.desc, q, q_out, k_new, v_new, self.alpha, self.beta, self.alpha_out,
+                            self.beta_out, self.k_cache, self.v_cache, self.cache_len, self.max_len_hint,
+                            self.o if o is None else o, self.o_out if o_out is None else o_out,
+                            self.workspace, stream)

@@ -1,0 +1,65 @@
+"""Shared helpers of the GPU tests: seeded inputs on both sides, the oracle
+call, and the parity bar.
+
+Parity bar (element by element against the fp64 oracle):
+  bf16 storage: max-abs <= 2e-2 and relative L2 <= 5e-3
+  fp32 storage: max-abs <= 1e-4 and relative L2 <= 1e-4
+Cache bytes, untouched slots, lengths and mask placement: bit-exact.
+"""
+import sys
+
+import torch
+
+import oracle
+from phase_aware_swa_amd import inputs
+
+TOL = {torch.bfloat16: (2e-2, 5e-3), torch.float32: (1e-4, 1e-4)}
+
+
+def say(*a):
+    """Names the case on stdout before a GPU step (flushed)."""
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def errors(gpu, ref):
+    g = gpu.detach().to("cpu", torch.float64)
+    r = ref.to(torch.float64)
+    assert torch.isfinite(g).all(), "non-finite values in the GPU output"
+    d = g - r
+    max_abs = d.abs().max().item() if d.numel() else 0.0
+    rel = (d.norm() / r.norm()).item() if r.norm() > 0 else d.norm().item()
+    return max_abs, rel
+
+
+def assert_parity(gpu, ref, dtype, what=""):
+    max_abs, rel = errors(gpu, ref)
+    tol_abs, tol_rel = TOL[dtype]
+    assert max_abs <= tol_abs and rel <= tol_rel, (
+        f"{what}: max-abs {max_abs:.3e} (<= {tol_abs}) rel-L2 {rel:.3e} (<= {tol_rel})")
+    return max_abs, rel
+
+
+def to_cpu(x):
+    return {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in x.items()}
+
+
+def to_dev(x, device="cuda"):
+    return {k: (v.to(device) if torch.is_tensor(v) and k != "needle_pos" else v) for k, v in x.items()}
+
+
+def oracle_prefill(xc, window, swa=True, cap=None, softmax_scale=None):
+    """The oracle on CPU copies of the inputs; caches start as sentinels."""
+    B, T = xc["q"].shape[:2]
+    Hkv, d = xc["k"].shape[2], xc["k"].shape[3]
+    cap = cap or T
+    kc = inputs.empty_cache(B, Hkv, cap, d, xc["q"].dtype)
+    vc = inputs.empty_cache(B, Hkv, cap, d, xc["q"].dtype)
+    return oracle.prefill(xc["q"], xc["q_out"], xc["out_pos"], xc["k"], xc["v"], xc["alpha"], xc["beta"],
+                          xc["alpha_out"], xc["beta_out"], window, softmax_scale=softmax_scale,
+                          k_cache=kc, v_cache=vc, swa=swa)
+
+
+def bits(t):
+    """Raw bit view for byte-exact comparisons."""
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)

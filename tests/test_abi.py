@@ -1,0 +1,105 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and rejects bad arguments with the documented status before any
+HIP call (no GPU needed: validation never reaches the runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from phase_aware_swa_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "orthros.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(orthros_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"orthros_prefill", "orthros_decode_step", "orthros_swa_prefill", "orthros_global_xattn"} <= set(names)
+    lib = binding.lib()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in orthros.h but not exported"
+
+
+def test_abi_version_and_status_text():
+    assert binding.abi_version() == 1
+    text = open(HEADER).read()
+    assert "#define ORTHROS_ABI_VERSION 1" in text
+    for code, name in binding.STATUS.items():
+        assert binding.status_str(code) == name
+        assert re.search(rf"\b{name}\s*=\s*{code}\b", text) or code == 0
+
+
+D = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, window=128, dtype=binding.BF16)
+FAKE = 1 << 20   # aligned, never dereferenced: every call below fails validation first
+
+
+def prefill_call(desc, T=100, cap=100, out_pos=(99, 99), ptr=FAKE, ws_bytes=1 << 30, ws=FAKE):
+    pos = (ctypes.c_int64 * len(out_pos))(*out_pos)
+    p = ctypes.c_void_p(ptr)
+    return binding.lib().orthros_prefill(ctypes.byref(desc), T, p, p, pos, p, p, p, p, p, p, p, p, cap, p, p,
+                                         ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def mk(**kw):
+    d = dict(D)
+    d.update(kw)
+    return binding.Desc(d["batch"], d["n_q_heads"], d["n_kv_heads"], d["head_dim"], d["window"],
+                        d.get("softmax_scale", 0.0), d["dtype"])
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(dtype=7), -3),
+    (dict(batch=0), -2),
+    (dict(n_q_heads=9), -2),
+    (dict(head_dim=96), -2),
+    (dict(window=0), -2),
+    (dict(softmax_scale=-1.0), -2),
+    (dict(softmax_scale=float("inf")), -2),
+])
+def test_bad_desc(change, status):
+    assert prefill_call(mk(**change)) == status
+    assert binding.lib().orthros_last_error()
+
+
+def test_bad_call_arguments():
+    d = mk()
+    assert prefill_call(d, T=0) == -2
+    assert prefill_call(d, T=100, cap=99) == -5
+    assert prefill_call(d, out_pos=(99, 100)) == -4
+    assert prefill_call(d, out_pos=(-1, 5)) == -4
+    assert prefill_call(d, ptr=0) == -1
+    assert prefill_call(d, ptr=FAKE + 8) == -8
+    assert prefill_call(d, ws=0) == -6
+    assert prefill_call(d, ws_bytes=16) == -6
+    assert b"workspace" in binding.lib().orthros_last_error()
+    n = None
+    assert binding.lib().orthros_prefill(None, 100, n, n, n, n, n, n, n, n, n, n, n, 100, n, n, n, 0, n) == -1
+
+
+def test_decode_bad_arguments():
+    L = binding.lib()
+    d = mk()
+    p = ctypes.c_void_p(FAKE)
+    call = lambda cap, hint, ws=FAKE, wsb=1 << 30: L.orthros_decode_step(
+        ctypes.byref(d), p, p, p, p, p, p, p, p, p, p, cap, p, hint, p, p, ctypes.c_void_p(ws), wsb, None)
+    assert call(cap=100, hint=100) == -5
+    assert call(cap=100, hint=-1) == -2
+    assert call(cap=100, hint=50, ws=0) == -6
+    assert call(cap=100, hint=50, wsb=8) == -6
+
+
+def test_workspace_sizes():
+    d = mk()
+    w1 = binding.prefill_workspace_size(d, 1000)
+    w2 = binding.prefill_workspace_size(d, 131072)
+    assert 0 < w1 <= w2
+    assert binding.prefill_workspace_size(mk(head_dim=5), 100) == 0
+    assert binding.prefill_workspace_size(d, 0) == 0
+    assert 0 < binding.decode_workspace_size(d, 10) <= binding.decode_workspace_size(d, 100000)
+    assert binding.decode_workspace_size(d, -1) == 0
