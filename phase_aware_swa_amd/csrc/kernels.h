@@ -75,6 +75,9 @@ struct DecodeParams {
 inline int xattn_heads_per_wg(int G) { return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
 
 hipError_t launch_swa(const SwaParams& p, hipStream_t s);
+// Streaming sliding-window kernel: bf16, Hq/Hkv a multiple of 4, window <= kRingMaxWindow.
+constexpr int kRingMaxWindow = 129;
+hipError_t launch_swa_ring(const SwaParams& p, hipStream_t s);
 hipError_t launch_xattn(const XattnParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 

@@ -49,6 +49,14 @@ CASES = [
     (1, 16, 2, 64, 300, 700),
     (1, 2, 1, 128, 2000, 1500),
     (2, 4, 2, 128, 5, 96),
+    # GQA groups of 4 / 8 with w <= 129 (the streaming kernel), incl. segment edges
+    (1, 4, 1, 64, 128, 300),
+    (2, 8, 2, 128, 1, 100),
+    (1, 4, 1, 128, 128, 1),
+    (1, 4, 1, 128, 128, 33),
+    (1, 4, 1, 128, 64, 4100),
+    (1, 8, 1, 128, 100, 2000),
+    (1, 4, 1, 128, 128, 40000),
 ]
 
 
