@@ -267,6 +267,248 @@ __global__ __launch_bounds__(256, 2) void swa_ring_kernel(SwaParams a, int n_til
     }
 }
 
+// ---------------------------------------------------------------------------
+// 16x16x32 form: 8 waves = 4 query heads x 2 sub-tiles of 16 rows; the
+// window of a 32-row tile spans 10 blocks of 16 keys = 5 aligned pairs, kept
+// in a 5-slot ring of 32-key pair slots.  Per wave it needs about half the
+// registers of the 32x32 form, so two workgroups (16 waves) fit on a CU.
+//
+// S^T = K Q^T per 16-key block leaves each lane (n = query, gq = lane/16)
+// with keys 4gq..4gq+3 of the block; the P^T operand of O^T = V^T P^T over a
+// pair is then [block 0 keys 4gq..+3, block 1 keys 4gq..+3].  V^T rows of a
+// pair slot store the 32 keys in exactly that order, so each PV operand is a
+// single 16-byte LDS read.
+template <int D>
+struct Pair {
+    static constexpr int NSLOT = 5;
+    static constexpr int KPART = 32 * D;    // bf16: K rows of the two blocks
+    static constexpr int VPART = D * 32;    // bf16: V^T rows, 32 keys each
+    static constexpr int SLOT = KPART + VPART;
+    // K: row = key of the pair (0..31); 16-byte chunks XOR-swizzled by row.
+    __device__ static int kofs(int r, int c)
+    {
+        const int sw = (D == 128) ? (r & 15) : ((r >> 1) & 7);
+        return r * D + ((c ^ sw) << 3);
+    }
+    // V^T: row d = 64 bytes = four 16-byte units; unit u holds keys
+    // 4u..4u+3 of block 0 then of block 1; XOR by bits 2..3 of d.
+    __device__ static int vofs(int d, int u) { return d * 32 + ((u ^ ((d >> 2) & 3)) << 3); }
+};
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void swa_ring16_kernel(
+    SwaParams a, int n_tiles, int hblocks, int n_seg, int tps)
+{
+    using R = Pair<D>;
+    constexpr int NS = R::NSLOT;
+    constexpr int C16 = D / 8;     // 16-byte chunks per row
+    constexpr int NQ = D / 32;     // MFMA k-steps over the head dim (32 each)
+    constexpr int ND = D / 16;     // 16-wide d tiles of O^T
+    __shared__ __align__(16) uint16_t ring[NS * R::SLOT];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hh = wv & 3, sub = wv >> 2;
+    const int n = lane & 15, gq = lane >> 4;
+    int64_t id = blockIdx.x;
+    const int seg = (int)(id % n_seg);
+    id /= n_seg;
+    const int hb = (int)(id % hblocks);
+    id /= hblocks;
+    const int g = (int)(id % a.Hkv);
+    const int b = (int)(id / a.Hkv);
+    const int G = a.Hq / a.Hkv;
+    const int h = g * G + hb * 4 + hh;
+    const int64_t T = a.T;
+    const int W = a.window;
+    const int t_begin = seg * tps;
+    const int t_end = t_begin + tps < n_tiles ? t_begin + tps : n_tiles;
+    if (t_begin >= t_end) return;
+    const bool writer = (hb == 0);
+    const float qs = a.qscale;
+
+    const uint16_t* __restrict__ al = (const uint16_t*)a.alpha + (int64_t)h * D;
+    const uint16_t* __restrict__ be = (const uint16_t*)a.beta + (int64_t)h * D;
+    const int64_t qrow_b = (int64_t)a.Hq * D * 2, krow_b = (int64_t)a.Hkv * D * 2;
+    const int64_t kv_seq = (int64_t)b * T * a.Hkv * D + (int64_t)g * D;
+    const int64_t q_seq = (int64_t)b * T * a.Hq * D + (int64_t)h * D;
+    const int64_t c_seq = ((int64_t)b * a.Hkv + g) * a.cap * D;
+
+    // staging of one pair (32 new keys): K chunk (kk, dc); V key pair kp x 4-wide d group dq
+    const int kk = tid / C16, dc = tid % C16;
+    const bool kthread = tid < 32 * C16;
+    const int kp = tid & 15, dq = tid >> 4;
+    const bool vthread = dq < D / 4;
+
+    auto load_pair = [&](int64_t pr, u32x4& kr, u32x2 (&vr)[2]) {
+        const int64_t kbase = pr * 32;
+        const int64_t avail = (T - kbase) * krow_b - g * D * 2;
+        const rsrc_t rk = make_rsrc((const uint16_t*)a.k + kv_seq + kbase * a.Hkv * D, avail);
+        const rsrc_t rv = make_rsrc((const uint16_t*)a.v + kv_seq + kbase * a.Hkv * D, avail);
+        kr = kthread ? buf_load16(rk, (uint32_t)(kk * krow_b + 16 * dc)) : u32x4{0u, 0u, 0u, 0u};
+        vr[0] = vr[1] = u32x2{0u, 0u};
+        if (vthread) {
+            vr[0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                rv, (int)(2 * kp * krow_b + 8 * dq), 0, 0));
+            vr[1] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                rv, (int)((2 * kp + 1) * krow_b + 8 * dq), 0, 0));
+        }
+    };
+    auto store_pair = [&](int64_t pr, bool own, const u32x4& kr, const u32x2 (&vr)[2]) {
+        uint16_t* Ks = ring + (int)(pr % NS) * R::SLOT;
+        if (kthread) *(u32x4*)(Ks + R::kofs(kk, dc)) = kr;
+        if (vthread) {
+            uint16_t* Vt = Ks + R::KPART;
+            const int key = 2 * kp, bb = key >> 4, lk = key & 15;
+            const int pos = bb * 4 + (lk & 3);           // within the 16-byte unit lk / 4
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const uint32_t w0 = vr[0][e], w1 = vr[1][e];
+                const int d0 = 4 * dq + 2 * e;
+                *(uint32_t*)(Vt + R::vofs(d0, lk >> 2) + pos) = (w0 & 0xffffu) | (w1 << 16);
+                *(uint32_t*)(Vt + R::vofs(d0 + 1, lk >> 2) + pos) = (w0 >> 16) | (w1 & 0xffff0000u);
+            }
+        }
+        if (own && writer) {
+            const int64_t kbase = pr * 32;
+            const int64_t avail = (T - kbase) * D * 2;
+            const rsrc_t ck = make_rsrc((uint16_t*)a.k_cache + c_seq + kbase * D, avail);
+            const rsrc_t cv = make_rsrc((uint16_t*)a.v_cache + c_seq + kbase * D, avail);
+            if (kthread) buf_store16(kr, ck, (uint32_t)(kk * D * 2 + 16 * dc));
+            if (vthread) {
+                __builtin_amdgcn_raw_buffer_store_b64(vr[0], cv, (int)(2 * kp * D * 2 + 8 * dq), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(vr[1], cv, (int)((2 * kp + 1) * D * 2 + 8 * dq), 0, 0);
+            }
+        }
+    };
+    // raw Q rows of the wave's 16-row sub-tile: lane (n, gq) holds q[row][32 i + 8 gq + 0..7]
+    auto load_q = [&](int64_t r0, u32x4 (&qr)[NQ]) {
+        const rsrc_t rq = make_rsrc((const uint16_t*)a.q + q_seq + r0 * a.Hq * D, (T - r0) * qrow_b - h * D * 2);
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) qr[i] = buf_load16(rq, (uint32_t)(n * qrow_b + 64 * i + 16 * gq));
+    };
+    // q * alpha + beta, packed as MFMA B operands (the softmax scale is
+    // applied to the scores inside the exponent instead)
+    auto scale_offset = [&](const u32x4 (&qr)[NQ], bf16x8 (&qf)[NQ]) {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int d0 = 32 * i + 8 * gq;
+            const u32x4 av = *(const u32x4*)(al + d0);
+            const u32x4 bv = *(const u32x4*)(be + d0);
+            u32x4 r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                r[e] = pack_bf16x2(__builtin_fmaf(bf16_lo(qr[i][e]), bf16_lo(av[e]), bf16_lo(bv[e])),
+                                   __builtin_fmaf(bf16_hi(qr[i][e]), bf16_hi(av[e]), bf16_hi(bv[e])));
+            qf[i] = __builtin_bit_cast(bf16x8, r);
+        }
+    };
+
+    u32x4 kreg;
+    u32x2 vreg[2];
+    u32x4 qraw[NQ];
+    bf16x8 qf[NQ];
+
+    {   // prologue: the first tile's window, one pair at a time (the halo is not owned)
+        const int64_t q0 = (int64_t)t_begin * 32;
+        const int64_t lo = q0 - W + 1 > 0 ? q0 - W + 1 : 0;
+        load_q(q0 + 16 * sub, qraw);
+        for (int64_t pr = lo >> 5; pr <= (q0 >> 5); ++pr) {
+            load_pair(pr, kreg, vreg);
+            store_pair(pr, pr == (q0 >> 5), kreg, vreg);
+        }
+        scale_offset(qraw, qf);
+        __syncthreads();
+    }
+
+    for (int tile = t_begin; tile < t_end; ++tile) {
+        const int64_t q0 = (int64_t)tile * 32;
+        const bool has_next = tile + 1 < t_end;
+        if (has_next) {
+            load_pair((q0 >> 5) + 1, kreg, vreg);
+            load_q(q0 + 32 + 16 * sub, qraw);
+        }
+        const int64_t lo = q0 - W + 1 > 0 ? q0 - W + 1 : 0;
+        const int r0 = 16 * sub;                    // wave's first row relative to q0
+
+        f32x4 oacc[ND];
+#pragma unroll
+        for (int i = 0; i < ND; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m_run = kNegBig, l_run = 0.f;        // m_run in scaled (exp2) units
+        for (int64_t pr = lo >> 5; pr <= (q0 >> 5); ++pr) {
+            const uint16_t* Ks = ring + (int)(pr % NS) * R::SLOT;
+            f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const bf16x8 k0 = *(const bf16x8*)(Ks + R::kofs(n, 4 * i + gq));
+                const bf16x8 k1 = *(const bf16x8*)(Ks + R::kofs(16 + n, 4 * i + gq));
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[i], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[i], s1, 0, 0, 0);
+            }
+            // s0[r]: key 32 pr + 4 gq + r, s1[r]: key 32 pr + 16 + 4 gq + r; row r0 + n (relative to q0)
+            const int dj = (int)(pr * 32 - q0) - r0;
+            const bool full = (dj + 31 <= 0) && (dj >= 15 - W + 1);
+            if (!full) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j0 = dj + 4 * gq + r, j1 = j0 + 16;
+                    if (j0 > n || j0 < n - W + 1) s0[r] = -INFINITY;
+                    if (j1 > n || j1 < n - W + 1) s1[r] = -INFINITY;
+                }
+            }
+            float lmax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(s0[0], s0[1]), __builtin_fmaxf(s0[2], s0[3])),
+                                         __builtin_fmaxf(__builtin_fmaxf(s1[0], s1[1]), __builtin_fmaxf(s1[2], s1[3])));
+            lmax *= qs;
+            if (__any(lmax > m_run + kRescaleMargin)) {
+                float rmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+                rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+                const float m_new = fmaxf(m_run, rmax);
+                const float corr = fast_exp2(m_run - m_new);
+                m_run = m_new;
+                l_run *= corr;
+#pragma unroll
+                for (int i = 0; i < ND; ++i) oacc[i] *= corr;
+            }
+            float p[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[r] = fast_exp2(__builtin_fmaf(s0[r], qs, -m_run));
+                p[4 + r] = fast_exp2(__builtin_fmaf(s1[r], qs, -m_run));
+            }
+            const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                              pack_bf16x2(p[6], p[7])};
+            l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+            const uint16_t* Vt = Ks + R::KPART;
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt) {
+                const bf16x8 vf = *(const bf16x8*)(Vt + R::vofs(16 * dt + n, gq));
+                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, oacc[dt], 0, 0, 0);
+            }
+        }
+        // ---- normalise and store the sub-tile (rows >= T fall outside the resource)
+        float l_tot = l_run + __shfl_xor(l_run, 16);
+        l_tot += __shfl_xor(l_tot, 32);
+        {
+            const float inv = 1.f / l_tot;
+            const int64_t r0g = q0 + r0;
+            const rsrc_t ro = make_rsrc((uint16_t*)a.o + q_seq + r0g * a.Hq * D, (T - r0g) * qrow_b - h * D * 2);
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt) {
+                u32x2 w;
+                w[0] = pack_bf16x2(oacc[dt][0] * inv, oacc[dt][1] * inv);
+                w[1] = pack_bf16x2(oacc[dt][2] * inv, oacc[dt][3] * inv);
+                buf_store8(w, ro, (uint32_t)(n * qrow_b + 2 * (16 * dt + 4 * gq)));
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (has_next) scale_offset(qraw, qf);
+        __syncthreads();   // every wave is done with the slot the next pair replaces
+        if (has_next) store_pair((q0 >> 5) + 1, true, kreg, vreg);
+        __syncthreads();
+    }
+}
+
 }  // namespace
 
 // Workgroups of the streaming kernel: about two per CU of the 256, each
@@ -285,10 +527,10 @@ hipError_t launch_swa_ring(const SwaParams& p, hipStream_t s)
     n_seg = (n_tiles + tps - 1) / tps;
     const int64_t n_wg = streams * n_seg;
     if (p.D == 64)
-        hipLaunchKernelGGL((swa_ring_kernel<64>), dim3((unsigned)n_wg), dim3(256), 0, s, p, n_tiles, hblocks, n_seg,
-                           tps);
+        hipLaunchKernelGGL((swa_ring16_kernel<64>), dim3((unsigned)n_wg), dim3(512), 0, s, p, n_tiles, hblocks,
+                           n_seg, tps);
     else
-        hipLaunchKernelGGL((swa_ring_kernel<128>), dim3((unsigned)n_wg), dim3(256), 0, s, p, n_tiles, hblocks,
+        hipLaunchKernelGGL((swa_ring16_kernel<128>), dim3((unsigned)n_wg), dim3(512), 0, s, p, n_tiles, hblocks,
                            n_seg, tps);
     return hipGetLastError();
 }
