@@ -28,245 +28,6 @@ namespace {
 constexpr int kSlots = 5;
 constexpr float kRescaleMargin = 8.0f;   // log2 units
 
-template <int D>
-struct Ring {
-    static constexpr int KBLK = 32 * D;     // bf16 per K block
-    static constexpr int VBLK = D * 32;     // bf16 per V^T block
-    static constexpr int SLOT = KBLK + VBLK;
-    // K block: row = key (D bf16), 16-byte chunks XOR-swizzled by row so the
-    // 16 lanes of one b128 read pass hit 16 different bank groups.
-    __device__ static int kofs(int r, int c)
-    {
-        const int sw = (D == 128) ? (r & 15) : ((r >> 1) & 7);
-        return r * D + ((c ^ sw) << 3);
-    }
-    // V^T block: row = head-dim index (32 keys = 64 bytes), 8-byte units
-    // XOR-swizzled by row so the 32 lanes of one b64 read pass are distinct.
-    __device__ static int vofs(int d, int u) { return d * 32 + ((u ^ ((d >> 2) & 7)) << 2); }
-};
-
-template <int D>
-__global__ __launch_bounds__(256, 2) void swa_ring_kernel(SwaParams a, int n_tiles, int hblocks, int n_seg,
-                                                          int tps)
-{
-    using R = Ring<D>;
-    constexpr int C16 = D / 8;     // 16-byte chunks per row
-    constexpr int NQ = D / 16;     // MFMA k-steps over the head dim
-    constexpr int ND = D / 32;     // 32-wide output tiles
-    constexpr int KCH = D / 64;    // K chunks per thread per block
-    __shared__ __align__(16) uint16_t ring[kSlots * R::SLOT];
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps row bases in SGPRs
-    const int n = lane & 31, half = lane >> 5;
-    int64_t id = blockIdx.x;
-    const int seg = (int)(id % n_seg);
-    id /= n_seg;
-    const int hb = (int)(id % hblocks);
-    id /= hblocks;
-    const int g = (int)(id % a.Hkv);
-    const int b = (int)(id / a.Hkv);
-    const int G = a.Hq / a.Hkv;
-    const int h = g * G + hb * 4 + wv;
-    const int64_t T = a.T;
-    const int W = a.window;
-    const int t_begin = seg * tps;
-    const int t_end = t_begin + tps < n_tiles ? t_begin + tps : n_tiles;
-    if (t_begin >= t_end) return;
-    const bool writer = (hb == 0);
-
-    const uint16_t* __restrict__ al = (const uint16_t*)a.alpha + (int64_t)h * D;
-    const uint16_t* __restrict__ be = (const uint16_t*)a.beta + (int64_t)h * D;
-    // Row strides in bytes; every tile and block below addresses its rows
-    // through a buffer resource whose range ends at row T, so rows >= T read
-    // as zeros and are never written.
-    const int64_t qrow_b = (int64_t)a.Hq * D * 2, krow_b = (int64_t)a.Hkv * D * 2;
-    const int64_t kv_seq = (int64_t)b * T * a.Hkv * D + (int64_t)g * D;     // element offset of (b, 0, g)
-    const int64_t q_seq = (int64_t)b * T * a.Hq * D + (int64_t)h * D;        // element offset of (b, 0, h)
-    const int64_t c_seq = ((int64_t)b * a.Hkv + g) * a.cap * D;              // element offset of cache (b, g, 0)
-
-    const int vkp = tid & 15, vdc = tid >> 4;     // V staging: key pair, 8-wide d chunk
-    const bool vthread = vdc < D / 8;
-
-    // ---- global -> registers for one 32-key block
-    auto load_block = [&](int64_t kb, u32x4 (&kr)[KCH], u32x4 (&vr)[2]) {
-        const int64_t kbase = kb * 32;
-        const int64_t avail = (T - kbase) * krow_b - g * D * 2;
-        const rsrc_t rk = make_rsrc((const uint16_t*)a.k + kv_seq + kbase * a.Hkv * D, avail);
-        const rsrc_t rv = make_rsrc((const uint16_t*)a.v + kv_seq + kbase * a.Hkv * D, avail);
-#pragma unroll
-        for (int r = 0; r < KCH; ++r) {
-            const int c = tid + 256 * r, kk = c / C16, dc = c % C16;
-            kr[r] = buf_load16(rk, (uint32_t)(kk * krow_b + 16 * dc));
-        }
-        vr[0] = vr[1] = u32x4{0u, 0u, 0u, 0u};
-        if (vthread) {
-            vr[0] = buf_load16(rv, (uint32_t)(2 * vkp * krow_b + 16 * vdc));
-            vr[1] = buf_load16(rv, (uint32_t)((2 * vkp + 1) * krow_b + 16 * vdc));
-        }
-    };
-    // ---- registers -> ring slot (and to the cache when this workgroup owns the block)
-    auto store_block = [&](int64_t kb, bool own, const u32x4 (&kr)[KCH], const u32x4 (&vr)[2]) {
-        uint16_t* Ks = ring + (int)(kb % kSlots) * R::SLOT;
-        uint16_t* Vt = Ks + R::KBLK;
-#pragma unroll
-        for (int r = 0; r < KCH; ++r) {
-            const int c = tid + 256 * r, kk = c / C16, dc = c % C16;
-            *(u32x4*)(Ks + R::kofs(kk, dc)) = kr[r];
-        }
-        if (vthread) {
-            const int u = vkp >> 1, sub = 2 * (vkp & 1);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t w0 = vr[0][e], w1 = vr[1][e];
-                const int d0 = 8 * vdc + 2 * e;
-                *(uint32_t*)(Vt + R::vofs(d0, u) + sub) = (w0 & 0xffffu) | (w1 << 16);
-                *(uint32_t*)(Vt + R::vofs(d0 + 1, u) + sub) = (w0 >> 16) | (w1 & 0xffff0000u);
-            }
-        }
-        if (own && writer) {
-            const int64_t kbase = kb * 32;
-            const int64_t avail = (T - kbase) * D * 2;
-            const rsrc_t ck = make_rsrc((uint16_t*)a.k_cache + c_seq + kbase * D, avail);
-            const rsrc_t cv = make_rsrc((uint16_t*)a.v_cache + c_seq + kbase * D, avail);
-#pragma unroll
-            for (int r = 0; r < KCH; ++r) {
-                const int c = tid + 256 * r, kk = c / C16, dc = c % C16;
-                buf_store16(kr[r], ck, (uint32_t)(kk * D * 2 + 16 * dc));
-            }
-            if (vthread) {
-                buf_store16(vr[0], cv, (uint32_t)(2 * vkp * D * 2 + 16 * vdc));
-                buf_store16(vr[1], cv, (uint32_t)((2 * vkp + 1) * D * 2 + 16 * vdc));
-            }
-        }
-    };
-    // ---- raw Q rows of a tile: lane (n, half) holds q[row q0+n][16 i + 8 half + 0..7]
-    auto load_q = [&](int64_t q0, u32x4 (&qr)[NQ]) {
-        const rsrc_t rq = make_rsrc((const uint16_t*)a.q + q_seq + q0 * a.Hq * D, (T - q0) * qrow_b - h * D * 2);
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) qr[i] = buf_load16(rq, (uint32_t)(n * qrow_b + 32 * i + 16 * half));
-    };
-    // q_hat = (q * alpha + beta) * scale * log2(e), packed as MFMA B operands
-    auto scale_offset = [&](const u32x4 (&qr)[NQ], bf16x8 (&qf)[NQ]) {
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-            const int d0 = 16 * i + 8 * half;
-            const u32x4 av = *(const u32x4*)(al + d0);
-            const u32x4 bv = *(const u32x4*)(be + d0);
-            u32x4 r;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                r[e] = pack_bf16x2((bf16_lo(qr[i][e]) * bf16_lo(av[e]) + bf16_lo(bv[e])) * a.qscale,
-                                   (bf16_hi(qr[i][e]) * bf16_hi(av[e]) + bf16_hi(bv[e])) * a.qscale);
-            qf[i] = __builtin_bit_cast(bf16x8, r);
-        }
-    };
-
-    u32x4 kreg[KCH], vreg[2];
-    u32x4 qraw[NQ];
-    bf16x8 qf[NQ];
-
-    // ---- prologue: the first tile's window (halo blocks are not owned: no cache write)
-    {
-        const int64_t q0 = (int64_t)t_begin * 32;
-        const int64_t kb_lo = (q0 - W + 1 > 0 ? q0 - W + 1 : 0) >> 5, kb_hi = q0 >> 5;
-        load_q(q0, qraw);
-        for (int64_t kb = kb_lo; kb <= kb_hi; ++kb) {
-            load_block(kb, kreg, vreg);
-            store_block(kb, kb == kb_hi, kreg, vreg);
-        }
-        scale_offset(qraw, qf);
-        __syncthreads();
-    }
-
-    for (int tile = t_begin; tile < t_end; ++tile) {
-        const int64_t q0 = (int64_t)tile * 32;
-        const bool has_next = tile + 1 < t_end;
-        if (has_next) {
-            load_block((q0 >> 5) + 1, kreg, vreg);
-            load_q(q0 + 32, qraw);
-        }
-
-        const int64_t kb_lo = (q0 - W + 1 > 0 ? q0 - W + 1 : 0) >> 5, kb_hi = q0 >> 5;
-        f32x16 oacc[ND];
-#pragma unroll
-        for (int i = 0; i < ND; ++i) oacc[i] = f32x16{};
-        float m_run = kNegBig, l_run = 0.f;
-        for (int64_t kb = kb_lo; kb <= kb_hi; ++kb) {
-            const uint16_t* Ks = ring + (int)(kb % kSlots) * R::SLOT;
-            const uint16_t* Vt = Ks + R::KBLK;
-            f32x16 s = f32x16{};
-#pragma unroll
-            for (int i = 0; i < NQ; ++i) {
-                const bf16x8 kf = *(const bf16x8*)(Ks + R::kofs(n, 2 * i + half));
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[i], s, 0, 0, 0);
-            }
-            // register r of lane (n, half) is key 32 kb + 8 (r/4) + 4 half + r%4 of row q0 + n
-            const int dj = (int)(kb * 32 - q0);   // first key of the block relative to q0
-            const bool full = (dj + 31 <= 0) && (dj >= 31 - W + 1);
-            float mloc = kNegBig;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                if (!full) {
-                    const int j = dj + 8 * (r >> 2) + 4 * half + (r & 3);
-                    if (j > n || j < n - W + 1) s[r] = -INFINITY;
-                }
-                mloc = fmaxf(mloc, s[r]);
-            }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-            if (__any(mloc > m_run + kRescaleMargin)) {
-                const float m_new = fmaxf(m_run, mloc);
-                const float corr = fast_exp2(m_run - m_new);
-                m_run = m_new;
-                l_run *= corr;
-#pragma unroll
-                for (int i = 0; i < ND; ++i) oacc[i] *= corr;
-            }
-            u32x4 pw[2];
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = fast_exp2(s[r] - m_run), p1 = fast_exp2(s[r + 1] - m_run);
-                l_run += p0 + p1;
-                pw[r >> 3][(r & 7) >> 1] = pack_bf16x2(p0, p1);
-            }
-#pragma unroll
-            for (int dt = 0; dt < ND; ++dt) {
-                const int d = 32 * dt + n;
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const u32x2 lo = *(const u32x2*)(Vt + R::vofs(d, 4 * c + half));
-                    const u32x2 hi = *(const u32x2*)(Vt + R::vofs(d, 4 * c + 2 + half));
-                    const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, pw[c]),
-                                                                       oacc[dt], 0, 0, 0);
-                }
-            }
-        }
-        // ---- normalise and store the tile (rows >= T fall outside the resource)
-        const float l_tot = l_run + __shfl_xor(l_run, 32);
-        {
-            const float inv = 1.f / l_tot;
-            const rsrc_t ro = make_rsrc((uint16_t*)a.o + q_seq + q0 * a.Hq * D, (T - q0) * qrow_b - h * D * 2);
-#pragma unroll
-            for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    u32x2 w;
-                    w[0] = pack_bf16x2(oacc[dt][4 * i] * inv, oacc[dt][4 * i + 1] * inv);
-                    w[1] = pack_bf16x2(oacc[dt][4 * i + 2] * inv, oacc[dt][4 * i + 3] * inv);
-                    buf_store8(w, ro, (uint32_t)(n * qrow_b + 2 * (32 * dt + 8 * i + 4 * half)));
-                }
-        }
-        // the accumulator is dead from here on: keep the alpha/beta loads of the
-        // next tile's scale-offset below the stores so they reuse its registers
-        __builtin_amdgcn_sched_barrier(0);
-        if (has_next) scale_offset(qraw, qf);
-        __syncthreads();   // every wave is done with the slot the next block replaces
-        if (has_next) store_block((q0 >> 5) + 1, true, kreg, vreg);
-        __syncthreads();
-    }
-}
-
 // ---------------------------------------------------------------------------
 // 16x16x32 form: 8 waves = 4 query heads x 2 sub-tiles of 16 rows; the
 // window of a 32-row tile spans 10 blocks of 16 keys = 5 aligned pairs, kept
@@ -356,6 +117,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     };
     auto store_pair = [&](int64_t pr, bool own, const u32x4& kr, const u32x2 (&vr)[2]) {
         uint16_t* Ks = ring + (int)(pr % NS) * R::SLOT;
+        // recompute the thread's LDS offsets here rather than keep them live
+        // across the tile (they would only take registers the tile needs)
+        int t = tid;
+        asm volatile("" : "+v"(t));
+        const int kk = t / C16, dc = t % C16, kp = t & 15, dq = t >> 4;
         if (kthread) *(u32x4*)(Ks + R::kofs(kk, dc)) = kr;
         if (vthread) {
             uint16_t* Vt = Ks + R::KPART;
@@ -388,7 +154,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         for (int i = 0; i < NQ; ++i) qr[i] = buf_load16(rq, (uint32_t)(n * qrow_b + 64 * i + 16 * gq));
     };
     // q * alpha + beta, packed as MFMA B operands (the softmax scale is
-    // applied to the scores inside the exponent instead)
+    // applied to the scores inside the exponent instead).  Two head-dim
+    // slices at a time, so at most 16 registers of alpha/beta are live.
     auto scale_offset = [&](const u32x4 (&qr)[NQ], bf16x8 (&qf)[NQ]) {
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
@@ -401,6 +168,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                 r[e] = pack_bf16x2(__builtin_fmaf(bf16_lo(qr[i][e]), bf16_lo(av[e]), bf16_lo(bv[e])),
                                    __builtin_fmaf(bf16_hi(qr[i][e]), bf16_hi(av[e]), bf16_hi(bv[e])));
             qf[i] = __builtin_bit_cast(bf16x8, r);
+            if (i & 1) __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -408,6 +176,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     u32x2 vreg[2];
     u32x4 qraw[NQ];
     bf16x8 qf[NQ];
+    const bf16x8 kOnes = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
     {   // prologue: the first tile's window, one pair at a time (the halo is not owned)
         const int64_t q0 = (int64_t)t_begin * 32;
@@ -434,7 +203,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         f32x4 oacc[ND];
 #pragma unroll
         for (int i = 0; i < ND; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float m_run = kNegBig, l_run = 0.f;        // m_run in scaled (exp2) units
+        f32x4 lacc = f32x4{0.f, 0.f, 0.f, 0.f};    // row sums of the bf16 P, from an all-ones V^T tile
+        float m_run = kNegBig;                      // running maximum, in scaled (exp2) units
         for (int64_t pr = lo >> 5; pr <= (q0 >> 5); ++pr) {
             const uint16_t* Ks = ring + (int)(pr % NS) * R::SLOT;
             f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
@@ -449,15 +219,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             const int dj = (int)(pr * 32 - q0) - r0;
             const bool full = (dj + 31 <= 0) && (dj >= 15 - W + 1);
             if (!full) {
+                // key dj + 4 gq + e (e = r or 16 + r) is in row n's window iff
+                // n - w + 1 <= key <= n, i.e. (unsigned)(e - c) <= w - 1 with c = n - w + 1 - dj - 4 gq
+                const int c = n - W + 1 - dj - 4 * gq;
+                const uint32_t wm1 = (uint32_t)(W - 1);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int j0 = dj + 4 * gq + r, j1 = j0 + 16;
-                    if (j0 > n || j0 < n - W + 1) s0[r] = -INFINITY;
-                    if (j1 > n || j1 < n - W + 1) s1[r] = -INFINITY;
+                    if ((uint32_t)(r - c) > wm1) s0[r] = -INFINITY;
+                    if ((uint32_t)(16 + r - c) > wm1) s1[r] = -INFINITY;
                 }
             }
-            float lmax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(s0[0], s0[1]), __builtin_fmaxf(s0[2], s0[3])),
-                                         __builtin_fmaxf(__builtin_fmaxf(s1[0], s1[1]), __builtin_fmaxf(s1[2], s1[3])));
+            float lmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                               fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
             lmax *= qs;
             if (__any(lmax > m_run + kRescaleMargin)) {
                 float rmax = fmaxf(lmax, __shfl_xor(lmax, 16));
@@ -465,7 +238,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                 const float m_new = fmaxf(m_run, rmax);
                 const float corr = fast_exp2(m_run - m_new);
                 m_run = m_new;
-                l_run *= corr;
+                lacc *= corr;
 #pragma unroll
                 for (int i = 0; i < ND; ++i) oacc[i] *= corr;
             }
@@ -477,8 +250,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             }
             const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                               pack_bf16x2(p[6], p[7])};
-            l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
             const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+            lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pb, lacc, 0, 0, 0);
             const uint16_t* Vt = Ks + R::KPART;
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt) {
@@ -486,11 +259,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                 oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, oacc[dt], 0, 0, 0);
             }
         }
+        // The next tile's scale-offset runs before this tile's O stores: the
+        // vector-memory counter retires in issue order, so waiting for the
+        // alpha/beta loads after the stores would also wait for the stores.
+        __builtin_amdgcn_sched_barrier(0);
+        if (has_next) scale_offset(qraw, qf);
+        __builtin_amdgcn_sched_barrier(0);
         // ---- normalise and store the sub-tile (rows >= T fall outside the resource)
-        float l_tot = l_run + __shfl_xor(l_run, 16);
-        l_tot += __shfl_xor(l_tot, 32);
         {
-            const float inv = 1.f / l_tot;
+            const float inv = __builtin_amdgcn_rcpf(lacc[0]);
             const int64_t r0g = q0 + r0;
             const rsrc_t ro = make_rsrc((uint16_t*)a.o + q_seq + r0g * a.Hq * D, (T - r0g) * qrow_b - h * D * 2);
 #pragma unroll
@@ -501,8 +278,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                 buf_store8(w, ro, (uint32_t)(n * qrow_b + 2 * (16 * dt + 4 * gq)));
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if (has_next) scale_offset(qraw, qf);
         __syncthreads();   // every wave is done with the slot the next pair replaces
         if (has_next) store_pair((q0 >> 5) + 1, true, kreg, vreg);
         __syncthreads();
