@@ -55,6 +55,47 @@ template <> struct Row8<float> {
     }
 };
 
+// A lane's 8-wide slice of one scale-offset query, and its dot product with
+// a key row slice.  bf16 storage: the query slice is rounded to bf16 and the
+// product uses v_dot2_f32_bf16 (exact products, fp32 accumulate), as the
+// bf16 MFMA path rounds its query operand; fp32 storage: plain fp32 FMAs.
+template <typename E> struct QSlice;
+template <> struct QSlice<uint16_t> {
+    bf16x2 q[4];
+    __device__ void set(const float* x)
+    {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] = __builtin_bit_cast(bf16x2, pack_bf16x2(x[2 * e], x[2 * e + 1]));
+    }
+    __device__ float dot(const Row8<uint16_t>& k) const
+    {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // copy the lane out of the vector first: a bit_cast applied to a
+            // vector element directly reads element 0 with this compiler
+            const uint32_t kw = k.w[e];
+            acc = __builtin_amdgcn_fdot2_f32_bf16(q[e], __builtin_bit_cast(bf16x2, kw), acc, false);
+        }
+        return acc;
+    }
+};
+template <> struct QSlice<float> {
+    float q[8];
+    __device__ void set(const float* x)
+    {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = x[e];
+    }
+    __device__ float dot(const Row8<float>& k) const
+    {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += q[e] * k[e];
+        return acc;
+    }
+};
+
 __device__ __forceinline__ float ld_elem(const uint16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
 __device__ __forceinline__ float ld_elem(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ void st_elem(uint16_t* p, int64_t i, float x) { p[i] = (uint16_t)f32_to_bf16_bits(x); }
@@ -88,11 +129,9 @@ __device__ __forceinline__ void attend_chunk(const float (*qs)[D], const E* kc, 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int c = lane % LPK, kg = lane / LPK;
 
-    float qr[HG][8];
+    QSlice<E> qr[HG];
 #pragma unroll
-    for (int hh = 0; hh < HG; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qr[hh][e] = qs[hh][8 * c + e];
+    for (int hh = 0; hh < HG; ++hh) qr[hh].set(&qs[hh][8 * c]);
 
     float m[HG], l[HG], acc[HG][8];
 #pragma unroll
@@ -125,10 +164,7 @@ __device__ __forceinline__ void attend_chunk(const float (*qs)[D], const E* kc, 
             float mx = m[hh];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                float dot = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dot += qr[hh][e] * kx[u][e];
-                dot = group_sum<LPK>(dot);
+                const float dot = group_sum<LPK>(qr[hh].dot(kx[u]));
                 s[u] = ok[u] ? dot : -INFINITY;
                 mx = fmaxf(mx, s[u]);
             }
@@ -271,40 +307,80 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p)
 
 // --------------------------------------------------------------- LSE merge
 
-// One workgroup per (sequence, query head); thread d owns output element d.
-// kinds = 1: the copy only (prefill); kinds = 2: copy and base token (decode).
+// One workgroup (256 threads) per (sequence, query head):
+//   o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s,
+// over the splits s that hold keys of the query's range.  Thread t owns
+// head-dim values 4 (t % (D/4)) .. +3 of split group t / (D/4); the split
+// groups are then added in a fixed order, so the result is run-to-run
+// identical.  kinds = 1: the copy only (prefill); kinds = 2: the copy, then
+// the base token (decode), which also advances cache_len.
 template <typename E, int D>
-__global__ __launch_bounds__(D) void merge_kernel(const float* ws_part, const int32_t* ws_len,
-                                                  int32_t* cache_len, int64_t max_len, int window,
-                                                  int Hq, int chunk, int n_split, int kinds,
-                                                  E* o_out, E* o)
+__global__ __launch_bounds__(256) void merge_kernel(const float* ws_part, const int32_t* ws_len,
+                                                    int32_t* cache_len, int64_t max_len, int window,
+                                                    int Hq, int chunk, int n_split, int kinds,
+                                                    E* o_out, E* o)
 {
-    const int b = blockIdx.x / Hq, h = blockIdx.x % Hq, d = threadIdx.x;
+    constexpr int TPR = D / 4;            // threads per head-dim row
+    constexpr int NG = 256 / TPR;         // split groups
+    __shared__ float red[NG][D + 1];
+    __shared__ float wmax[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int b = blockIdx.x / Hq, h = blockIdx.x % Hq;
+    const int gp = tid / TPR, d4 = tid % TPR;
     const int64_t L = ws_len[b];
     const int64_t kind_stride = (int64_t)n_split * (D + 2);
     const float* part = ws_part + ((int64_t)b * Hq + h) * kinds * kind_stride;
-    const int64_t row = ((int64_t)b * Hq + h) * D + d;
+    const int64_t row = ((int64_t)b * Hq + h) * D;
     if (L < 0 || L > max_len) {
-        st_elem(o_out, row, __builtin_nanf(""));
-        if (kinds == 2) st_elem(o, row, __builtin_nanf(""));
+        for (int d = tid; d < D; d += 256) {
+            st_elem(o_out, row + d, __builtin_nanf(""));
+            if (kinds == 2) st_elem(o, row + d, __builtin_nanf(""));
+        }
         return;
     }
     for (int kind = 0; kind < kinds; ++kind) {
         const int64_t lo = kind == 0 ? 0 : (L - window + 1 > 0 ? L - window + 1 : 0);
         const int s0 = (int)(lo / chunk), s1 = (int)(L / chunk);
         const float* pk = part + kind * kind_stride;
-        float M = kNegBig;
-        for (int s = s0; s <= s1; ++s) M = fmaxf(M, pk[(int64_t)s * (D + 2)]);
-        float num = 0.f, den = 0.f;
-        for (int s = s0; s <= s1; ++s) {
+        // M = max over splits
+        float mx = kNegBig;
+        for (int s = s0 + tid; s <= s1; s += 256) mx = fmaxf(mx, pk[(int64_t)s * (D + 2)]);
+#pragma unroll
+        for (int x = 32; x > 0; x >>= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
+        if (lane == 0) wmax[wv] = mx;
+        __syncthreads();
+        const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+        // this thread's split group: weighted sums of 4 head-dim values and of l
+        float n0 = 0.f, n1 = 0.f, n2 = 0.f, n3 = 0.f, den = 0.f;
+        for (int s = s0 + gp; s <= s1; s += NG) {
             const float* ps = pk + (int64_t)s * (D + 2);
             const float f = fast_exp2(ps[0] - M);
+            const float2 a = *(const float2*)(ps + 2 + 4 * d4);
+            const float2 c = *(const float2*)(ps + 4 + 4 * d4);
             den += f * ps[1];
-            num += f * ps[2 + d];
+            n0 += f * a.x;
+            n1 += f * a.y;
+            n2 += f * c.x;
+            n3 += f * c.y;
         }
-        st_elem(kind == 0 ? o_out : o, row, num / den);
+        red[gp][4 * d4] = n0;
+        red[gp][4 * d4 + 1] = n1;
+        red[gp][4 * d4 + 2] = n2;
+        red[gp][4 * d4 + 3] = n3;
+        if (d4 == 0) red[gp][D] = den;
+        __syncthreads();
+        for (int d = tid; d < D; d += 256) {
+            float num = 0.f, dsum = 0.f;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                num += red[g][d];
+                dsum += red[g][D];
+            }
+            st_elem(kind == 0 ? o_out : o, row + d, num / dsum);
+        }
+        __syncthreads();
     }
-    if (cache_len && h == 0 && d == 0) cache_len[b] = (int32_t)(L + 1);
+    if (cache_len && h == 0 && tid == 0) cache_len[b] = (int32_t)(L + 1);
 }
 
 template <typename E, int D, int HG>
@@ -322,7 +398,7 @@ hipError_t launch_xattn_t(const XattnParams& p, hipStream_t st)
     }
     int64_t max_len = 0;
     for (int b = 0; b < p.B; ++b) max_len = p.pos[b] > max_len ? p.pos[b] : max_len;
-    hipLaunchKernelGGL((merge_kernel<E, D>), dim3(p.B * p.Hq), dim3(D), 0, st, p.ws_part, p.ws_len,
+    hipLaunchKernelGGL((merge_kernel<E, D>), dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part, p.ws_len,
                        (int32_t*)nullptr, max_len, 0, p.Hq, p.chunk, p.n_split, 1, (E*)p.o_out, (E*)nullptr);
     return hipGetLastError();
 }
@@ -335,7 +411,7 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t st)
                        st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((merge_kernel<E, D>), dim3(p.B * p.Hq), dim3(D), 0, st, p.ws_part, p.ws_len,
+    hipLaunchKernelGGL((merge_kernel<E, D>), dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part, p.ws_len,
                        p.cache_len, p.max_len, p.window, p.Hq, p.chunk, p.n_split, 2, (E*)p.o_out, (E*)p.o);
     return hipGetLastError();
 }
