@@ -17,6 +17,7 @@ the same workload on this machine's host cores (cpu_baseline).
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill|swa|xattn|decode|copy]
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "prefill attn tokens/s at 128K (SWA w=128 + 1 global query); decode us/step"
+PROFILES = os.path.join(ROOT, "profiles")
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
@@ -45,6 +47,28 @@ def swa_flops(B, T, Hq, d, w):
 def xattn_bytes(B, pos_plus_1, Hkv, d, es=2):
     """Algorithmic bytes of the copy's global read: K and V of keys [0, P]."""
     return B * pos_plus_1 * Hkv * d * 2 * es
+
+
+def measured_traffic(summary):
+    """HBM bytes per launch from a committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a copy kernel's reading), or None
+    when the kernel sources changed since those counters were taken."""
+    path = os.path.join(PROFILES, summary)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "#", " ")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if "traffic_bytes_per_launch" not in fields or "sources" not in fields:
+        return None
+    h = hashlib.sha256()
+    for f in fields["sources"].split():
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest()[:16] != fields.get("source_sha256_16"):
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def timed(fn, steps, warmup):
@@ -199,10 +223,18 @@ def main():
     if "swa" in out:
         s = out["swa"]
         result["roofline"] = {"bound": "hbm", "achieved": s["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                              "frac": s["GBps"] / HBM_PEAK_GBS, "traffic": None,
-                              "kernel": "orthros_swa_prefill (swa_bf16_kernel)",
+                              "frac": s["GBps"] / HBM_PEAK_GBS,
+                              "traffic": measured_traffic("traffic_swa_prefill_gqa_8b_128k.md"),
+                              "kernel": "orthros_swa_prefill (swa_ring16_kernel<128>)",
+                              "algorithmic_bytes": s["bytes"],
                               "mfma_algorithmic_TFLOPs": s["TFLOPs"],
                               "mfma_algorithmic_frac": s["TFLOPs"] / BF16_PEAK_TFLOPS}
+    if "xattn" in out:
+        x = out["xattn"]
+        result["roofline_xattn"] = {"bound": "hbm", "achieved": x["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": x["GBps"] / HBM_PEAK_GBS,
+                                    "traffic": measured_traffic("traffic_global_xattn_gqa_8b_128k.md"),
+                                    "kernel": "orthros_global_xattn (split-K + merge)"}
     if "decode" in out:
         result["decode_us_per_step"] = out["decode"]["us_per_step"]
     result["kernels"] = out
