@@ -19,19 +19,24 @@ class Prefill:
 
     x: the input dict of inputs.prefill_inputs (tensors already on `device`).
     cap: cache capacity (>= T); slots [T, cap) hold the sentinel and must
-    stay untouched.
+    stay untouched.  k_cache / v_cache: caller-owned caches to write into
+    instead (their capacity is used).
     """
 
-    def __init__(self, cfg, x, device="cuda", cap=None, softmax_scale=0.0):
+    def __init__(self, cfg, x, device="cuda", cap=None, softmax_scale=0.0, k_cache=None, v_cache=None):
         self.cfg = cfg
         self.x = x
         B, T = cfg["batch"], x["q"].shape[1]
         Hq, Hkv, d, dt = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["dtype"]
         self.T = T
         self.desc = desc_for(cfg, softmax_scale)
-        self.cap = cap or T
-        self.k_cache = empty_cache(B, Hkv, self.cap, d, dt, device)
-        self.v_cache = empty_cache(B, Hkv, self.cap, d, dt, device)
+        if k_cache is not None:
+            self.k_cache, self.v_cache = k_cache, v_cache
+            self.cap = k_cache.shape[2]
+        else:
+            self.cap = cap or T
+            self.k_cache = empty_cache(B, Hkv, self.cap, d, dt, device)
+            self.v_cache = empty_cache(B, Hkv, self.cap, d, dt, device)
         self.o = torch.empty(B, T, Hq, d, dtype=dt, device=device)
         self.o_out = torch.empty(B, Hq, d, dtype=dt, device=device)
         ws = binding.prefill_workspace_size(self.desc, T)

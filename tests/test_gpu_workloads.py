@@ -87,3 +87,47 @@ def test_gqa_8b_decode_b16_workload():
     assert torch.equal(dec.cache_len.cpu(), lc)
     assert torch.equal(bits(dec.k_cache.cpu()), bits(kc))
     assert torch.equal(bits(dec.v_cache.cpu()), bits(vc))
+
+
+def test_gqa_8b_prefill_1m_36_layers_resident():
+    """B1, 32/8 heads, d128, T = 2^20, w128, 36 layers whose caches (144 GiB)
+    all stay resident.  Every layer: cache bytes against its own K/V, and a
+    checksum re-read after all 36 layers (no layer overwrites another).
+    Layers 0, 17, 35: the copy's global query against the oracle in full and
+    Eq. (4) rows of three 512-row segments (start, middle, end)."""
+    cfg = dict(inputs.WORKLOADS["gqa_8b_prefill_1m"])
+    T, L, B, Hkv, d = cfg["T"], cfg["layers"], cfg["batch"], cfg["n_kv_heads"], cfg["head_dim"]
+    w = cfg["window"]
+    say("workload gqa_8b_prefill_1m: allocate 36 resident caches")
+    kc_all = torch.empty(L, B, Hkv, T, d, dtype=torch.bfloat16, device="cuda")
+    vc_all = torch.empty_like(kc_all)
+    sums = []
+    checked = {0, 17, 35}
+    for layer in range(L):
+        say(f"workload gqa_8b_prefill_1m: layer {layer}")
+        x = inputs.prefill_inputs(seed=1000 + layer, device="cuda", **cfg)
+        run = Prefill(cfg, x, k_cache=kc_all[layer], v_cache=vc_all[layer])
+        run.run()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(kc_all[layer]), bits(x["k"].transpose(1, 2)))
+        assert torch.equal(bits(vc_all[layer]), bits(x["v"].transpose(1, 2)))
+        sums.append((bits(kc_all[layer]).sum().item(), bits(vc_all[layer]).sum().item()))
+        if layer in checked:
+            k_h, v_h = x["k"].cpu(), x["v"].cpu()
+            q_out = x["q_out"].cpu()
+            ab = [x[n].cpu() for n in ("alpha", "beta", "alpha_out", "beta_out")]
+            ref = oracle.prefill(None, q_out, x["out_pos"], k_h, v_h, *ab, w, swa=False)
+            assert_parity(run.o_out, ref["o_out"], torch.bfloat16, f"layer {layer} o_out")
+            for s in (0, T // 2, T - 512):
+                lo = max(0, s - w + 1)
+                qs = x["q"][:, lo:s + 512].cpu().contiguous()
+                rows = torch.tensor([(0, t - lo, h) for t in range(s, s + 512) for h in range(cfg["n_q_heads"])])
+                ref_rows = oracle.swa_rows(qs, k_h[:, lo:s + 512].contiguous(), v_h[:, lo:s + 512].contiguous(),
+                                           ab[0], ab[1], w, rows)
+                got = run.o[0, s:s + 512].cpu().reshape(-1, d)
+                assert_parity(got, ref_rows, torch.bfloat16, f"layer {layer} o rows {s}..{s + 511}")
+        del run, x
+        torch.cuda.empty_cache()
+    say("workload gqa_8b_prefill_1m: re-read all caches")
+    for layer in range(L):
+        assert sums[layer] == (bits(kc_all[layer]).sum().item(), bits(vc_all[layer]).sum().item())
