@@ -4,8 +4,11 @@
 // ("Orthros:阶段感知异构注意力精读笔记" §2.3 Eq. (4), the fused cache
 // write of §2.1), organised for HBM streaming:
 //
-//   - a workgroup (4 waves = the 4 query heads it serves) walks one segment
-//     of one KV head's sequence, 32 rows at a time;
+//   - a workgroup of 4 waves walks one segment of one KV head's sequence,
+//     32 rows at a time, for the 4 query heads it serves: wave (sub-tile s,
+//     head pair p) owns rows 16 s .. 16 s + 15 of both heads of the pair,
+//     so every K/V fragment it reads from LDS feeds two MFMAs, and two
+//     workgroups share a CU (2 waves per SIMD, up to 256 registers each);
 //   - the window of a 32-row tile spans at most 5 blocks of 32 keys, kept in
 //     a 5-slot ring of K and V^T blocks in LDS (16 KB per slot at d = 128,
 //     XOR-swizzled instead of padded so that two workgroups fit in one CU's
@@ -13,11 +16,16 @@
 //     stays on chip between tiles;
 //   - while a tile computes, the next tile's new K/V block and its Q rows
 //     are already in flight into registers (one-tile software pipeline);
+//   - within a tile the diagonal pair goes first, so the running maxima
+//     and the accumulators start from it (no clearing, no rescale), and
+//     its causal mask is a fixed bias in the first S MFMA's accumulator;
 //   - softmax keeps a running maximum per row but rescales the accumulator
 //     only when a block's maximum exceeds it by more than 2^8 (the row sum
 //     and the accumulator share the stale maximum, so the final quotient is
 //     unchanged; probabilities stay <= 256, well inside bf16 and fp32);
 //   - the workgroup that brings a block in writes it to the cache.
+
+#include <type_traits>
 
 #include "device.h"
 #include "kernels.h"
@@ -29,10 +37,8 @@ constexpr int kSlots = 5;
 constexpr float kRescaleMargin = 8.0f;   // log2 units
 
 // ---------------------------------------------------------------------------
-// 16x16x32 form: 8 waves = 4 query heads x 2 sub-tiles of 16 rows; the
-// window of a 32-row tile spans 10 blocks of 16 keys = 5 aligned pairs, kept
-// in a 5-slot ring of 32-key pair slots.  Per wave it needs about half the
-// registers of the 32x32 form, so two workgroups (16 waves) fit on a CU.
+// 16x16x32 form: the window of a 32-row tile spans 10 blocks of 16 keys =
+// 5 aligned pairs, kept in a 5-slot ring of 32-key pair slots.
 //
 // S^T = K Q^T per 16-key block leaves each lane (n = query, gq = lane/16)
 // with keys 4gq..4gq+3 of the block; the P^T operand of O^T = V^T P^T over a
@@ -57,19 +63,23 @@ struct Pair {
 };
 
 template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void swa_ring16_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void swa_ring_kernel(
     SwaParams a, int n_tiles, int hblocks, int n_seg, int tps)
 {
     using R = Pair<D>;
     constexpr int NS = R::NSLOT;
-    constexpr int C16 = D / 8;     // 16-byte chunks per row
-    constexpr int NQ = D / 32;     // MFMA k-steps over the head dim (32 each)
-    constexpr int ND = D / 16;     // 16-wide d tiles of O^T
+    constexpr int NT = 256;
+    constexpr int C16 = D / 8;                 // 16-byte chunks per row
+    constexpr int NQ = D / 32;                 // MFMA k-steps over the head dim (32 each)
+    constexpr int ND = D / 16;                 // 16-wide d tiles of O^T
+    constexpr int KCH = 32 * C16 / NT;         // K chunks per thread per pair
+    constexpr int VCH = 16 * (D / 4) / NT;     // V (key pair, 4-wide d group) items per thread per pair
+    static_assert(KCH >= 1 && VCH >= 1, "head dim");
     __shared__ __align__(16) uint16_t ring[NS * R::SLOT];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hh = wv & 3, sub = wv >> 2;
+    const int hp = wv & 1, sub = wv >> 1;       // head pair, 16-row sub-tile
     const int n = lane & 15, gq = lane >> 4;
     int64_t id = blockIdx.x;
     const int seg = (int)(id % n_seg);
@@ -79,7 +89,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const int g = (int)(id % a.Hkv);
     const int b = (int)(id / a.Hkv);
     const int G = a.Hq / a.Hkv;
-    const int h = g * G + hb * 4 + hh;
+    const int h0 = g * G + hb * 4 + 2 * hp;     // the wave's heads: h0, h0 + 1
     const int64_t T = a.T;
     const int W = a.window;
     const int t_begin = seg * tps;
@@ -88,48 +98,54 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const bool writer = (hb == 0);
     const float qs = a.qscale;
 
-    const uint16_t* __restrict__ al = (const uint16_t*)a.alpha + (int64_t)h * D;
-    const uint16_t* __restrict__ be = (const uint16_t*)a.beta + (int64_t)h * D;
+    const uint16_t* __restrict__ al = (const uint16_t*)a.alpha + (int64_t)h0 * D;
+    const uint16_t* __restrict__ be = (const uint16_t*)a.beta + (int64_t)h0 * D;
     const int64_t qrow_b = (int64_t)a.Hq * D * 2, krow_b = (int64_t)a.Hkv * D * 2;
     const int64_t kv_seq = (int64_t)b * T * a.Hkv * D + (int64_t)g * D;
-    const int64_t q_seq = (int64_t)b * T * a.Hq * D + (int64_t)h * D;
+    const int64_t q_seq = (int64_t)b * T * a.Hq * D + (int64_t)h0 * D;
     const int64_t c_seq = ((int64_t)b * a.Hkv + g) * a.cap * D;
 
-    // staging of one pair (32 new keys): K chunk (kk, dc); V key pair kp x 4-wide d group dq
-    const int kk = tid / C16, dc = tid % C16;
-    const bool kthread = tid < 32 * C16;
-    const int kp = tid & 15, dq = tid >> 4;
-    const bool vthread = dq < D / 4;
-
-    auto load_pair = [&](int64_t pr, u32x4& kr, u32x2 (&vr)[2]) {
+    // staging of one pair (32 new keys): K chunk c = tid + 256 j -> (row c / C16, chunk c % C16);
+    // V item i = tid + 256 j -> key pair i & 15, 4-wide d group i >> 4
+    auto load_pair = [&](int64_t pr, u32x4 (&kr)[KCH], u32x2 (&vr)[VCH][2]) {
         const int64_t kbase = pr * 32;
         const int64_t avail = (T - kbase) * krow_b - g * D * 2;
         const rsrc_t rk = make_rsrc((const uint16_t*)a.k + kv_seq + kbase * a.Hkv * D, avail);
         const rsrc_t rv = make_rsrc((const uint16_t*)a.v + kv_seq + kbase * a.Hkv * D, avail);
-        kr = kthread ? buf_load16(rk, (uint32_t)(kk * krow_b + 16 * dc)) : u32x4{0u, 0u, 0u, 0u};
-        vr[0] = vr[1] = u32x2{0u, 0u};
-        if (vthread) {
-            vr[0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+#pragma unroll
+        for (int j = 0; j < KCH; ++j) {
+            const int c = tid + NT * j;
+            kr[j] = buf_load16(rk, (uint32_t)((c / C16) * krow_b + 16 * (c % C16)));
+        }
+#pragma unroll
+        for (int j = 0; j < VCH; ++j) {
+            const int it = tid + NT * j, kp = it & 15, dq = it >> 4;
+            vr[j][0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
                 rv, (int)(2 * kp * krow_b + 8 * dq), 0, 0));
-            vr[1] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+            vr[j][1] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
                 rv, (int)((2 * kp + 1) * krow_b + 8 * dq), 0, 0));
         }
     };
-    auto store_pair = [&](int64_t pr, bool own, const u32x4& kr, const u32x2 (&vr)[2]) {
+    auto store_pair = [&](int64_t pr, bool own, const u32x4 (&kr)[KCH], const u32x2 (&vr)[VCH][2]) {
         uint16_t* Ks = ring + (int)(pr % NS) * R::SLOT;
+        uint16_t* Vt = Ks + R::KPART;
         // recompute the thread's LDS offsets here rather than keep them live
         // across the tile (they would only take registers the tile needs)
         int t = tid;
         asm volatile("" : "+v"(t));
-        const int kk = t / C16, dc = t % C16, kp = t & 15, dq = t >> 4;
-        if (kthread) *(u32x4*)(Ks + R::kofs(kk, dc)) = kr;
-        if (vthread) {
-            uint16_t* Vt = Ks + R::KPART;
+#pragma unroll
+        for (int j = 0; j < KCH; ++j) {
+            const int c = t + NT * j;
+            *(u32x4*)(Ks + R::kofs(c / C16, c % C16)) = kr[j];
+        }
+#pragma unroll
+        for (int j = 0; j < VCH; ++j) {
+            const int it = t + NT * j, kp = it & 15, dq = it >> 4;
             const int key = 2 * kp, bb = key >> 4, lk = key & 15;
             const int pos = bb * 4 + (lk & 3);           // within the 16-byte unit lk / 4
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const uint32_t w0 = vr[0][e], w1 = vr[1][e];
+                const uint32_t w0 = vr[j][0][e], w1 = vr[j][1][e];
                 const int d0 = 4 * dq + 2 * e;
                 *(uint32_t*)(Vt + R::vofs(d0, lk >> 2) + pos) = (w0 & 0xffffu) | (w1 << 16);
                 *(uint32_t*)(Vt + R::vofs(d0 + 1, lk >> 2) + pos) = (w0 >> 16) | (w1 & 0xffff0000u);
@@ -140,43 +156,84 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             const int64_t avail = (T - kbase) * D * 2;
             const rsrc_t ck = make_rsrc((uint16_t*)a.k_cache + c_seq + kbase * D, avail);
             const rsrc_t cv = make_rsrc((uint16_t*)a.v_cache + c_seq + kbase * D, avail);
-            if (kthread) buf_store16(kr, ck, (uint32_t)(kk * D * 2 + 16 * dc));
-            if (vthread) {
-                __builtin_amdgcn_raw_buffer_store_b64(vr[0], cv, (int)(2 * kp * D * 2 + 8 * dq), 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b64(vr[1], cv, (int)((2 * kp + 1) * D * 2 + 8 * dq), 0, 0);
+#pragma unroll
+            for (int j = 0; j < KCH; ++j) {
+                const int c = t + NT * j;
+                buf_store16(kr[j], ck, (uint32_t)((c / C16) * D * 2 + 16 * (c % C16)));
+            }
+#pragma unroll
+            for (int j = 0; j < VCH; ++j) {
+                const int it = t + NT * j, kp = it & 15, dq = it >> 4;
+                __builtin_amdgcn_raw_buffer_store_b64(vr[j][0], cv, (int)(2 * kp * D * 2 + 8 * dq), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(vr[j][1], cv, (int)((2 * kp + 1) * D * 2 + 8 * dq), 0, 0);
             }
         }
     };
-    // raw Q rows of the wave's 16-row sub-tile: lane (n, gq) holds q[row][32 i + 8 gq + 0..7]
-    auto load_q = [&](int64_t r0, u32x4 (&qr)[NQ]) {
-        const rsrc_t rq = make_rsrc((const uint16_t*)a.q + q_seq + r0 * a.Hq * D, (T - r0) * qrow_b - h * D * 2);
+    // raw Q rows of the wave's 16-row sub-tile for both heads:
+    // lane (n, gq) holds q[row][head][32 i + 8 gq + 0..7]
+    auto load_q = [&](int64_t r0, u32x4 (&qr)[2][NQ]) {
+        const rsrc_t rq = make_rsrc((const uint16_t*)a.q + q_seq + r0 * a.Hq * D,
+                                    (T - r0) * qrow_b - h0 * D * 2);
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) qr[i] = buf_load16(rq, (uint32_t)(n * qrow_b + 64 * i + 16 * gq));
+        for (int hd = 0; hd < 2; ++hd)
+#pragma unroll
+            for (int i = 0; i < NQ; ++i)
+                qr[hd][i] = buf_load16(rq, (uint32_t)(n * qrow_b + hd * D * 2 + 64 * i + 16 * gq));
     };
     // q * alpha + beta, packed as MFMA B operands (the softmax scale is
-    // applied to the scores inside the exponent instead).  Two head-dim
-    // slices at a time, so at most 16 registers of alpha/beta are live.
-    auto scale_offset = [&](const u32x4 (&qr)[NQ], bf16x8 (&qf)[NQ]) {
+    // applied to the scores inside the exponent instead).  Element e is one
+    // v_dot2_f32_bf16 of (q_e masked to its half of the word) with the alpha
+    // word, accumulated onto beta_e.  All alpha/beta loads go out together
+    // (one L1/L2 round trip); the pair loop's registers are free by then.
+    auto scale_offset = [&](const u32x4 (&qr)[2][NQ], bf16x8 (&qf)[2][NQ]) {
+        u32x4 av[2][NQ], bv[2][NQ];
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-            const int d0 = 32 * i + 8 * gq;
-            const u32x4 av = *(const u32x4*)(al + d0);
-            const u32x4 bv = *(const u32x4*)(be + d0);
-            u32x4 r;
+        for (int hd = 0; hd < 2; ++hd)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                r[e] = pack_bf16x2(__builtin_fmaf(bf16_lo(qr[i][e]), bf16_lo(av[e]), bf16_lo(bv[e])),
-                                   __builtin_fmaf(bf16_hi(qr[i][e]), bf16_hi(av[e]), bf16_hi(bv[e])));
-            qf[i] = __builtin_bit_cast(bf16x8, r);
-            if (i & 1) __builtin_amdgcn_sched_barrier(0);
-        }
+            for (int i = 0; i < NQ; ++i) {
+                const int d0 = hd * D + 32 * i + 8 * gq;
+                av[hd][i] = *(const u32x4*)(al + d0);
+                bv[hd][i] = *(const u32x4*)(be + d0);
+            }
+#pragma unroll
+        for (int hd = 0; hd < 2; ++hd)
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                u32x4 r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t w = qr[hd][i][e], aw = av[hd][i][e], bw = bv[hd][i][e];
+                    const bf16x2 a2 = __builtin_bit_cast(bf16x2, aw);
+                    r[e] = pack_bf16x2(
+                        __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w & 0xffffu), a2, bf16_lo(bw),
+                                                        false),
+                        __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w & 0xffff0000u), a2,
+                                                        bf16_hi(bw), false));
+                }
+                qf[hd][i] = __builtin_bit_cast(bf16x8, r);
+            }
     };
 
-    u32x4 kreg;
-    u32x2 vreg[2];
-    u32x4 qraw[NQ];
-    bf16x8 qf[NQ];
+    u32x4 kreg[KCH];
+    u32x2 vreg[VCH][2];
+    u32x4 qraw[2][NQ];
+    bf16x8 qf[2][NQ];
     const bf16x8 kOnes = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+
+    // Causal mask of the diagonal pair (keys q0 .. q0 + 31 of a tile against
+    // the wave's rows q0 + 16 sub + n): the same for every tile.  -inf where
+    // the key is outside the row's window, else 0; it enters the pair's
+    // first S MFMA as the accumulator.
+    f32x4 dbias[2];
+    {
+        const int c = n - W + 1 + 16 * sub - 4 * gq;
+        const uint32_t wm1 = (uint32_t)(W - 1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            dbias[0][r] = (uint32_t)(r - c) > wm1 ? -INFINITY : 0.f;
+            dbias[1][r] = (uint32_t)(16 + r - c) > wm1 ? -INFINITY : 0.f;
+        }
+    }
 
     {   // prologue: the first tile's window, one pair at a time (the halo is not owned)
         const int64_t q0 = (int64_t)t_begin * 32;
@@ -200,65 +257,93 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         const int64_t lo = q0 - W + 1 > 0 ? q0 - W + 1 : 0;
         const int r0 = 16 * sub;                    // wave's first row relative to q0
 
-        f32x4 oacc[ND];
-#pragma unroll
-        for (int i = 0; i < ND; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        f32x4 lacc = f32x4{0.f, 0.f, 0.f, 0.f};    // row sums of the bf16 P, from an all-ones V^T tile
-        float m_run = kNegBig;                      // running maximum, in scaled (exp2) units
-        for (int64_t pr = lo >> 5; pr <= (q0 >> 5); ++pr) {
+        f32x4 oacc[2][ND];
+        f32x4 lacc[2];                              // row sums of the bf16 P, from an all-ones V^T tile
+        float m_run[2];                             // running maxima, in scaled (exp2) units
+        // One pair of 16-key blocks against both heads.  The diagonal pair
+        // goes first: every row has its own key there, so its row maxima
+        // start the running maxima, and its MFMAs start the accumulators
+        // from zero (no clearing, no rescale).
+        auto attend = [&](auto first_tag, int64_t pr) {
+            constexpr bool FIRST = decltype(first_tag)::value;
             const uint16_t* Ks = ring + (int)(pr % NS) * R::SLOT;
-            f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+            const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 s[2][2];
 #pragma unroll
             for (int i = 0; i < NQ; ++i) {
                 const bf16x8 k0 = *(const bf16x8*)(Ks + R::kofs(n, 4 * i + gq));
                 const bf16x8 k1 = *(const bf16x8*)(Ks + R::kofs(16 + n, 4 * i + gq));
-                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[i], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[i], s1, 0, 0, 0);
-            }
-            // s0[r]: key 32 pr + 4 gq + r, s1[r]: key 32 pr + 16 + 4 gq + r; row r0 + n (relative to q0)
-            const int dj = (int)(pr * 32 - q0) - r0;
-            const bool full = (dj + 31 <= 0) && (dj >= 15 - W + 1);
-            if (!full) {
-                // key dj + 4 gq + e (e = r or 16 + r) is in row n's window iff
-                // n - w + 1 <= key <= n, i.e. (unsigned)(e - c) <= w - 1 with c = n - w + 1 - dj - 4 gq
-                const int c = n - W + 1 - dj - 4 * gq;
-                const uint32_t wm1 = (uint32_t)(W - 1);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if ((uint32_t)(r - c) > wm1) s0[r] = -INFINITY;
-                    if ((uint32_t)(16 + r - c) > wm1) s1[r] = -INFINITY;
+                for (int hd = 0; hd < 2; ++hd) {
+                    const f32x4 c0 = i ? s[hd][0] : (FIRST ? dbias[0] : zero);
+                    const f32x4 c1 = i ? s[hd][1] : (FIRST ? dbias[1] : zero);
+                    s[hd][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[hd][i], c0, 0, 0, 0);
+                    s[hd][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[hd][i], c1, 0, 0, 0);
                 }
             }
-            float lmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                               fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-            lmax *= qs;
-            if (__any(lmax > m_run + kRescaleMargin)) {
-                float rmax = fmaxf(lmax, __shfl_xor(lmax, 16));
-                rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
-                const float m_new = fmaxf(m_run, rmax);
-                const float corr = fast_exp2(m_run - m_new);
-                m_run = m_new;
-                lacc *= corr;
+            // s[.][0][r]: key 32 pr + 4 gq + r, s[.][1][r]: key 32 pr + 16 + 4 gq + r; row r0 + n (relative to q0)
+            if constexpr (!FIRST) {
+                const int dj = (int)(pr * 32 - q0) - r0;
+                const bool full = (dj + 31 <= 0) && (dj >= 15 - W + 1);
+                if (!full) {
+                    // key dj + 4 gq + e (e = r or 16 + r) is in row n's window iff
+                    // n - w + 1 <= key <= n, i.e. (unsigned)(e - c) <= w - 1 with c = n - w + 1 - dj - 4 gq
+                    const int c = n - W + 1 - dj - 4 * gq;
+                    const uint32_t wm1 = (uint32_t)(W - 1);
 #pragma unroll
-                for (int i = 0; i < ND; ++i) oacc[i] *= corr;
-            }
-            float p[8];
+                    for (int r = 0; r < 4; ++r) {
+                        const bool m0 = (uint32_t)(r - c) > wm1, m1 = (uint32_t)(16 + r - c) > wm1;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                p[r] = fast_exp2(__builtin_fmaf(s0[r], qs, -m_run));
-                p[4 + r] = fast_exp2(__builtin_fmaf(s1[r], qs, -m_run));
+                        for (int hd = 0; hd < 2; ++hd) {
+                            if (m0) s[hd][0][r] = -INFINITY;
+                            if (m1) s[hd][1][r] = -INFINITY;
+                        }
+                    }
+                }
             }
-            const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                              pack_bf16x2(p[6], p[7])};
-            const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-            lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pb, lacc, 0, 0, 0);
+            bf16x8 pb[2];
+#pragma unroll
+            for (int hd = 0; hd < 2; ++hd) {
+                const f32x4 s0 = s[hd][0], s1 = s[hd][1];
+                float lmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                                   fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+                lmax *= qs;
+                if constexpr (FIRST) {
+                    float rmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+                    m_run[hd] = fmaxf(rmax, __shfl_xor(rmax, 32));
+                } else if (__any(lmax > m_run[hd] + kRescaleMargin)) {
+                    float rmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+                    rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+                    const float m_new = fmaxf(m_run[hd], rmax);
+                    const float corr = fast_exp2(m_run[hd] - m_new);
+                    m_run[hd] = m_new;
+                    lacc[hd] *= corr;
+#pragma unroll
+                    for (int i = 0; i < ND; ++i) oacc[hd][i] *= corr;
+                }
+                float p[8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    p[r] = fast_exp2(__builtin_fmaf(s0[r], qs, -m_run[hd]));
+                    p[4 + r] = fast_exp2(__builtin_fmaf(s1[r], qs, -m_run[hd]));
+                }
+                const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                  pack_bf16x2(p[6], p[7])};
+                pb[hd] = __builtin_bit_cast(bf16x8, pw);
+                lacc[hd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pb[hd], FIRST ? zero : lacc[hd], 0, 0, 0);
+            }
             const uint16_t* Vt = Ks + R::KPART;
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt) {
                 const bf16x8 vf = *(const bf16x8*)(Vt + R::vofs(16 * dt + n, gq));
-                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, oacc[dt], 0, 0, 0);
+#pragma unroll
+                for (int hd = 0; hd < 2; ++hd)
+                    oacc[hd][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[hd], FIRST ? zero : oacc[hd][dt],
+                                                                           0, 0, 0);
             }
-        }
+        };
+        attend(std::true_type{}, q0 >> 5);
+        for (int64_t pr = lo >> 5; pr < (q0 >> 5); ++pr) attend(std::false_type{}, pr);
         // The next tile's scale-offset runs before this tile's O stores: the
         // vector-memory counter retires in issue order, so waiting for the
         // alpha/beta loads after the stores would also wait for the stores.
@@ -267,15 +352,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         __builtin_amdgcn_sched_barrier(0);
         // ---- normalise and store the sub-tile (rows >= T fall outside the resource)
         {
-            const float inv = __builtin_amdgcn_rcpf(lacc[0]);
             const int64_t r0g = q0 + r0;
-            const rsrc_t ro = make_rsrc((uint16_t*)a.o + q_seq + r0g * a.Hq * D, (T - r0g) * qrow_b - h * D * 2);
+            const rsrc_t ro = make_rsrc((uint16_t*)a.o + q_seq + r0g * a.Hq * D,
+                                        (T - r0g) * qrow_b - h0 * D * 2);
 #pragma unroll
-            for (int dt = 0; dt < ND; ++dt) {
-                u32x2 w;
-                w[0] = pack_bf16x2(oacc[dt][0] * inv, oacc[dt][1] * inv);
-                w[1] = pack_bf16x2(oacc[dt][2] * inv, oacc[dt][3] * inv);
-                buf_store8(w, ro, (uint32_t)(n * qrow_b + 2 * (16 * dt + 4 * gq)));
+            for (int hd = 0; hd < 2; ++hd) {
+                const float inv = __builtin_amdgcn_rcpf(lacc[hd][0]);
+#pragma unroll
+                for (int dt = 0; dt < ND; ++dt) {
+                    u32x2 w;
+                    w[0] = pack_bf16x2(oacc[hd][dt][0] * inv, oacc[hd][dt][1] * inv);
+                    w[1] = pack_bf16x2(oacc[hd][dt][2] * inv, oacc[hd][dt][3] * inv);
+                    buf_store8(w, ro, (uint32_t)(n * qrow_b + hd * D * 2 + 2 * (16 * dt + 4 * gq)));
+                }
             }
         }
         __syncthreads();   // every wave is done with the slot the next pair replaces
@@ -302,10 +391,10 @@ hipError_t launch_swa_ring(const SwaParams& p, hipStream_t s)
     n_seg = (n_tiles + tps - 1) / tps;
     const int64_t n_wg = streams * n_seg;
     if (p.D == 64)
-        hipLaunchKernelGGL((swa_ring16_kernel<64>), dim3((unsigned)n_wg), dim3(512), 0, s, p, n_tiles, hblocks,
+        hipLaunchKernelGGL((swa_ring_kernel<64>), dim3((unsigned)n_wg), dim3(256), 0, s, p, n_tiles, hblocks,
                            n_seg, tps);
     else
-        hipLaunchKernelGGL((swa_ring16_kernel<128>), dim3((unsigned)n_wg), dim3(512), 0, s, p, n_tiles, hblocks,
+        hipLaunchKernelGGL((swa_ring_kernel<128>), dim3((unsigned)n_wg), dim3(256), 0, s, p, n_tiles, hblocks,
                            n_seg, tps);
     return hipGetLastError();
 }
