@@ -88,6 +88,17 @@ size_t len_bytes(const orthros_desc* d)
 
 struct Split { int chunk, n_split; size_t bytes; };
 
+orthros::Dt dt_of(const orthros_desc* d) { return d->dtype == ORTHROS_F32 ? orthros::Dt::F32 : orthros::Dt::BF16; }
+
+bool fused_prefill(const orthros_desc* d)
+{
+    return orthros::ring_applies(dt_of(d), d->n_q_heads, d->n_kv_heads, d->window);
+}
+
+// Key splits of the output copy in prefill.  The separate cross-attention
+// kernel uses power-of-two chunks; the fused path (streaming SWA kernel with
+// the copy's query folded in) leaves one partial per segment of its launch.
+// The workspace covers whichever the call takes.
 Split prefill_split(const orthros_desc* d, int64_t T)
 {
     Split s;
@@ -95,6 +106,24 @@ Split prefill_split(const orthros_desc* d, int64_t T)
     s.n_split = (int)((T + s.chunk - 1) / s.chunk);
     s.bytes = len_bytes(d) + (size_t)d->batch * d->n_q_heads * s.n_split * (d->head_dim + 2) * 4;
     return s;
+}
+
+Split fused_split(const orthros_desc* d, int64_t T)
+{
+    const orthros::RingGeom r = orthros::ring_geometry(d->batch, d->n_q_heads, d->n_kv_heads, T);
+    Split s;
+    s.chunk = 32 * r.tps;
+    s.n_split = r.n_seg;
+    s.bytes = len_bytes(d) + (size_t)d->batch * d->n_q_heads * s.n_split * (d->head_dim + 2) * 4;
+    return s;
+}
+
+size_t prefill_ws_bytes(const orthros_desc* d, int64_t T)
+{
+    const size_t a = prefill_split(d, T).bytes;
+    if (!fused_prefill(d)) return a;
+    const size_t b = fused_split(d, T).bytes;
+    return a > b ? a : b;
 }
 
 Split decode_split(const orthros_desc* d, int64_t max_len)
@@ -161,15 +190,15 @@ orthros_status validate_xattn(const orthros_desc* d, int64_t T, const void* q_ou
     if ((st = check_ptrs({q_out, alpha_out, beta_out, k_cache, v_cache, o_out}))) return st;
     if (!ws) return fail(ORTHROS_E_WORKSPACE, "workspace is NULL");
     if ((st = check_ptrs({ws}))) return st;
-    const Split sp = prefill_split(d, T);
-    if (ws_bytes < sp.bytes)
-        return fail(ORTHROS_E_WORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, sp.bytes);
+    const size_t need = prefill_ws_bytes(d, T);
+    if (ws_bytes < need)
+        return fail(ORTHROS_E_WORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, need);
     return ORTHROS_OK;
 }
 
-orthros_status run_swa(const orthros_desc* d, int64_t T, const void* q, const void* k, const void* v,
-                       const void* alpha, const void* beta, void* k_cache, void* v_cache, int64_t cap, void* o,
-                       hipStream_t s)
+orthros::SwaParams swa_params(const orthros_desc* d, int64_t T, const void* q, const void* k, const void* v,
+                              const void* alpha, const void* beta, void* k_cache, void* v_cache, int64_t cap,
+                              void* o)
 {
     orthros::SwaParams p;
     p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
@@ -177,15 +206,14 @@ orthros_status run_swa(const orthros_desc* d, int64_t T, const void* q, const vo
     p.T = T; p.cap = cap;
     p.B = d->batch; p.Hq = d->n_q_heads; p.Hkv = d->n_kv_heads; p.D = d->head_dim; p.window = d->window;
     p.qscale = qscale_of(d);
-    p.dt = d->dtype == ORTHROS_F32 ? orthros::Dt::F32 : orthros::Dt::BF16;
-    return hip_status(orthros::launch_swa(p, s), "sliding-window kernel launch");
+    p.dt = dt_of(d);
+    return p;
 }
 
-orthros_status run_xattn(const orthros_desc* d, int64_t T, const void* q_out, const int64_t* out_pos,
-                         const void* alpha_out, const void* beta_out, const void* k_cache, const void* v_cache,
-                         int64_t cap, void* o_out, void* ws, hipStream_t s)
+orthros::XattnParams xattn_params(const orthros_desc* d, const Split& sp, const void* q_out,
+                                  const int64_t* out_pos, const void* alpha_out, const void* beta_out,
+                                  const void* k_cache, const void* v_cache, int64_t cap, void* o_out, void* ws)
 {
-    const Split sp = prefill_split(d, T);
     orthros::XattnParams p;
     p.q_out = q_out; p.alpha_out = alpha_out; p.beta_out = beta_out;
     p.k_cache = k_cache; p.v_cache = v_cache; p.o_out = o_out;
@@ -196,7 +224,24 @@ orthros_status run_xattn(const orthros_desc* d, int64_t T, const void* q_out, co
     p.B = d->batch; p.Hq = d->n_q_heads; p.Hkv = d->n_kv_heads; p.D = d->head_dim;
     p.chunk = sp.chunk; p.n_split = sp.n_split;
     p.qscale = qscale_of(d);
-    p.dt = d->dtype == ORTHROS_F32 ? orthros::Dt::F32 : orthros::Dt::BF16;
+    p.dt = dt_of(d);
+    return p;
+}
+
+orthros_status run_swa(const orthros_desc* d, int64_t T, const void* q, const void* k, const void* v,
+                       const void* alpha, const void* beta, void* k_cache, void* v_cache, int64_t cap, void* o,
+                       hipStream_t s)
+{
+    const orthros::SwaParams p = swa_params(d, T, q, k, v, alpha, beta, k_cache, v_cache, cap, o);
+    return hip_status(orthros::launch_swa(p, s), "sliding-window kernel launch");
+}
+
+orthros_status run_xattn(const orthros_desc* d, int64_t T, const void* q_out, const int64_t* out_pos,
+                         const void* alpha_out, const void* beta_out, const void* k_cache, const void* v_cache,
+                         int64_t cap, void* o_out, void* ws, hipStream_t s)
+{
+    const orthros::XattnParams p = xattn_params(d, prefill_split(d, T), q_out, out_pos, alpha_out, beta_out,
+                                                k_cache, v_cache, cap, o_out, ws);
     return hip_status(orthros::launch_xattn(p, s), "cross-attention kernel launch");
 }
 
@@ -207,7 +252,7 @@ extern "C" {
 size_t orthros_prefill_workspace_size(const orthros_desc* desc, int64_t T)
 {
     if (check_desc(desc) || T < 1 || T > INT32_MAX) return 0;
-    return prefill_split(desc, T).bytes;
+    return prefill_ws_bytes(desc, T);
 }
 
 size_t orthros_decode_workspace_size(const orthros_desc* desc, int64_t max_len)
@@ -251,6 +296,14 @@ orthros_status orthros_prefill(const orthros_desc* desc, int64_t T, const void* 
     st = validate_xattn(desc, T, q_out, out_pos, alpha_out, beta_out, k_cache, v_cache, cap, o_out, workspace,
                         workspace_bytes);
     if (st) return st;
+    if (fused_prefill(desc)) {
+        // one pass over K/V: the streaming SWA kernel also attends the copy's
+        // query to the pairs it brings in, then the LSE merge
+        const orthros::SwaParams p = swa_params(desc, T, q, k, v, alpha, beta, k_cache, v_cache, cap, o);
+        const orthros::XattnParams x = xattn_params(desc, fused_split(desc, T), q_out, out_pos, alpha_out,
+                                                    beta_out, k_cache, v_cache, cap, o_out, workspace);
+        return hip_status(orthros::launch_swa_ring_fused(p, x, (hipStream_t)stream), "fused prefill kernel launch");
+    }
     st = run_swa(desc, T, q, k, v, alpha, beta, k_cache, v_cache, cap, o, (hipStream_t)stream);
     if (st) return st;
     return run_xattn(desc, T, q_out, out_pos, alpha_out, beta_out, k_cache, v_cache, cap, o_out, workspace,

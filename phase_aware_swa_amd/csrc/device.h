@@ -65,11 +65,14 @@ __device__ __forceinline__ void buf_store8(u32x2 v, rsrc_t r, uint32_t off)
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)off, 0, 0);
 }
 
-// DPP lane movement inside a row of 16 lanes.
+// DPP lane movement inside a row of 16 lanes.  Every pattern used here
+// reads a lane of the same row, so bound_ctrl never applies; written this
+// way (old = 0, bound_ctrl set) the compiler folds the move into the DPP
+// form of the instruction that consumes it (v_add_f32_dpp).
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x)
 {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]

@@ -444,6 +444,21 @@ hipError_t launch_xattn(const XattnParams& p, hipStream_t st)
     return p.D == 64 ? xattn_by_hg<uint16_t, 64>(p, st) : xattn_by_hg<uint16_t, 128>(p, st);
 }
 
+hipError_t launch_merge(const XattnParams& p, hipStream_t st)
+{
+    int64_t max_len = 0;
+    for (int b = 0; b < p.B; ++b) max_len = p.pos[b] > max_len ? p.pos[b] : max_len;
+    if (p.D == 64)
+        hipLaunchKernelGGL((merge_kernel<uint16_t, 64>), dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part, p.ws_len,
+                           (int32_t*)nullptr, max_len, 0, p.Hq, p.chunk, p.n_split, 1, (uint16_t*)p.o_out,
+                           (uint16_t*)nullptr);
+    else
+        hipLaunchKernelGGL((merge_kernel<uint16_t, 128>), dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part,
+                           p.ws_len, (int32_t*)nullptr, max_len, 0, p.Hq, p.chunk, p.n_split, 1,
+                           (uint16_t*)p.o_out, (uint16_t*)nullptr);
+    return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st)
 {
     if (p.dt == Dt::F32) return p.D == 64 ? decode_by_hg<float, 64>(p, st) : decode_by_hg<float, 128>(p, st);

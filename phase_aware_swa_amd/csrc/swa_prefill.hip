@@ -377,7 +377,7 @@ hipError_t launch_swa(const SwaParams& p, hipStream_t s)
 {
     if (p.dt == Dt::F32) return p.D == 64 ? launch_f32<64>(p, s) : launch_f32<128>(p, s);
     const int HS = swa_heads_per_wg(p.Hq / p.Hkv);
-    if (HS == 4 && p.window <= kRingMaxWindow) return launch_swa_ring(p, s);
+    if (ring_applies(p.dt, p.Hq, p.Hkv, p.window)) return launch_swa_ring(p, s);
     if (p.D == 64) {
         if (HS == 4) return launch_bf16<64, 4>(p, s);
         if (HS == 2) return launch_bf16<64, 2>(p, s);

@@ -62,9 +62,20 @@ struct Pair {
     __device__ static int vofs(int d, int u) { return d * 32 + ((u ^ ((d >> 2) & 3)) << 3); }
 };
 
-template <int D>
+// Output-copy side of the fused kernel: the copy's raw query and its
+// scale-offset, where the partials go, and the copy positions of the batch
+// rows b0 .. b0 + nb - 1 this launch covers.
+struct GlobalArgs {
+    const void* q_out;    // [B][Hq][D]
+    const void* alpha_out;
+    const void* beta_out;
+    float* ws_part;       // [B][Hq][1][n_seg][D+2]: m (exp2 units), l, acc
+    int32_t* ws_len;      // [B]: the copy position, for the merge
+};
+
+template <int D, bool GQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void swa_ring_kernel(
-    SwaParams a, int n_tiles, int hblocks, int n_seg, int tps)
+    SwaParams a, int n_tiles, int hblocks, int n_seg, int tps, int b0, GlobalArgs ga, PosBlock pos)
 {
     using R = Pair<D>;
     constexpr int NS = R::NSLOT;
@@ -87,9 +98,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int hb = (int)(id % hblocks);
     id /= hblocks;
     const int g = (int)(id % a.Hkv);
-    const int b = (int)(id / a.Hkv);
+    const int b = b0 + (int)(id / a.Hkv);
     const int G = a.Hq / a.Hkv;
-    const int h0 = g * G + hb * 4 + 2 * hp;     // the wave's heads: h0, h0 + 1
+    const int hbase = g * G + hb * 4;
+    const int h0 = hbase + 2 * hp;              // the wave's heads: h0, h0 + 1
     const int64_t T = a.T;
     const int W = a.window;
     const int t_begin = seg * tps;
@@ -235,6 +247,106 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     }
 
+    // ---- the output copy's global query (Eq. (5)), fused: wave w serves
+    // head hbase + w over every key of the pairs this workgroup brings in
+    // (keys j <= P only).  Scores: lanes (group kg, chunk kc) dot 16-byte K
+    // chunks with the scaled query, a DPP sum over the LPK lanes of a key;
+    // the online softmax state (gm, gl) is wave-uniform; P goes to scalar
+    // registers as bf16 pairs, and lane l accumulates rows l + 64 r of
+    // V^T P with v_dot2_f32_bf16.
+    constexpr int LPK = D / 8;                  // lanes per key (16-byte chunks of a row)
+    constexpr int STEPS = 32 * LPK / 64;        // keys of the pair per lane group
+    constexpr int RPL = D / 64;                 // V^T rows per lane
+    const int kg = lane / LPK, kc = lane % LPK;
+    u32x4 gqq = u32x4{0u, 0u, 0u, 0u};          // q' * alpha' + beta', d = 8 kc .. 8 kc + 7
+    float gm = kNegBig, gl = 0.f, gacc[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) gacc[r] = 0.f;
+    int64_t P = -1;
+    if constexpr (GQ) {
+        const int hg = hbase + wv;
+        P = pos.v[b - b0];
+        const int64_t o = (int64_t)hg * D + 8 * kc;
+        const u32x4 qw = *(const u32x4*)((const uint16_t*)ga.q_out + (int64_t)b * a.Hq * D + o);
+        const u32x4 aw = *(const u32x4*)((const uint16_t*)ga.alpha_out + o);
+        const u32x4 bw = *(const u32x4*)((const uint16_t*)ga.beta_out + o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t w = qw[e], av = aw[e], bv = bw[e];
+            gqq[e] = pack_bf16x2(__builtin_fmaf(bf16_lo(w), bf16_lo(av), bf16_lo(bv)),
+                                 __builtin_fmaf(bf16_hi(w), bf16_hi(av), bf16_hi(bv)));
+        }
+    }
+    auto global_pair = [&](int64_t pr) {
+        const uint16_t* Ks = ring + (int)(pr % NS) * R::SLOT;
+        // keys past P only in the pair that holds P: lim = last valid key of the pair
+        const int64_t lim64 = P - pr * 32;
+        const int lim = lim64 < 31 ? (int)lim64 : 31;
+        float sc[STEPS];
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            const int key = kg * STEPS + st;
+            const u32x4 kw = *(const u32x4*)(Ks + R::kofs(key, kc));
+            float part = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t x = kw[e], y = gqq[e];
+                part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y),
+                                                       part, false);
+            }
+            part = group_sum<LPK>(part);
+            sc[st] = key <= lim ? part : -INFINITY;
+        }
+        float lmax = sc[0];
+#pragma unroll
+        for (int st = 1; st < STEPS; ++st) lmax = fmaxf(lmax, sc[st]);
+#pragma unroll
+        for (int x = LPK; x < 64; x <<= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, x));
+        lmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lmax * qs)));
+        if (lmax > gm + kRescaleMargin) {
+            const float corr = fast_exp2(gm - lmax);
+            gm = lmax;
+            gl *= corr;
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) gacc[r] *= corr;
+        }
+        float p[STEPS], lsum = 0.f;
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            p[st] = fast_exp2(__builtin_fmaf(sc[st], qs, -gm));
+            lsum += p[st];
+        }
+#pragma unroll
+        for (int x = LPK; x < 64; x <<= 1) lsum += __shfl_xor(lsum, x);
+        gl += __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lsum)));
+        // bf16 pairs (keys 2 j, 2 j + 1) of the whole pair, wave-uniform
+        uint32_t pw[16];
+#pragma unroll
+        for (int j = 0; j < STEPS / 2; ++j) {
+            const int wrd = (int)pack_bf16x2(p[2 * j], p[2 * j + 1]);
+#pragma unroll
+            for (int grp = 0; grp < 64 / LPK; ++grp)
+                pw[grp * (STEPS / 2) + j] = (uint32_t)__builtin_amdgcn_readlane(wrd, grp * LPK);
+        }
+        const uint16_t* Vt = Ks + R::KPART;
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            const int d = lane + 64 * r;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                // unit u of V^T row d: keys (4u, 4u+1), (4u+2, 4u+3), (16+4u, 17+4u), (18+4u, 19+4u)
+                const u32x4 vw = *(const u32x4*)(Vt + R::vofs(d, u));
+                const int jj[4] = {2 * u, 2 * u + 1, 8 + 2 * u, 9 + 2 * u};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t x = vw[e], y = pw[jj[e]];
+                    gacc[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x),
+                                                              __builtin_bit_cast(bf16x2, y), gacc[r], false);
+                }
+            }
+        }
+    };
+
     {   // prologue: the first tile's window, one pair at a time (the halo is not owned)
         const int64_t q0 = (int64_t)t_begin * 32;
         const int64_t lo = q0 - W + 1 > 0 ? q0 - W + 1 : 0;
@@ -367,10 +479,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 }
             }
         }
+        if constexpr (GQ) {
+            if (q0 <= P) global_pair(q0 >> 5);     // this tile's own pair
+        }
         __syncthreads();   // every wave is done with the slot the next pair replaces
         if (has_next) store_pair((q0 >> 5) + 1, true, kreg, vreg);
         __syncthreads();
     }
+    if constexpr (GQ) {
+        float* part = ga.ws_part + (((int64_t)b * a.Hq + hbase + wv) * n_seg + seg) * (D + 2);
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) part[2 + lane + 64 * r] = gacc[r];
+        if (lane == 0) {
+            part[0] = gm;
+            part[1] = gl;
+        }
+        if (seg == 0 && g == 0 && hb == 0 && tid == 0) ga.ws_len[b] = (int32_t)P;
+    }
+}
+
+}  // namespace
+
+RingGeom ring_geometry(int B, int Hq, int Hkv, int64_t T)
+{
+    RingGeom r;
+    r.hblocks = (Hq / Hkv) / 4;
+    r.n_tiles = (int)((T + 31) / 32);
+    const int64_t streams = (int64_t)B * Hkv * r.hblocks;
+    constexpr int64_t kTargetWgs = 512;
+    int n_seg = (int)((kTargetWgs + streams - 1) / streams);
+    if (n_seg > r.n_tiles) n_seg = r.n_tiles;
+    if (n_seg < 1) n_seg = 1;
+    r.tps = (r.n_tiles + n_seg - 1) / n_seg;
+    r.n_seg = (r.n_tiles + r.tps - 1) / r.tps;
+    return r;
+}
+
+namespace {
+
+template <bool GQ>
+hipError_t launch_ring(const SwaParams& p, const GlobalArgs& ga, const int64_t* pos_host, hipStream_t s)
+{
+    const RingGeom r = ring_geometry(p.B, p.Hq, p.Hkv, p.T);
+    const int per_launch = GQ ? kPosPerLaunch : p.B;
+    for (int b0 = 0; b0 < p.B; b0 += per_launch) {
+        const int nb = p.B - b0 < per_launch ? p.B - b0 : per_launch;
+        PosBlock pos;
+        for (int i = 0; i < kPosPerLaunch; ++i) pos.v[i] = (GQ && i < nb) ? pos_host[b0 + i] : 0;
+        const int64_t n_wg = (int64_t)nb * p.Hkv * r.hblocks * r.n_seg;
+        if (p.D == 64)
+            hipLaunchKernelGGL((swa_ring_kernel<64, GQ>), dim3((unsigned)n_wg), dim3(256), 0, s, p, r.n_tiles,
+                               r.hblocks, r.n_seg, r.tps, b0, ga, pos);
+        else
+            hipLaunchKernelGGL((swa_ring_kernel<128, GQ>), dim3((unsigned)n_wg), dim3(256), 0, s, p, r.n_tiles,
+                               r.hblocks, r.n_seg, r.tps, b0, ga, pos);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -379,24 +545,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // walking an equal share of one (sequence, KV head, 4-head block) stream.
 hipError_t launch_swa_ring(const SwaParams& p, hipStream_t s)
 {
-    const int G = p.Hq / p.Hkv;
-    const int hblocks = G / 4;
-    const int n_tiles = (int)((p.T + 31) / 32);
-    const int64_t streams = (int64_t)p.B * p.Hkv * hblocks;
-    constexpr int64_t kTargetWgs = 512;
-    int n_seg = (int)((kTargetWgs + streams - 1) / streams);
-    if (n_seg > n_tiles) n_seg = n_tiles;
-    if (n_seg < 1) n_seg = 1;
-    const int tps = (n_tiles + n_seg - 1) / n_seg;
-    n_seg = (n_tiles + tps - 1) / tps;
-    const int64_t n_wg = streams * n_seg;
-    if (p.D == 64)
-        hipLaunchKernelGGL((swa_ring_kernel<64>), dim3((unsigned)n_wg), dim3(256), 0, s, p, n_tiles, hblocks,
-                           n_seg, tps);
-    else
-        hipLaunchKernelGGL((swa_ring_kernel<128>), dim3((unsigned)n_wg), dim3(256), 0, s, p, n_tiles, hblocks,
-                           n_seg, tps);
-    return hipGetLastError();
+    return launch_ring<false>(p, GlobalArgs{}, nullptr, s);
+}
+
+hipError_t launch_swa_ring_fused(const SwaParams& p, const XattnParams& x, hipStream_t s)
+{
+    const GlobalArgs ga{x.q_out, x.alpha_out, x.beta_out, x.ws_part, x.ws_len};
+    const hipError_t e = launch_ring<true>(p, ga, x.pos, s);
+    if (e != hipSuccess) return e;
+    return launch_merge(x, s);
 }
 
 }  // namespace orthros

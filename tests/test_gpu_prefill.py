@@ -176,19 +176,48 @@ def test_base_stream_isolated_from_output_stream():
     assert not torch.equal(bits(run.o_out), bits(oo))
 
 
-def test_stages_equal_fused_call():
-    """orthros_swa_prefill then orthros_global_xattn gives the bits of orthros_prefill."""
-    cfg = make_cfg(1, 8, 2, 128, 128, torch.bfloat16)
-    say("stages vs fused")
-    x = to_dev(inputs.prefill_inputs(T=1234, seed=15, **cfg))
+@pytest.mark.parametrize("G", [4, 2], ids=["fused", "separate"])
+def test_stages_match_one_call(G):
+    """orthros_swa_prefill then orthros_global_xattn against orthros_prefill.
+    o and the caches are bit-identical.  With G = 4 the one call takes the
+    fused path (the copy's query rides on the streaming SWA kernel, other
+    key splits), so o_out of both is checked against the oracle; with G = 2
+    the one call runs the same two kernels and o_out is bit-identical."""
+    cfg = make_cfg(2, 2 * G, 2, 128, 128, torch.bfloat16)
+    say("stages vs one call, G =", G)
+    xc = inputs.prefill_inputs(T=1234, seed=15, **cfg)
+    xc["out_pos"] = [1233, 600]
+    x = to_dev(xc)
     a = Prefill(cfg, x)
     a.run()
     b = Prefill(cfg, x)
     b.run_swa()
     b.run_xattn()
     torch.cuda.synchronize()
-    assert torch.equal(bits(a.o), bits(b.o)) and torch.equal(bits(a.o_out), bits(b.o_out))
-    assert torch.equal(bits(a.k_cache), bits(b.k_cache))
+    assert torch.equal(bits(a.o), bits(b.o))
+    assert torch.equal(bits(a.k_cache), bits(b.k_cache)) and torch.equal(bits(a.v_cache), bits(b.v_cache))
+    if G == 2:
+        assert torch.equal(bits(a.o_out), bits(b.o_out))
+    else:
+        ref = oracle_prefill(xc, 128)
+        assert_parity(a.o_out, ref["o_out"], torch.bfloat16, "o_out (one call)")
+        assert_parity(b.o_out, ref["o_out"], torch.bfloat16, "o_out (stages)")
+
+
+def test_fused_copy_positions_at_segment_edges():
+    """Fused path, 8 sequences whose copies sit at 0, inside the first pair,
+    on both sides of pair and segment boundaries, mid-prompt and at T-1.
+    (B8 x 2 KV heads x one 4-head block = 16 streams -> 32 segments of
+    5 tiles = 160 keys at T = 5000.)"""
+    cfg = make_cfg(8, 8, 2, 128, 128, torch.bfloat16)
+    run_case(cfg, 5000, seed=18, out_pos=[0, 31, 32, 159, 160, 161, 2501, 4999])
+
+
+def test_fused_more_sequences_than_one_launch():
+    """67 sequences: the fused kernel takes copy positions 64 per launch."""
+    cfg = make_cfg(67, 4, 1, 64, 16, torch.bfloat16)
+    g = torch.Generator().manual_seed(19)
+    run_case(cfg, 70, seed=19, out_pos=torch.randint(0, 70, (67,), generator=g).tolist())
 
 
 def test_explicit_softmax_scale():
