@@ -1,18 +1,21 @@
 """Benchmark of the Orthros per-layer attention step on one MI355X.
 
-A step is one orthros_prefill call (base-stream sliding-window attention
-with the fused cache write, then the output copy's split-K global
-cross-attention and its merge) over the 128K-token, batch-2, 32/8-head
-workload, with every input already resident in HBM.  value = prefill
+A step is one orthros_prefill call over the 128K-token, batch-2,
+32/8-head workload, with every input already resident in HBM: one pass of
+the streaming kernel (base-stream sliding-window attention, the fused
+cache write, and the output copy's global query folded in as one partial
+per segment), then the LSE merge of those partials.  value = prefill
 tokens per second (B * T / time per step).  The decode step latency
 (batch 16, lengths U[8192, 131072], 1024 steps) is reported beside it.
 
 Timing: warm-up calls, then K calls bracketed by torch.cuda.synchronize()
-and HIP events on the stream the kernels run on.  The dominant kernel's
-roofline figure comes from HIP events around orthros_swa_prefill launches
-alone (the same kernel and launch configuration), against the algorithmic
-bytes of one launch.  The fp64 CPU oracle is timed on a bounded sample of
-the same workload on this machine's host cores (cpu_baseline).
+and HIP events on the stream the kernels run on.  The roofline figure is
+for the step's dominant kernel, the fused streaming kernel: the step's
+algorithmic bytes over the step time (the merge that follows it in the
+same call takes a few microseconds of that).  The separate entry points
+orthros_swa_prefill and orthros_global_xattn are timed too, as a
+breakdown.  The fp64 CPU oracle is timed on a bounded sample of the same
+workload on this machine's host cores (cpu_baseline).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill|swa|xattn|decode|copy]
 """
@@ -42,6 +45,13 @@ def swa_flops(B, T, Hq, d, w):
     """Algorithmic flops: 4 d per (query, admissible key) (QK^T and PV)."""
     keys = sum(min(t + 1, w) for t in range(min(T, w))) + max(0, T - w) * w
     return 4 * d * B * Hq * keys
+
+
+def prefill_bytes(B, T, Hq, Hkv, d, es=2):
+    """Algorithmic bytes of one orthros_prefill step: those of the SWA pass
+    (which also serves the copy's key reads: one pass over K/V), plus the
+    copy's query read and its output written."""
+    return swa_bytes(B, T, Hq, Hkv, d, es) + 2 * B * Hq * d * es
 
 
 def xattn_bytes(B, pos_plus_1, Hkv, d, es=2):
@@ -164,6 +174,10 @@ def main():
         if args.only in ("all", "prefill"):
             sec, wall = timed(run.run, args.steps, args.warmup)
             ms = sec / args.steps * 1e3
+            nbytes = prefill_bytes(B, T, Hq, Hkv, d)
+            fl = swa_flops(B, T, Hq, d, w) + 4 * d * B * Hq * T
+            out["prefill"] = {"kernel": "orthros_prefill", "us": ms * 1e3, "bytes": nbytes, "flops": fl,
+                              "GBps": nbytes / (ms * 1e-3) / 1e9, "TFLOPs": fl / (ms * 1e-3) / 1e12}
             result = {"metric": METRIC, "value": B * T * args.steps / sec, "unit": "tokens/s", "n_gpus": 1,
                       "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
                       "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
@@ -220,15 +234,21 @@ def main():
     if result is None:
         result = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "data": "synthetic",
                   "dtype": "bf16", "config": {"workload": "gqa_8b_prefill_128k"}}
-    if "swa" in out:
-        s = out["swa"]
+    if "prefill" in out:
+        s = out["prefill"]
         result["roofline"] = {"bound": "hbm", "achieved": s["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": s["GBps"] / HBM_PEAK_GBS,
-                              "traffic": measured_traffic("traffic_swa_prefill_gqa_8b_128k.md"),
-                              "kernel": "orthros_swa_prefill (swa_ring16_kernel<128>)",
+                              "traffic": measured_traffic("traffic_prefill_fused_gqa_8b_128k.md"),
+                              "kernel": "orthros_prefill: swa_ring_kernel<128, true> (+ merge_kernel)",
                               "algorithmic_bytes": s["bytes"],
                               "mfma_algorithmic_TFLOPs": s["TFLOPs"],
                               "mfma_algorithmic_frac": s["TFLOPs"] / BF16_PEAK_TFLOPS}
+    if "swa" in out:
+        s = out["swa"]
+        result["roofline_swa"] = {"bound": "hbm", "achieved": s["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": s["GBps"] / HBM_PEAK_GBS,
+                                  "traffic": measured_traffic("traffic_swa_prefill_gqa_8b_128k.md"),
+                                  "kernel": "orthros_swa_prefill: swa_ring_kernel<128, false>"}
     if "xattn" in out:
         x = out["xattn"]
         result["roofline_xattn"] = {"bound": "hbm", "achieved": x["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",

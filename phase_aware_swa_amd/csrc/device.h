@@ -78,6 +78,7 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <- 7-i inside each 8 lanes
 constexpr int kDppMirror = 0x140;     // lane i <- 15-i inside each 16 lanes
+constexpr int kDppRor8 = 0x128;       // lane i <- i ^ 8 inside each 16 lanes (rotate by 8)
 
 // Sum over aligned groups of N lanes (N = 8 or 16); every lane of a group
 // ends with the same bits (each step adds a pair in both orders, and fp32
@@ -90,6 +91,12 @@ __device__ __forceinline__ float group_sum(float x)
     x += dpp_mov<kDppHalfMirror>(x);
     if constexpr (N == 16) x += dpp_mov<kDppMirror>(x);
     return x;
+}
+
+// Value of lane (lane ^ x) of the wave (x < 64), through ds_bpermute.
+__device__ __forceinline__ float lane_xor(float v, int lane, int x)
+{
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ x) << 2, __float_as_int(v)));
 }
 
 // Maps a launch-order workgroup id to a logical id so that the round-robin

@@ -249,15 +249,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     // ---- the output copy's global query (Eq. (5)), fused: wave w serves
     // head hbase + w over every key of the pairs this workgroup brings in
-    // (keys j <= P only).  Scores: lanes (group kg, chunk kc) dot 16-byte K
-    // chunks with the scaled query, a DPP sum over the LPK lanes of a key;
-    // the online softmax state (gm, gl) is wave-uniform; P goes to scalar
-    // registers as bf16 pairs, and lane l accumulates rows l + 64 r of
-    // V^T P with v_dot2_f32_bf16.
+    // (keys j <= P only).  Lanes (group kg, chunk kc): a group of LPK lanes
+    // covers STEPS keys, each lane dotting its 16-byte K chunk with the
+    // scaled query for every key of the group, in the order s ^ m with
+    // m = kc / 2; a transposing DPP reduction then leaves lane (kg, kc)
+    // with the full score of key STEPS kg + m (both lanes of a pair).  The
+    // online softmax state (gm) is wave-uniform, gl is per lane (each key
+    // counted twice); P goes to scalar registers as bf16 pairs, and lane l
+    // accumulates rows l + 64 r of V^T P with v_dot2_f32_bf16.
     constexpr int LPK = D / 8;                  // lanes per key (16-byte chunks of a row)
     constexpr int STEPS = 32 * LPK / 64;        // keys of the pair per lane group
     constexpr int RPL = D / 64;                 // V^T rows per lane
-    const int kg = lane / LPK, kc = lane % LPK;
+    static_assert(STEPS == 8 || STEPS == 4, "head dim");
+    const int kg = lane / LPK, kc = lane % LPK, km = kc >> 1;
     u32x4 gqq = u32x4{0u, 0u, 0u, 0u};          // q' * alpha' + beta', d = 8 kc .. 8 kc + 7
     float gm = kNegBig, gl = 0.f, gacc[RPL];
 #pragma unroll
@@ -282,11 +286,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // keys past P only in the pair that holds P: lim = last valid key of the pair
         const int64_t lim64 = P - pr * 32;
         const int lim = lim64 < 31 ? (int)lim64 : 31;
-        float sc[STEPS];
+        float v[STEPS];
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
-            const int key = kg * STEPS + st;
-            const u32x4 kw = *(const u32x4*)(Ks + R::kofs(key, kc));
+            const u32x4 kw = *(const u32x4*)(Ks + R::kofs(kg * STEPS + (st ^ km), kc));
             float part = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -294,14 +297,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y),
                                                        part, false);
             }
-            part = group_sum<LPK>(part);
-            sc[st] = key <= lim ? part : -INFINITY;
+            v[st] = part;
         }
-        float lmax = sc[0];
+        // slot s holds key s ^ m; each stage adds the partner's slot that
+        // holds the same key and halves the slots (partner m' = m ^ 4, m ^ 3,
+        // m ^ 1, m)
+        if constexpr (STEPS == 8) {
 #pragma unroll
-        for (int st = 1; st < STEPS; ++st) lmax = fmaxf(lmax, sc[st]);
+            for (int j = 0; j < 4; ++j) v[j] += dpp_mov<kDppRor8>(v[j + 4]);
+        }
+        v[0] += dpp_mov<kDppHalfMirror>(v[3]);
+        v[1] += dpp_mov<kDppHalfMirror>(v[2]);
+        v[0] += dpp_mov<kDppXor2>(v[1]);
+        v[0] += dpp_mov<kDppXor1>(v[0]);
+        const int key = kg * STEPS + km;
+        const float sc = key <= lim ? v[0] : -INFINITY;
+        // pair maximum: over the group's keys, then over the groups
+        float lmax = fmaxf(sc, dpp_mov<kDppXor2>(sc));
+        lmax = fmaxf(lmax, dpp_mov<kDppHalfMirror>(lmax));
+        if constexpr (STEPS == 8) lmax = fmaxf(lmax, dpp_mov<kDppRor8>(lmax));
 #pragma unroll
-        for (int x = LPK; x < 64; x <<= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, x));
+        for (int x = LPK; x < 64; x <<= 1) lmax = fmaxf(lmax, lane_xor(lmax, lane, x));
         lmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lmax * qs)));
         if (lmax > gm + kRescaleMargin) {
             const float corr = fast_exp2(gm - lmax);
@@ -310,24 +326,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int r = 0; r < RPL; ++r) gacc[r] *= corr;
         }
-        float p[STEPS], lsum = 0.f;
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-            p[st] = fast_exp2(__builtin_fmaf(sc[st], qs, -gm));
-            lsum += p[st];
-        }
-#pragma unroll
-        for (int x = LPK; x < 64; x <<= 1) lsum += __shfl_xor(lsum, x);
-        gl += __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lsum)));
-        // bf16 pairs (keys 2 j, 2 j + 1) of the whole pair, wave-uniform
+        const float p = fast_exp2(__builtin_fmaf(sc, qs, -gm));
+        gl += p;
+        // bf16 pairs (keys 2 j, 2 j + 1): the partner m ^ 1 sits at kc ^ 2;
+        // lanes with m even hold them in order
+        const int wrd = (int)pack_bf16x2(p, dpp_mov<kDppXor2>(p));
         uint32_t pw[16];
 #pragma unroll
-        for (int j = 0; j < STEPS / 2; ++j) {
-            const int wrd = (int)pack_bf16x2(p[2 * j], p[2 * j + 1]);
-#pragma unroll
-            for (int grp = 0; grp < 64 / LPK; ++grp)
-                pw[grp * (STEPS / 2) + j] = (uint32_t)__builtin_amdgcn_readlane(wrd, grp * LPK);
-        }
+        for (int j = 0; j < 16; ++j)
+            pw[j] = (uint32_t)__builtin_amdgcn_readlane(wrd, LPK * ((2 * j) / STEPS) + 2 * ((2 * j) % STEPS));
         const uint16_t* Vt = Ks + R::KPART;
 #pragma unroll
         for (int r = 0; r < RPL; ++r) {
@@ -490,9 +497,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         float* part = ga.ws_part + (((int64_t)b * a.Hq + hbase + wv) * n_seg + seg) * (D + 2);
 #pragma unroll
         for (int r = 0; r < RPL; ++r) part[2 + lane + 64 * r] = gacc[r];
+        // every key was counted by the two lanes of its pair
+        int ln = lane;
+        asm volatile("" : "+v"(ln));   // recompute the exchange addresses here, not across the loop
+        float lsum = group_sum<16>(gl);
+        lsum += lane_xor(lsum, ln, 16);
+        lsum += lane_xor(lsum, ln, 32);
         if (lane == 0) {
             part[0] = gm;
-            part[1] = gl;
+            part[1] = 0.5f * lsum;
         }
         if (seg == 0 && g == 0 && hb == 0 && tid == 0) ga.ws_len[b] = (int32_t)P;
     }
