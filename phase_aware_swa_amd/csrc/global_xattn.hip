@@ -123,6 +123,8 @@ __device__ __forceinline__ void attend_chunk(const float (*qs)[D], const E* kc, 
                              int64_t lo, int64_t hi, float (*red)[HG][D + 2],
                              float* out, int64_t out_stride)
 {
+    constexpr bool kBf16 = sizeof(E) == 2;
+    static_assert(kUnroll % 2 == 0, "keys go in pairs");
     constexpr int LPK = D / 8;        // lanes per key row
     constexpr int KPW = 64 / LPK;     // key rows per wave per step
     constexpr int KPS = 4 * KPW;      // key rows per workgroup per step
@@ -158,6 +160,18 @@ __device__ __forceinline__ void attend_chunk(const float (*qs)[D], const E* kc, 
                 vx[u].load(vr + 8 * c);
             }
         }
+        // bf16: V values of keys (u, u+1) paired per head-dim value, shared by the heads
+        uint32_t vp[kUnroll / 2][8];
+        if constexpr (kBf16) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; u += 2)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t a0 = vx[u].w[w], a1 = vx[u + 1].w[w];
+                    vp[u / 2][2 * w] = (a0 & 0xffffu) | (a1 << 16);
+                    vp[u / 2][2 * w + 1] = (a0 >> 16) | (a1 & 0xffff0000u);
+                }
+        }
 #pragma unroll
         for (int hh = 0; hh < HG; ++hh) {
             float s[kUnroll];
@@ -173,12 +187,28 @@ __device__ __forceinline__ void attend_chunk(const float (*qs)[D], const E* kc, 
             l[hh] *= corr;
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[hh][e] *= corr;
+            if constexpr (kBf16) {
+                // keys in pairs: P as a bf16 pair, V as (key u, key u+1) pairs
+                // per head-dim value, one v_dot2_f32_bf16 per value; the row
+                // sum takes the same rounded weights
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const float p = fast_exp2(s[u] - mx);
-                l[hh] += p;
+                for (int u = 0; u < kUnroll; u += 2) {
+                    const uint32_t pp = pack_bf16x2(fast_exp2(s[u] - mx), fast_exp2(s[u + 1] - mx));
+                    l[hh] += bf16_lo(pp) + bf16_hi(pp);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[hh][e] += p * vx[u][e];
+                    for (int e = 0; e < 8; ++e)
+                        acc[hh][e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, vp[u / 2][e]),
+                                                                     __builtin_bit_cast(bf16x2, pp), acc[hh][e],
+                                                                     false);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const float p = fast_exp2(s[u] - mx);
+                    l[hh] += p;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[hh][e] += p * vx[u][e];
+                }
             }
         }
     }
