@@ -97,39 +97,46 @@ def timed(fn, steps, warmup):
     return start.elapsed_time(end) / 1e3, wall
 
 
-def cpu_baseline(cfg, x_dev, budget_rows=1024):
-    """The fp64 oracle on a bounded sample of the workload: SWA for
-    budget_rows consecutive tokens of sequence 0 (all heads) and the global
-    query of sequence 0 (all heads, all keys); the whole workload's time is
-    extrapolated from those rates."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, x_dev, one_thread_rows=128):
+    """The fp64 oracle on the whole workload (Eq. (4) for every token and
+    head, the cache, and each sequence's global query over all its keys),
+    about 10 s on 16 host threads; plus the Eq. (4) rate of a single thread
+    on a short run of rows."""
     import torch
 
     import oracle
     B, T, Hq = cfg["batch"], cfg["T"], cfg["n_q_heads"]
     w = cfg["window"]
     nthreads = oracle.default_threads()
-    t0 = T // 2
-    lo = t0 - w + 1
-    sl = slice(lo, t0 + budget_rows)
-    q = x_dev["q"][:1, sl].cpu().contiguous()
-    k = x_dev["k"][:1, sl].cpu().contiguous()
-    v = x_dev["v"][:1, sl].cpu().contiguous()
+    q = x_dev["q"].cpu().contiguous()
+    k = x_dev["k"].cpu().contiguous()
+    v = x_dev["v"].cpu().contiguous()
     a, b = x_dev["alpha"].cpu(), x_dev["beta"].cpu()
-    rows = torch.tensor([(0, t - lo, h) for t in range(t0, t0 + budget_rows) for h in range(Hq)])
     s = time.perf_counter()
-    oracle.swa_rows(q, k, v, a, b, w, rows, nthreads=nthreads)
-    t_swa = (time.perf_counter() - s) / budget_rows            # seconds per token (all heads)
-    k1 = x_dev["k"][:1].cpu().contiguous()
-    v1 = x_dev["v"][:1].cpu().contiguous()
+    oracle.prefill(q, x_dev["q_out"].cpu().contiguous(), [T - 1] * B, k, v, a, b, x_dev["alpha_out"].cpu(),
+                   x_dev["beta_out"].cpu(), w, nthreads=nthreads)
+    t_all = time.perf_counter() - s
+    t0 = T // 2
+    rows = torch.tensor([(0, t, h) for t in range(t0, t0 + one_thread_rows) for h in range(Hq)])
     s = time.perf_counter()
-    oracle.prefill(None, x_dev["q_out"][:1].cpu().contiguous(), [T - 1], k1, v1, a, b,
-                   x_dev["alpha_out"].cpu(), x_dev["beta_out"].cpu(), w, swa=False, nthreads=nthreads)
-    t_glob = time.perf_counter() - s                              # seconds per sequence
-    total = t_swa * B * T + t_glob * B
-    return {"value": B * T / total, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"fp64 oracle, {nthreads} threads: Eq. (4) rows for {budget_rows} consecutive tokens x "
-                      f"{Hq} heads of sequence 0 ({t_swa * 1e3:.2f} ms/token) plus one sequence's global "
-                      f"query over all {T} keys ({t_glob:.2f} s), extrapolated to B={B} x T={T}"}
+    oracle.swa_rows(q[:1], k[:1], v[:1], a, b, w, rows, nthreads=1)
+    t_row1 = (time.perf_counter() - s) / one_thread_rows            # seconds per token, 1 thread
+    return {"value": B * T / t_all, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "one_thread_swa_tokens_per_s": 1.0 / t_row1,
+            "sample": f"fp64 oracle, {nthreads} threads, the whole workload (B={B} x T={T}: Eq. (4) for every "
+                      f"token x {Hq} heads, the cache, and the global query over all {T} keys) in {t_all:.1f} s; "
+                      f"one thread: Eq. (4) for {one_thread_rows} tokens x {Hq} heads"}
 
 
 def main():
@@ -220,10 +227,20 @@ def main():
 
         sec, _ = timed(one_pass, 2, 1)
         us = sec / 2 / nsteps * 1e6
+        # one more pass with an event pair around every step: the per-step distribution
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nsteps)]
+        dec.cache_len.copy_(len0)
+        for s_, (e0, e1) in enumerate(evs):
+            e0.record()
+            dec.step(xd["q"][s_], xd["q_out"][s_], xd["k_new"][s_], xd["v_new"][s_])
+            e1.record()
+        torch.cuda.synchronize()
+        per = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
         lens = len0.double()
         step_bytes = float(((lens + nsteps / 2).sum() * Hkv * d * 2 * 2).item())   # mean history K+V per step
         out["decode"] = {"workload": "gqa_8b_decode_b16", "us_per_step": us, "steps": nsteps,
-                         "bytes_per_step": step_bytes, "GBps": step_bytes / (us * 1e-6) / 1e9}
+                         "bytes_per_step": step_bytes, "GBps": step_bytes / (us * 1e-6) / 1e9,
+                         "p50_us": per[len(per) // 2], "p99_us": per[min(len(per) - 1, (99 * len(per)) // 100)]}
         if result is None:
             result = {"metric": METRIC, "value": us, "unit": "us/step", "n_gpus": 1, "steps": nsteps,
                       "warmup": 1, "ms_per_step": us / 1e3, "higher_is_better": False, "scaling": "weak",
