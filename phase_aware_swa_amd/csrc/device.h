@@ -93,6 +93,19 @@ __device__ __forceinline__ float group_sum(float x)
     return x;
 }
 
+// Maximum over the whole wave of a value that is already uniform within each
+// row of 16 lanes: two DPP row broadcasts (row 0 -> 1, 2 -> 3, then 1 -> 2, 3)
+// leave the total in lane 63.
+__device__ __forceinline__ float wave_max_of_rows(float x)
+{
+    constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), kRowBcast15,
+                                                            0xa, 0xf, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), kRowBcast31,
+                                                            0xc, 0xf, false)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
 // Value of lane (lane ^ x) of the wave (x < 64), through ds_bpermute.
 __device__ __forceinline__ float lane_xor(float v, int lane, int x)
 {

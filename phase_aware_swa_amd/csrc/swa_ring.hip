@@ -312,13 +312,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         v[0] += dpp_mov<kDppXor1>(v[0]);
         const int key = kg * STEPS + km;
         const float sc = key <= lim ? v[0] : -INFINITY;
-        // pair maximum: over the group's keys, then over the groups
+        // pair maximum: over the keys of a row of 16 lanes, then over the rows
         float lmax = fmaxf(sc, dpp_mov<kDppXor2>(sc));
         lmax = fmaxf(lmax, dpp_mov<kDppHalfMirror>(lmax));
-        if constexpr (STEPS == 8) lmax = fmaxf(lmax, dpp_mov<kDppRor8>(lmax));
-#pragma unroll
-        for (int x = LPK; x < 64; x <<= 1) lmax = fmaxf(lmax, lane_xor(lmax, lane, x));
-        lmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lmax * qs)));
+        lmax = fmaxf(lmax, dpp_mov<kDppRor8>(lmax));
+        lmax = wave_max_of_rows(lmax) * qs;
         if (lmax > gm + kRescaleMargin) {
             const float corr = fast_exp2(gm - lmax);
             gm = lmax;
@@ -467,6 +465,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // vector-memory counter retires in issue order, so waiting for the
         // alpha/beta loads after the stores would also wait for the stores.
         __builtin_amdgcn_sched_barrier(0);
+        // the copy's step on this tile's own pair (LDS and ALU only) runs
+        // while the next tile's Q rows may still be arriving
+        if constexpr (GQ) {
+            if (q0 <= P) global_pair(q0 >> 5);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         if (has_next) scale_offset(qraw, qf);
         __builtin_amdgcn_sched_barrier(0);
         // ---- normalise and store the sub-tile (rows >= T fall outside the resource)
@@ -485,9 +489,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     buf_store8(w, ro, (uint32_t)(n * qrow_b + hd * D * 2 + 2 * (16 * dt + 4 * gq)));
                 }
             }
-        }
-        if constexpr (GQ) {
-            if (q0 <= P) global_pair(q0 >> 5);     // this tile's own pair
         }
         __syncthreads();   // every wave is done with the slot the next pair replaces
         if (has_next) store_pair((q0 >> 5) + 1, true, kreg, vreg);
