@@ -58,6 +58,8 @@ def lib():
         L.oracle_swa_rows.argtypes = [sp, i64] + [vp] * 5 + [i64, vp, vp]
         L.oracle_swa_rows.restype = ctypes.c_int
         L.oracle_decode_step.argtypes = [sp] + [vp] * 10 + [i64, vp, vp, vp]
+        L.oracle_copies.argtypes = [sp, i64, i64] + [vp] * 6 + [i64, vp]
+        L.oracle_copies.restype = ctypes.c_int
         L.oracle_decode_step.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -157,3 +159,22 @@ def decode_step(q, q_out, k_new, v_new, alpha, beta, alpha_out, beta_out, window
     if rc != 0:
         raise ValueError("oracle_decode_step rejected its arguments")
     return o, o_out
+
+
+def copies(q_out, pos, alpha_out, beta_out, k_cache, v_cache, T, softmax_scale=None, nthreads=None):
+    """Eq. (5) for T_out output copies per sequence (the PT / SFT modes).
+
+    q_out [B,T_out,Hq,d]; pos [B,T_out] original positions (any order,
+    0 <= pos < T); k_cache, v_cache [B,Hkv,cap,d] with slots [0, T) filled.
+    Returns o_out as float64 [B,T_out,Hq,d].
+    """
+    B, T_out, Hq, d = q_out.shape
+    Hkv = k_cache.shape[1]
+    pos = torch.as_tensor(pos, dtype=torch.int32).reshape(B, T_out).contiguous()
+    o_out = torch.zeros(B, T_out, Hq, d, dtype=torch.float64)
+    s = make_shape(B, Hq, Hkv, d, 1, q_out.dtype, softmax_scale, nthreads)
+    rc = lib().oracle_copies(ctypes.byref(s), T, T_out, _p(q_out), _p(pos), _p(alpha_out), _p(beta_out),
+                             _p(k_cache), _p(v_cache), k_cache.shape[2], _p(o_out))
+    if rc != 0:
+        raise ValueError("oracle_copies rejected its arguments")
+    return o_out

@@ -26,7 +26,11 @@
  *     slot ([N] §2.3 Eq. (5), §2.4);
  *   - prefill: one copy per sequence; decode: one base token and one copy
  *     per step, the copy reading the whole history including the new token
- *     ([N] §2.4 walk-through, §2.5 mode table).
+ *     ([N] §2.4 walk-through, §2.5 mode table);
+ *   - pre-training and fine-tuning modes: T_out copies per sequence at
+ *     arbitrary original positions (every position in PT, the answer
+ *     positions in SFT; [N] §2.5 mode table), each the Eq. (5) query of its
+ *     own position.
  *
  * Positions are 0-based here: the window of row t is [max(0, t-w+1), t].
  * Softmax uses the textbook max-subtracted form in fp64.  Every input is
@@ -224,6 +228,61 @@ int oracle_prefill(const oracle_shape* s, int64_t T,
     int64_t units = (int64_t)s->batch * Hq;
     if (o) parallel_for(s->nthreads, units, prefill_swa_unit, &c);
     if (o_out) parallel_for(s->nthreads, units, prefill_global_unit, &c);
+    return 0;
+}
+
+/* ---------------------------------------------------------- many copies */
+
+typedef struct {
+    const oracle_shape* s;
+    int64_t T_out, cap;
+    const void *q_out, *alpha_out, *beta_out, *k_cache, *v_cache;
+    const int32_t* pos;
+    double* o_out;
+} copies_ctx;
+
+/* Unit = (b, i, h): Eq. (5) for copy i of sequence b, query head h, keys
+ * [0, pos[b][i]] of the cache. */
+static void copies_unit(void* p, int64_t u)
+{
+    copies_ctx* c = (copies_ctx*)p;
+    const oracle_shape* s = c->s;
+    int Hq = s->n_q_heads, Hkv = s->n_kv_heads, d = s->head_dim;
+    int h = (int)(u % Hq), g = h / (Hq / Hkv);
+    int64_t bi = u / Hq, b = bi / c->T_out;
+    int64_t qrow = (bi * Hq + h) * d;
+    double* qh = (double*)malloc((size_t)d * sizeof(double));
+    scale_offset(c->q_out, qrow, c->alpha_out, c->beta_out, h, d, s->dtype, qh);
+    attend(qh, d, s->softmax_scale, c->k_cache, c->v_cache, s->dtype,
+           (b * Hkv + g) * c->cap * d, d, 0, c->pos[bi], c->o_out + qrow);
+    free(qh);
+}
+
+/*
+ * Eq. (5) for T_out output copies per sequence ([N] §2.5 mode table: PT
+ * copies every position, SFT the answer positions): copy i of sequence b
+ * sits at original position pos[b][i] and attends the cached keys
+ * [0, pos[b][i]] with its own query q_out[b][i] ([N] §2.4: the mask follows
+ * the original position, never the copy's slot).  The copies neither write
+ * the cache nor see one another.  Returns 0, or -1 on a bad shape or a
+ * position outside [0, T).
+ * Layouts: q_out, o_out [B][T_out][Hq][d], pos [B][T_out] (int32).
+ */
+int oracle_copies(const oracle_shape* s, int64_t T, int64_t T_out,
+                  const void* q_out, const int32_t* pos,
+                  const void* alpha_out, const void* beta_out,
+                  const void* k_cache, const void* v_cache, int64_t cap,
+                  double* o_out)
+{
+    if (!s || s->n_kv_heads < 1 || s->n_q_heads % s->n_kv_heads || T < 1 ||
+        T_out < 1 || cap < T || !pos || !o_out)
+        return -1;
+    for (int64_t i = 0; i < (int64_t)s->batch * T_out; ++i)
+        if (pos[i] < 0 || pos[i] >= T) return -1;
+    copies_ctx c = {s, T_out, cap, q_out, alpha_out, beta_out, k_cache, v_cache,
+                    pos, o_out};
+    parallel_for(s->nthreads, (int64_t)s->batch * T_out * s->n_q_heads,
+                 copies_unit, &c);
     return 0;
 }
 
