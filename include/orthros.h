@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ORTHROS_ABI_VERSION 1
+#define ORTHROS_ABI_VERSION 2
 
 typedef enum {
     ORTHROS_OK = 0,
@@ -144,6 +144,38 @@ orthros_status orthros_global_xattn(const orthros_desc* desc, int64_t T,
                                     const void* k_cache, const void* v_cache, int64_t cap,
                                     void* o_out,
                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* -------------------------------------------------- many output copies */
+
+/*
+ * Output copies at many positions per sequence: the pre-training and
+ * fine-tuning modes of [N] §2.5 (mode table: PT copies every position,
+ * T_out = T; SFT copies the answer positions).  Copy i of sequence b sits
+ * at original position out_pos[b][i]; its query q_out[b][i], scale-offset
+ * by alpha_out/beta_out, attends over cache slots [0, out_pos[b][i]]
+ * ([N] §2.3 Eq. (5), §2.4: the mask follows the original position, never
+ * the copy's slot).  The copies neither write the cache nor see one
+ * another.  The cache must already hold slots [0, T) (stream order after
+ * orthros_swa_prefill or orthros_prefill suffices).
+ *
+ *   T          prompt length per sequence, 1 <= T <= cap
+ *   T_out      copies per sequence, >= 1
+ *   q_out      device [B][T_out][Hq][d]   the copies' projected queries x' W_Q
+ *   out_pos    device int32 [B][T_out]    original positions, in any order
+ *              (ascending is fastest); 4-byte aligned.  A copy whose
+ *              position lies outside [0, T) reads nothing and gets NaN in
+ *              o_out (the positions live on the device, so they are checked
+ *              there)
+ *   alpha_out, beta_out  device [Hq][d]
+ *   k_cache, v_cache     device [B][Hkv][cap][d], read only
+ *   o_out      device [B][T_out][Hq][d]
+ * Needs no workspace.  Results are run-to-run identical.
+ */
+orthros_status orthros_copies(const orthros_desc* desc, int64_t T, int64_t T_out,
+                              const void* q_out, const int32_t* out_pos,
+                              const void* alpha_out, const void* beta_out,
+                              const void* k_cache, const void* v_cache, int64_t cap,
+                              void* o_out, void* stream);
 
 /* -------------------------------------------------------------- decode */
 

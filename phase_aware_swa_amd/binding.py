@@ -63,6 +63,8 @@ def lib():
         L.orthros_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, vp, vp, vp,
                                           sz, vp]
         L.orthros_decode_step.restype = ctypes.c_int
+        L.orthros_copies.argtypes = [dp, i64, i64, vp, vp, vp, vp, vp, vp, i64, vp, vp]
+        L.orthros_copies.restype = ctypes.c_int
         L.orthros_status_str.argtypes = [ctypes.c_int]
         L.orthros_status_str.restype = ctypes.c_char_p
         L.orthros_last_error.argtypes = []
@@ -142,6 +144,14 @@ def decode_step(desc, q, q_out, k_new, v_new, alpha, beta, alpha_out, beta_out, 
         _ptr(alpha_out), _ptr(beta_out), _ptr(k_cache), _ptr(v_cache),
         k_cache.shape[2] if k_cache is not None else 0, _ptr(cache_len), max_len_hint, _ptr(o), _ptr(o_out),
         _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def copies(desc, T, q_out, out_pos, alpha_out, beta_out, k_cache, v_cache, o_out, stream=None):
+    """orthros_copies; q_out / o_out [B, T_out, Hq, d]; out_pos a device int32 tensor [B, T_out]."""
+    _check(lib().orthros_copies(
+        ctypes.byref(desc), T, q_out.shape[1] if q_out is not None else 0, _ptr(q_out), _ptr(out_pos),
+        _ptr(alpha_out), _ptr(beta_out), _ptr(k_cache), _ptr(v_cache),
+        k_cache.shape[2] if k_cache is not None else 0, _ptr(o_out), _stream(stream)))
 
 
 def abi_version():

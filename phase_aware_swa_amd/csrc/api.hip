@@ -310,6 +310,32 @@ orthros_status orthros_prefill(const orthros_desc* desc, int64_t T, const void* 
                      (hipStream_t)stream);
 }
 
+orthros_status orthros_copies(const orthros_desc* desc, int64_t T, int64_t T_out, const void* q_out,
+                              const int32_t* out_pos, const void* alpha_out, const void* beta_out,
+                              const void* k_cache, const void* v_cache, int64_t cap, void* o_out, void* stream)
+{
+    g_err.clear();
+    orthros_status st = check_desc(desc);
+    if (st) return st;
+    if ((st = check_T(desc, T, cap))) return st;
+    if (T_out < 1 || T_out > INT32_MAX)
+        return fail(ORTHROS_E_SHAPE, "T_out = %lld outside [1, 2^31)", (long long)T_out);
+    const int64_t rowq = (int64_t)desc->n_q_heads * desc->head_dim;
+    if ((int64_t)desc->batch * T_out > kMaxElems / rowq)
+        return fail(ORTHROS_E_SHAPE, "copy tensors overflow the library's 2^50-element bound");
+    if ((st = check_ptrs({q_out, alpha_out, beta_out, k_cache, v_cache, o_out}))) return st;
+    if (!out_pos) return fail(ORTHROS_E_NULL, "out_pos is NULL");
+    if (reinterpret_cast<uintptr_t>(out_pos) & 3u) return fail(ORTHROS_E_ALIGN, "out_pos is not 4-byte aligned");
+    orthros::CopiesParams p;
+    p.q_out = q_out; p.pos = out_pos; p.alpha_out = alpha_out; p.beta_out = beta_out;
+    p.k_cache = k_cache; p.v_cache = v_cache; p.o_out = o_out;
+    p.T = T; p.T_out = T_out; p.cap = cap;
+    p.B = desc->batch; p.Hq = desc->n_q_heads; p.Hkv = desc->n_kv_heads; p.D = desc->head_dim;
+    p.qscale = qscale_of(desc);
+    p.dt = dt_of(desc);
+    return hip_status(orthros::launch_copies(p, (hipStream_t)stream), "copies kernel launch");
+}
+
 orthros_status orthros_decode_step(const orthros_desc* desc, const void* q, const void* q_out,
                                    const void* k_new, const void* v_new, const void* alpha, const void* beta,
                                    const void* alpha_out, const void* beta_out, void* k_cache, void* v_cache,

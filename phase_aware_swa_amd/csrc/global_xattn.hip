@@ -335,6 +335,41 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p)
                                vnew, wlo, hi, red, out + kind_stride, head_stride);
 }
 
+// ------------------------------------------------ many copies: general form
+
+// One workgroup per (copy, KV group block, sequence): the copy's HG heads
+// attend over keys [0, pos] with the chunk worker, whose one partial stays
+// in LDS and is normalised in place.  A position outside [0, T) gives NaN.
+template <typename E, int D, int HG>
+__global__ __launch_bounds__(256) void copies_simple_kernel(CopiesParams p)
+{
+    __shared__ float qs[HG][D];
+    __shared__ float red[4][HG][D + 2];
+    __shared__ float part[HG][D + 2];
+    const int64_t i = blockIdx.x;
+    const int G = p.Hq / p.Hkv, hblocks = G / HG;
+    const int g = blockIdx.y / hblocks, hb = blockIdx.y % hblocks;
+    const int b = blockIdx.z;
+    const int h0 = g * G + hb * HG;
+    const int64_t row = ((int64_t)b * p.T_out + i) * p.Hq * D;     // copy i's query / output row
+    const int64_t P = p.pos[(int64_t)b * p.T_out + i];
+    if (P < 0 || P >= p.T) {
+        for (int idx = threadIdx.x; idx < HG * D; idx += blockDim.x)
+            st_elem((E*)p.o_out, row + (int64_t)h0 * D + idx, __builtin_nanf(""));
+        return;
+    }
+    load_queries<E, D, HG>(qs, (const E*)p.q_out, (const E*)p.alpha_out, (const E*)p.beta_out, row, h0,
+                           p.qscale);
+    __syncthreads();
+    const int64_t crow = ((int64_t)b * p.Hkv + g) * p.cap * D;
+    attend_chunk<E, D, HG>(qs, (const E*)p.k_cache + crow, (const E*)p.v_cache + crow, -1, nullptr, nullptr, 0, P,
+                           red, &part[0][0], D + 2);
+    for (int idx = threadIdx.x; idx < HG * D; idx += blockDim.x) {
+        const int hh = idx / D, d = idx % D;
+        st_elem((E*)p.o_out, row + (int64_t)(h0 + hh) * D + d, part[hh][2 + d] / part[hh][1]);
+    }
+}
+
 // --------------------------------------------------------------- LSE merge
 
 // One workgroup (256 threads) per (sequence, query head):
@@ -472,6 +507,24 @@ hipError_t launch_xattn(const XattnParams& p, hipStream_t st)
 {
     if (p.dt == Dt::F32) return p.D == 64 ? xattn_by_hg<float, 64>(p, st) : xattn_by_hg<float, 128>(p, st);
     return p.D == 64 ? xattn_by_hg<uint16_t, 64>(p, st) : xattn_by_hg<uint16_t, 128>(p, st);
+}
+
+template <typename E, int D>
+hipError_t launch_copies_simple(const CopiesParams& p, hipStream_t st)
+{
+    const int G = p.Hq / p.Hkv, HG = xattn_heads_per_wg(G);
+    const dim3 grid((unsigned)p.T_out, (unsigned)(p.Hkv * (G / HG)), (unsigned)p.B);
+    if (HG == 4) hipLaunchKernelGGL((copies_simple_kernel<E, D, 4>), grid, dim3(256), 0, st, p);
+    else if (HG == 2) hipLaunchKernelGGL((copies_simple_kernel<E, D, 2>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((copies_simple_kernel<E, D, 1>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_copies(const CopiesParams& p, hipStream_t st)
+{
+    if (p.dt == Dt::F32)
+        return p.D == 64 ? launch_copies_simple<float, 64>(p, st) : launch_copies_simple<float, 128>(p, st);
+    return p.D == 64 ? launch_copies_simple<uint16_t, 64>(p, st) : launch_copies_simple<uint16_t, 128>(p, st);
 }
 
 hipError_t launch_merge(const XattnParams& p, hipStream_t st)

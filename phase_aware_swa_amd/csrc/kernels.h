@@ -97,4 +97,20 @@ hipError_t launch_xattn(const XattnParams& p, hipStream_t s);
 hipError_t launch_merge(const XattnParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 
+// Output copies at many positions per sequence (no workspace).
+struct CopiesParams {
+    const void* q_out;      // [B][T_out][Hq][D]
+    const int32_t* pos;     // device [B][T_out]
+    const void* alpha_out;  // [Hq][D]
+    const void* beta_out;
+    const void* k_cache;    // [B][Hkv][cap][D]
+    const void* v_cache;
+    void* o_out;            // [B][T_out][Hq][D]
+    int64_t T, T_out, cap;
+    int32_t B, Hq, Hkv, D;
+    float qscale;
+    Dt dt;
+};
+hipError_t launch_copies(const CopiesParams& p, hipStream_t s);
+
 }  // namespace orthros

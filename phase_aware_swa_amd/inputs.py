@@ -92,6 +92,21 @@ def prefill_inputs(batch, n_q_heads, n_kv_heads, head_dim, T, dtype, seed,
     return x
 
 
+def copies_inputs(batch, n_q_heads, head_dim, T, T_out, dtype, seed, device="cpu", positions="tail"):
+    """The output copies of the PT / SFT modes: raw projected copy queries
+    q_out [B,T_out,Hq,d] ~ N(0,1) and their original positions pos
+    [B,T_out] (int32).  positions="tail": the last T_out positions in
+    order (an SFT answer span; T_out = T is PT); "random": uniform draws
+    over [0, T), unsorted, repeats allowed."""
+    g = _gen(seed, device)
+    q_out = _normal((batch, T_out, n_q_heads, head_dim), g, device, dtype)
+    if positions == "tail":
+        pos = torch.arange(T - T_out, T, device=device, dtype=torch.int32).repeat(batch, 1)
+    else:
+        pos = torch.randint(0, T, (batch, T_out), generator=g, device=device).to(torch.int32)
+    return q_out, pos.contiguous()
+
+
 def decode_inputs(batch, n_q_heads, n_kv_heads, head_dim, dtype, seed, steps,
                   len_lo, len_hi, device="cpu", **_):
     """Tensors for a run of decode steps.

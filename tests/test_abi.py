@@ -20,16 +20,17 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"orthros_prefill", "orthros_decode_step", "orthros_swa_prefill", "orthros_global_xattn"} <= set(names)
+    assert {"orthros_prefill", "orthros_decode_step", "orthros_swa_prefill", "orthros_global_xattn",
+            "orthros_copies"} <= set(names)
     lib = binding.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in orthros.h but not exported"
 
 
 def test_abi_version_and_status_text():
-    assert binding.abi_version() == 1
+    assert binding.abi_version() == 2
     text = open(HEADER).read()
-    assert "#define ORTHROS_ABI_VERSION 1" in text
+    assert "#define ORTHROS_ABI_VERSION 2" in text
     for code, name in binding.STATUS.items():
         assert binding.status_str(code) == name
         assert re.search(rf"\b{name}\s*=\s*{code}\b", text) or code == 0
@@ -103,3 +104,28 @@ def test_workspace_sizes():
     assert binding.prefill_workspace_size(d, 0) == 0
     assert 0 < binding.decode_workspace_size(d, 10) <= binding.decode_workspace_size(d, 100000)
     assert binding.decode_workspace_size(d, -1) == 0
+
+
+def copies_call(desc, T=100, T_out=4, cap=100, ptr=FAKE, pos=FAKE):
+    p = ctypes.c_void_p(ptr)
+    return binding.lib().orthros_copies(ctypes.byref(desc), T, T_out, p, ctypes.c_void_p(pos), p, p, p, p, cap,
+                                        p, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T_out=0), -2),
+    (dict(T=0), -2),
+    (dict(cap=50), -5),
+    (dict(ptr=0), -1),
+    (dict(pos=0), -1),
+    (dict(ptr=FAKE + 8), -8),
+    (dict(pos=FAKE + 2), -8),
+])
+def test_copies_rejects_bad_arguments(kw, status):
+    assert copies_call(mk(), **kw) == status
+    assert binding.lib().orthros_last_error().decode()
+
+
+def test_copies_rejects_bad_desc():
+    assert copies_call(mk(dtype=5)) == -3
+    assert copies_call(mk(head_dim=96)) == -2
