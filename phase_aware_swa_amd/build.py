@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liborthros.so")
-SOURCES = ["api.hip", "swa_prefill.hip", "swa_ring.hip", "global_xattn.hip"]
+SOURCES = ["api.hip", "swa_prefill.hip", "swa_ring.hip", "global_xattn.hip", "copies_flash.hip"]
 # The streaming kernel never produces or tests NaNs (masked scores are -inf,
 # running maxima start finite), so fmax needs no NaN quieting there.
 EXTRA = {"swa_ring.hip": ["-fno-honor-nans"]}

@@ -522,6 +522,7 @@ hipError_t launch_copies_simple(const CopiesParams& p, hipStream_t st)
 
 hipError_t launch_copies(const CopiesParams& p, hipStream_t st)
 {
+    if (copies_flash_applies(p)) return launch_copies_flash(p, st);
     if (p.dt == Dt::F32)
         return p.D == 64 ? launch_copies_simple<float, 64>(p, st) : launch_copies_simple<float, 128>(p, st);
     return p.D == 64 ? launch_copies_simple<uint16_t, 64>(p, st) : launch_copies_simple<uint16_t, 128>(p, st);

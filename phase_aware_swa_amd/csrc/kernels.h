@@ -112,5 +112,8 @@ struct CopiesParams {
     Dt dt;
 };
 hipError_t launch_copies(const CopiesParams& p, hipStream_t s);
+// The MFMA flash form of the copies (bf16, groups of 4 query heads).
+bool copies_flash_applies(const CopiesParams& p);
+hipError_t launch_copies_flash(const CopiesParams& p, hipStream_t s);
 
 }  // namespace orthros

@@ -65,6 +65,10 @@ CASES = [
     (1, 8, 1, 128, 1000, 64, "tail"),       # G = 8
     (3, 2, 2, 64, 90, 1, "random"),         # one copy (the prefill shape) per sequence
     (1, 4, 2, 128, 33, 33, "tail"),         # short prompt, ragged tiles
+    # bf16 with groups of 4 / 8 takes the MFMA flash kernel: many two-pair steps
+    (1, 8, 2, 64, 2100, 2100, "tail"),      # PT, d = 64
+    (2, 8, 1, 128, 3000, 333, "random"),    # G = 8, a ragged last tile of copies
+    (1, 4, 1, 128, 4096, 40, "tail"),       # SFT: one tile, positions 4056..4095
 ]
 
 
