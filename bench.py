@@ -17,7 +17,7 @@ orthros_swa_prefill and orthros_global_xattn are timed too, as a
 breakdown.  The fp64 CPU oracle is timed on a bounded sample of the same
 workload on this machine's host cores (cpu_baseline).
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill|swa|xattn|decode|copy]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill|swa|xattn|copies|decode|copy]
 """
 import argparse
 import hashlib
@@ -144,7 +144,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", default="all", choices=["all", "prefill", "swa", "xattn", "decode", "copy"])
+    ap.add_argument("--only", default="all",
+                    choices=["all", "prefill", "swa", "xattn", "copies", "decode", "copy"])
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -156,7 +157,7 @@ def main():
     import torch
 
     from phase_aware_swa_amd import inputs
-    from phase_aware_swa_amd.runner import Decode, Prefill
+    from phase_aware_swa_amd.runner import Copies, Decode, Prefill
 
     torch.cuda.set_device(0)
     out = {}
@@ -209,6 +210,31 @@ def main():
             result["cpu_baseline"] = cpu_baseline(cfg, x)
         del run, x
         torch.cuda.empty_cache()
+
+    if args.only in ("all", "copies"):
+        # output copies at many positions (SFT answer span, PT every position): MFMA-bound
+        for name in ("gqa_8b_sft_32k", "gqa_8b_pt_16k"):
+            ccfg = dict(inputs.WORKLOADS[name])
+            cB, cT, cTo = ccfg["batch"], ccfg["T"], ccfg["T_out"]
+            xc = inputs.prefill_inputs(seed=7, device="cuda", **ccfg)
+            pre = Prefill(ccfg, xc)
+            pre.run_swa()                       # fills the caches, not timed
+            q_out, pos = inputs.copies_inputs(cB, Hq, d, cT, cTo, torch.bfloat16, seed=8, device="cuda")
+            cp = Copies(ccfg, cT, q_out, pos, xc["alpha_out"], xc["beta_out"], pre.k_cache, pre.v_cache)
+            sec, _ = timed(cp.run, max(3, args.steps // 4), args.warmup)
+            t = sec / max(3, args.steps // 4)
+            keys = float((pos.double() + 1).sum().item())           # admissible (copy, key) pairs per head
+            fl = 4 * d * Hq * keys
+            nbytes = cB * cT * Hkv * d * 2 * 2 + 2 * cB * cTo * Hq * d * 2
+            out[name] = {"kernel": "orthros_copies (copies_flash_kernel<128>)", "us": t * 1e6, "T": cT,
+                         "T_out": cTo, "copies_per_s": cB * cTo / t, "flops": fl, "TFLOPs": fl / t / 1e12,
+                         "bytes": nbytes, "GBps": nbytes / t / 1e9}
+            result_copies = {"bound": "mfma", "achieved": fl / t / 1e12, "peak": BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": fl / t / 1e12 / BF16_PEAK_TFLOPS, "traffic": None,
+                             "kernel": f"orthros_copies at {name}"}
+            out[name]["roofline"] = result_copies
+            del pre, cp, xc, q_out, pos
+            torch.cuda.empty_cache()
 
     if args.only in ("all", "decode"):
         dcfg = dict(inputs.WORKLOADS["gqa_8b_decode_b16"])

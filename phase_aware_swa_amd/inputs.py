@@ -33,6 +33,12 @@ WORKLOADS = {
     "gqa_8b_decode_b16": dict(kind="decode", dtype=torch.bfloat16, batch=16, n_q_heads=32,
                               n_kv_heads=8, head_dim=128, window=128, len_lo=8192,
                               len_hi=131072, steps=1024),
+    # output copies at many positions (the SFT and PT modes): an answer span
+    # of 4096 copies after a 28K prompt, and every position of a 16K sequence
+    "gqa_8b_sft_32k": dict(kind="copies", dtype=torch.bfloat16, batch=2, n_q_heads=32, n_kv_heads=8,
+                           head_dim=128, T=32768, T_out=4096, window=128),
+    "gqa_8b_pt_16k": dict(kind="copies", dtype=torch.bfloat16, batch=1, n_q_heads=32, n_kv_heads=8,
+                          head_dim=128, T=16384, T_out=16384, window=128),
 }
 
 # A bf16 NaN bit pattern written into cache slots that must never be read or

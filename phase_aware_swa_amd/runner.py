@@ -84,3 +84,21 @@ class Decode:
                             self.beta_out, self.k_cache, self.v_cache, self.cache_len, self.max_len_hint,
                             self.o if o is None else o, self.o_out if o_out is None else o_out,
                             self.workspace, stream)
+
+
+class Copies:
+    """Buffers for orthros_copies over caches filled by a prior SWA pass.
+
+    q_out [B,T_out,Hq,d] and pos [B,T_out] (int32) on the device.
+    """
+
+    def __init__(self, cfg, T, q_out, pos, alpha_out, beta_out, k_cache, v_cache, softmax_scale=0.0):
+        self.desc = desc_for(cfg, softmax_scale)
+        self.T = T
+        self.q_out, self.pos, self.alpha_out, self.beta_out = q_out, pos, alpha_out, beta_out
+        self.k_cache, self.v_cache = k_cache, v_cache
+        self.o_out = torch.empty_like(q_out)
+
+    def run(self, stream=None):
+        binding.copies(self.desc, self.T, self.q_out, self.pos, self.alpha_out, self.beta_out, self.k_cache,
+                       self.v_cache, self.o_out, stream)

@@ -131,3 +131,30 @@ def test_gqa_8b_prefill_1m_36_layers_resident():
     say("workload gqa_8b_prefill_1m: re-read all caches")
     for layer in range(L):
         assert sums[layer] == (bits(kc_all[layer]).sum().item(), bits(vc_all[layer]).sum().item())
+
+
+@pytest.mark.parametrize("name", ["gqa_8b_sft_32k", "gqa_8b_pt_16k"])
+def test_copies_workload(name):
+    """The many-copy workloads in the launch configuration the benchmark
+    times: the library's SWA pass fills the cache, orthros_copies runs over
+    all T_out copies, and 96 sampled copies (the first, the last, and random
+    ones) are checked against the oracle for every head."""
+    from phase_aware_swa_amd.runner import Copies
+    cfg = dict(inputs.WORKLOADS[name])
+    B, T, T_out, Hq, d = cfg["batch"], cfg["T"], cfg["T_out"], cfg["n_q_heads"], cfg["head_dim"]
+    say(f"workload {name}: generate")
+    x = inputs.prefill_inputs(seed=7, device="cuda", **cfg)
+    pre = Prefill(cfg, x)
+    pre.run_swa()
+    q_out, pos = inputs.copies_inputs(B, Hq, d, T, T_out, torch.bfloat16, seed=8, device="cuda")
+    cp = Copies(cfg, T, q_out, pos, x["alpha_out"], x["beta_out"], pre.k_cache, pre.v_cache)
+    say(f"workload {name}: copies")
+    cp.run()
+    torch.cuda.synchronize()
+    g = torch.Generator().manual_seed(9)
+    pick = torch.cat([torch.tensor([0, T_out - 1]), torch.randint(0, T_out, (94,), generator=g)]).unique()
+    say(f"workload {name}: oracle on {pick.numel()} copies x {B} sequences")
+    kc, vc = pre.k_cache.cpu(), pre.v_cache.cpu()
+    ref = oracle.copies(q_out[:, pick].cpu().contiguous(), pos[:, pick].cpu(), x["alpha_out"].cpu(),
+                        x["beta_out"].cpu(), kc, vc, T)
+    assert_parity(cp.o_out[:, pick], ref, torch.bfloat16, f"{name} o_out (sampled copies)")
