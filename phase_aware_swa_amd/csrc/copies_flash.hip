@@ -14,8 +14,9 @@
 //     through a 4-slot LDS ring, two pairs per step: while a step computes,
 //     the next two pairs are in flight into registers, and the slots they
 //     land in are the previous step's, so one barrier per step suffices;
-//   - S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 (layout in
-//     pair_tile.h); keys past a copy's position are masked in the pairs
+//   - S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 (K layout in
+//     pair_tile.h); V stays row-major in LDS and its V^T operands come from
+//     the transposing LDS read; keys past a copy's position are masked in the pairs
 //     that reach past the smallest position of the wave's copies; a wave
 //     skips the pairs past its largest position;
 //   - online softmax in the exp2 domain, rescaled only when a block's
@@ -38,20 +39,38 @@ namespace {
 constexpr int kNs = 4;                    // pair slots of the ring
 constexpr float kMargin = 8.0f;           // lazy-rescale margin, log2 units
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// A pair slot: K rows as in PairTile (read as MFMA A operands of S^T), then
+// V rows kept row-major (32 keys x D), read with ds_read_b64_tr_b16: inside
+// each 16-lane group, output lane l, slot k is element l & 3 of the 8-byte
+// chunk that source lane 4k + (l >> 2) addresses.  Source lane 4k + q of
+// group gq addresses V[key][16 dt + 4q .. + 3] for the group's k-th key, so
+// output lane m receives V[those 4 keys][16 dt + m] -- the V^T operand,
+// transposed by the read.  The 8-byte chunks of a V row are XOR-swizzled
+// by the row so that the two 16-lane groups of a 32-lane access hit
+// distinct banks.
+template <int D>
+struct CopyTile : PairTile<D> {
+    using PairTile<D>::KPART;
+    __device__ static int vswz(int r) { return D == 128 ? 4 * (r & 7) : 4 * ((r >> 1) & 3); }
+    // element offset of 8-byte chunk c8 of V row r, relative to the V part
+    __device__ static int vofs8(int r, int c8) { return r * D + ((c8 ^ vswz(r)) << 2); }
+};
+
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void copies_flash_kernel(
     CopiesParams a, int n_tiles, int hblocks)
 {
-    using R = PairTile<D>;
+    using R = CopyTile<D>;
     constexpr int NT = 256;
     constexpr int C16 = D / 8;                 // 16-byte chunks per row
     constexpr int NQ = D / 32;                 // MFMA k-steps over the head dim
     constexpr int ND = D / 16;                 // 16-wide d tiles of O^T
-    constexpr int KPC = 32 * C16;              // K chunks per pair
-    constexpr int VPC = 16 * (D / 4);          // V (key pair, 4-wide d group) items per pair
+    constexpr int KPC = 32 * C16;              // 16-byte chunks of K (and of V) per pair
     constexpr int KCH = KPC / NT;              // per thread and pair
-    constexpr int VCH = VPC / NT;
-    static_assert(KCH >= 1 && VCH >= 1 && KPC == KCH * NT && VPC == VCH * NT, "head dim");
+    static_assert(KCH >= 1 && KPC == KCH * NT, "head dim");
     __shared__ __align__(16) uint16_t ring[kNs * R::SLOT];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -127,9 +146,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
     }
 
-    // staging of pairs (32 cache rows each): K chunk c = tid + 256 j -> (row c / C16, chunk c % C16);
-    // V item i = tid + 256 j -> key pair i & 15, 4-wide d group i >> 4
-    auto load_pair = [&](int64_t pr, u32x4 (&kr)[KCH], u32x2 (&vr)[VCH][2]) {
+    // staging of pairs (32 cache rows each): K and V chunk c = tid + 256 j -> (row c / C16, chunk c % C16)
+    auto load_pair = [&](int64_t pr, u32x4 (&kr)[KCH], u32x4 (&vr)[KCH]) {
         const int64_t kbase = pr * 32;
         const int64_t avail = (T - kbase) * D * 2;
         const rsrc_t rk = make_rsrc((const uint16_t*)a.k_cache + c_seq + kbase * D, avail);
@@ -138,17 +156,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int j = 0; j < KCH; ++j) {
             const int c = tid + NT * j;
             kr[j] = buf_load16(rk, (uint32_t)((c / C16) * D * 2 + 16 * (c % C16)));
-        }
-#pragma unroll
-        for (int j = 0; j < VCH; ++j) {
-            const int it = tid + NT * j, kp = it & 15, dq = it >> 4;
-            vr[j][0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                rv, (int)(2 * kp * D * 2 + 8 * dq), 0, 0));
-            vr[j][1] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                rv, (int)((2 * kp + 1) * D * 2 + 8 * dq), 0, 0));
+            vr[j] = buf_load16(rv, (uint32_t)((c / C16) * D * 2 + 16 * (c % C16)));
         }
     };
-    auto store_pair = [&](int64_t pr, const u32x4 (&kr)[KCH], const u32x2 (&vr)[VCH][2]) {
+    auto store_pair = [&](int64_t pr, const u32x4 (&kr)[KCH], const u32x4 (&vr)[KCH]) {
         uint16_t* Ks = ring + (int)(pr & (kNs - 1)) * R::SLOT;
         uint16_t* Vt = Ks + R::KPART;
         int t = tid;
@@ -157,19 +168,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int j = 0; j < KCH; ++j) {
             const int c = t + NT * j;
             *(u32x4*)(Ks + R::kofs(c / C16, c % C16)) = kr[j];
-        }
-#pragma unroll
-        for (int j = 0; j < VCH; ++j) {
-            const int it = t + NT * j, kp = it & 15, dq = it >> 4;
-            const int key = 2 * kp, bb = key >> 4, lk = key & 15;
-            const int posn = bb * 4 + (lk & 3);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const uint32_t w0 = vr[j][0][e], w1 = vr[j][1][e];
-                const int d0 = 4 * dq + 2 * e;
-                *(uint32_t*)(Vt + R::vofs(d0, lk >> 2) + posn) = (w0 & 0xffffu) | (w1 << 16);
-                *(uint32_t*)(Vt + R::vofs(d0 + 1, lk >> 2) + posn) = (w0 >> 16) | (w1 & 0xffff0000u);
-            }
+            *(u32x4*)(Vt + R::vofs8(c / C16, 2 * (c % C16))) = vr[j];
         }
     };
 
@@ -238,10 +237,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             pb[hd] = __builtin_bit_cast(bf16x8, pw4);
             lacc[hd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pb[hd], FIRST ? zero : lacc[hd], 0, 0, 0);
         }
+        // V^T operands by transposing reads: this lane addresses key row 4 gq + (n >> 2)
+        // (block 0) and 16 + 4 gq + (n >> 2) (block 1), chunk 4 dt + (n & 3)
         const uint16_t* Vt = Ks + R::KPART;
+        const int vrow = 4 * gq + (n >> 2);
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
-            const bf16x8 vf = *(const bf16x8*)(Vt + R::vofs(16 * dt + n, gq));
+            const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(Vt + R::vofs8(vrow, 4 * dt + (n & 3))));
+            const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(Vt + R::vofs8(16 + vrow, 4 * dt + (n & 3))));
+            const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
 #pragma unroll
             for (int hd = 0; hd < 2; ++hd)
                 oacc[hd][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[hd], FIRST ? zero : oacc[hd][dt],
@@ -253,7 +260,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int64_t last = pmax >> 5;
     const int64_t wlast = wmax >> 5;
     u32x4 kreg[2][KCH];
-    u32x2 vreg[2][VCH][2];
+    u32x4 vreg[2][KCH];
     load_pair(0, kreg[0], vreg[0]);
     if (last >= 1) load_pair(1, kreg[1], vreg[1]);
     store_pair(0, kreg[0], vreg[0]);
@@ -278,15 +285,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     // ---- normalise and store (copies past T_out fall outside the resource)
     const rsrc_t ro = make_rsrc((uint16_t*)a.o_out + q_seq + c0 * a.Hq * D, (T_out - c0) * qrow_b - h0 * D * 2);
-    const bool bad = myp_raw == -2;
+    // an invalid position's NaN is written as a bit pattern (this file is
+    // compiled assuming no NaN arithmetic)
+    const uint32_t nan_mask = myp_raw == -2 ? 0xffffffffu : 0u;
+    constexpr uint32_t kNanPair = 0x7fc07fc0u;
 #pragma unroll
     for (int hd = 0; hd < 2; ++hd) {
-        const float inv = bad ? __builtin_nanf("") : __builtin_amdgcn_rcpf(lacc[hd][0]);
+        const float inv = __builtin_amdgcn_rcpf(lacc[hd][0]);
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
             u32x2 w;
             w[0] = pack_bf16x2(oacc[hd][dt][0] * inv, oacc[hd][dt][1] * inv);
             w[1] = pack_bf16x2(oacc[hd][dt][2] * inv, oacc[hd][dt][3] * inv);
+            w[0] = (w[0] & ~nan_mask) | (kNanPair & nan_mask);
+            w[1] = (w[1] & ~nan_mask) | (kNanPair & nan_mask);
             buf_store8(w, ro, (uint32_t)(n * qrow_b + hd * D * 2 + 2 * (16 * dt + 4 * gq)));
         }
     }
