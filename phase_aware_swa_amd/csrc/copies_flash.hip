@@ -39,31 +39,11 @@ namespace {
 constexpr int kNs = 4;                    // pair slots of the ring
 constexpr float kMargin = 8.0f;           // lazy-rescale margin, log2 units
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// A pair slot: K rows as in PairTile (read as MFMA A operands of S^T), then
-// V rows kept row-major (32 keys x D), read with ds_read_b64_tr_b16: inside
-// each 16-lane group, output lane l, slot k is element l & 3 of the 8-byte
-// chunk that source lane 4k + (l >> 2) addresses.  Source lane 4k + q of
-// group gq addresses V[key][16 dt + 4q .. + 3] for the group's k-th key, so
-// output lane m receives V[those 4 keys][16 dt + m] -- the V^T operand,
-// transposed by the read.  The 8-byte chunks of a V row are XOR-swizzled
-// by the row so that the two 16-lane groups of a 32-lane access hit
-// distinct banks.
-template <int D>
-struct CopyTile : PairTile<D> {
-    using PairTile<D>::KPART;
-    __device__ static int vswz(int r) { return D == 128 ? 4 * (r & 7) : 4 * ((r >> 1) & 3); }
-    // element offset of 8-byte chunk c8 of V row r, relative to the V part
-    __device__ static int vofs8(int r, int c8) { return r * D + ((c8 ^ vswz(r)) << 2); }
-};
-
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void copies_flash_kernel(
     CopiesParams a, int n_tiles, int hblocks)
 {
-    using R = CopyTile<D>;
+    using R = PairTile<D>;
     constexpr int NT = 256;
     constexpr int C16 = D / 8;                 // 16-byte chunks per row
     constexpr int NQ = D / 32;                 // MFMA k-steps over the head dim
@@ -146,7 +126,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
     }
 
-    // staging of pairs (32 cache rows each): K and V chunk c = tid + 256 j -> (row c / C16, chunk c % C16)
+    // staging of pairs (32 cache rows each): K chunk c = tid + 256 j -> (row c / C16, chunk c % C16),
+    // V item tid + 256 j -> (row, chunk) by PairTile::vitem
     auto load_pair = [&](int64_t pr, u32x4 (&kr)[KCH], u32x4 (&vr)[KCH]) {
         const int64_t kbase = pr * 32;
         const int64_t avail = (T - kbase) * D * 2;
@@ -155,8 +136,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int j = 0; j < KCH; ++j) {
             const int c = tid + NT * j;
+            int vr_row, vr_c;
+            R::vitem(c, vr_row, vr_c);
             kr[j] = buf_load16(rk, (uint32_t)((c / C16) * D * 2 + 16 * (c % C16)));
-            vr[j] = buf_load16(rv, (uint32_t)((c / C16) * D * 2 + 16 * (c % C16)));
+            vr[j] = buf_load16(rv, (uint32_t)(vr_row * D * 2 + 16 * vr_c));
         }
     };
     auto store_pair = [&](int64_t pr, const u32x4 (&kr)[KCH], const u32x4 (&vr)[KCH]) {
@@ -167,8 +150,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int j = 0; j < KCH; ++j) {
             const int c = t + NT * j;
+            int vr_row, vr_c;
+            R::vitem(c, vr_row, vr_c);
             *(u32x4*)(Ks + R::kofs(c / C16, c % C16)) = kr[j];
-            *(u32x4*)(Vt + R::vofs8(c / C16, 2 * (c % C16))) = vr[j];
+            *(u32x4*)(Vt + R::vofs16(vr_row, vr_c)) = vr[j];
         }
     };
 
@@ -238,15 +223,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             lacc[hd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pb[hd], FIRST ? zero : lacc[hd], 0, 0, 0);
         }
         // V^T operands by transposing reads: this lane addresses key row 4 gq + (n >> 2)
-        // (block 0) and 16 + 4 gq + (n >> 2) (block 1), chunk 4 dt + (n & 3)
-        const uint16_t* Vt = Ks + R::KPART;
-        const int vrow = 4 * gq + (n >> 2);
+        // (block 0) and 16 + 4 gq + (n >> 2) (block 1), dims 16 dt + 4 (n & 3)
+        // (one base per pair, opaque, so that the steps stay immediate offsets)
+        int vo = (int)(pr & (kNs - 1)) * R::SLOT + R::KPART + R::vofs_tr(4 * gq + (n >> 2), 0, n & 3);
+        asm volatile("" : "+v"(vo));
+        const uint16_t* vb = ring + vo;
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
-            const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(Vt + R::vofs8(vrow, 4 * dt + (n & 3))));
-            const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(Vt + R::vofs8(16 + vrow, 4 * dt + (n & 3))));
+            const s16x4 v0 = lds_read_tr(vb + dt * R::V_DT);
+            const s16x4 v1 = lds_read_tr(vb + R::V_KEY16 + dt * R::V_DT);
             const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
             const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
 #pragma unroll

@@ -4,19 +4,32 @@
 //
 // S^T = K Q^T per 16-key block leaves each lane (n = query, gq = lane/16)
 // with keys 4gq..4gq+3 of the block; the P^T operand of O^T = V^T P^T over a
-// pair is then [block 0 keys 4gq..+3, block 1 keys 4gq..+3].  V^T rows of a
-// pair slot store the 32 keys in exactly that order, so each PV operand is a
-// single 16-byte LDS read.  Both parts are XOR-swizzled instead of padded:
-// the MFMA operand reads (16 rows x 16 bytes per 16 lanes) hit 16 distinct
-// 16-byte bank groups.
+// pair is then [block 0 keys 4gq..+3, block 1 keys 4gq..+3].
+//
+// K rows: 16-byte chunks XOR-swizzled by row, so the S^T operand reads
+// (16 rows x 16 bytes per 16 lanes) hit 16 distinct 16-byte bank groups.
+//
+// V is stored in 256-byte lines of 8 keys x 16 head dims,
+// [key / 8][d / 16][key % 8][d % 16], and read with ds_read_b64_tr_b16:
+// inside each 16-lane group, output lane l, slot k is element l & 3 of the
+// 8-byte chunk that source lane 4k + (l >> 2) addresses.  Source lane
+// 4k + q of a group addresses keys' d = 16 dt + 4q .. + 3, so output lane m
+// receives V[the group's 4 keys][16 dt + m] -- the V^T operand, transposed
+// by the read.  A 32-lane access of 8 keys x 4 chunks then covers one line
+// (every LDS bank once), and dt is an immediate offset.
 #pragma once
 
+#include <hip/hip_runtime.h>
+
 namespace orthros {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 template <int D>
 struct PairTile {
     static constexpr int KPART = 32 * D;    // bf16: K rows of the two blocks
-    static constexpr int VPART = D * 32;    // bf16: V^T rows, 32 keys each
+    static constexpr int VPART = 32 * D;    // bf16: V rows of the two blocks
     static constexpr int SLOT = KPART + VPART;
     // K: row = key of the pair (0..31); 16-byte chunks XOR-swizzled by row.
     __device__ static int kofs(int r, int c)
@@ -24,9 +37,28 @@ struct PairTile {
         const int sw = (D == 128) ? (r & 15) : ((r >> 1) & 7);
         return r * D + ((c ^ sw) << 3);
     }
-    // V^T: row d = 64 bytes = four 16-byte units; unit u holds keys
-    // 4u..4u+3 of block 0 then of block 1; XOR by bits 2..3 of d.
-    __device__ static int vofs(int d, int u) { return d * 32 + ((u ^ ((d >> 2) & 3)) << 3); }
+    // V: element offset of head dims 16 dt + 4 q .. + 3 of key r (an 8-byte
+    // transposing-read chunk), and of 16-byte chunk c (dims 8c .. 8c + 7).
+    __device__ static int vofs_tr(int r, int dt, int q) { return (r >> 3) * 8 * D + dt * 128 + (r & 7) * 16 + 4 * q; }
+    __device__ static int vofs16(int r, int c) { return (r >> 3) * 8 * D + (c >> 1) * 128 + (r & 7) * 16 + 8 * (c & 1); }
+    // Immediate steps of vofs_tr: dt + 1 is one line on, key r + 16
+    // (r < 16) two 8-key groups on, and key r + 4 (r & 7 < 4) half a line.
+    static constexpr int V_DT = 128, V_KEY16 = 16 * D, V_KEY8 = 8 * D, V_KEY4 = 64;
+    // Staging order of V chunks: item it -> key row, 16-byte chunk.  The 16
+    // lanes of one 16-byte LDS store cover one line (8 keys x 2 chunks), and
+    // a wave's global loads cover 8 keys x 128 contiguous bytes.
+    __device__ static void vitem(int it, int& r, int& c)
+    {
+        constexpr int LDT = D == 128 ? 3 : 2;        // log2(D / 16)
+        r = ((it >> (4 + LDT)) << 3) | ((it >> 1) & 7);
+        c = (((it >> 4) & ((1 << LDT) - 1)) << 1) | (it & 1);
+    }
 };
+
+// Four bf16 of V^T through the transposing read (see above).
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+}
 
 }  // namespace orthros

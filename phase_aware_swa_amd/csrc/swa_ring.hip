@@ -10,7 +10,7 @@
 //     so every K/V fragment it reads from LDS feeds two MFMAs, and two
 //     workgroups share a CU (2 waves per SIMD, up to 256 registers each);
 //   - the window of a 32-row tile spans at most 5 blocks of 32 keys, kept in
-//     a 5-slot ring of K and V^T blocks in LDS (16 KB per slot at d = 128,
+//     a 5-slot ring of K and V blocks in LDS (16 KB per slot at d = 128,
 //     XOR-swizzled instead of padded so that two workgroups fit in one CU's
 //     160 KB): each K/V byte is read from HBM once, and the 128-key halo
 //     stays on chip between tiles;
@@ -65,9 +65,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int C16 = D / 8;                 // 16-byte chunks per row
     constexpr int NQ = D / 32;                 // MFMA k-steps over the head dim (32 each)
     constexpr int ND = D / 16;                 // 16-wide d tiles of O^T
-    constexpr int KCH = 32 * C16 / NT;         // K chunks per thread per pair
-    constexpr int VCH = 16 * (D / 4) / NT;     // V (key pair, 4-wide d group) items per thread per pair
-    static_assert(KCH >= 1 && VCH >= 1, "head dim");
+    constexpr int KCH = 32 * C16 / NT;         // K (and V) chunks per thread per pair
+    static_assert(KCH >= 1, "head dim");
     __shared__ __align__(16) uint16_t ring[NS * R::SLOT];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -99,9 +98,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int64_t q_seq = (int64_t)b * T * a.Hq * D + (int64_t)h0 * D;
     const int64_t c_seq = ((int64_t)b * a.Hkv + g) * a.cap * D;
 
-    // staging of one pair (32 new keys): K chunk c = tid + 256 j -> (row c / C16, chunk c % C16);
-    // V item i = tid + 256 j -> key pair i & 15, 4-wide d group i >> 4
-    auto load_pair = [&](int64_t pr, u32x4 (&kr)[KCH], u32x2 (&vr)[VCH][2]) {
+    // staging of one pair (32 new keys): K chunk c = tid + 256 j -> (row c / C16, chunk c % C16),
+    // V item tid + 256 j -> (row, chunk) by PairTile::vitem
+    auto load_pair = [&](int64_t pr, u32x4 (&kr)[KCH], u32x4 (&vr)[KCH]) {
         const int64_t kbase = pr * 32;
         const int64_t avail = (T - kbase) * krow_b - g * D * 2;
         const rsrc_t rk = make_rsrc((const uint16_t*)a.k + kv_seq + kbase * a.Hkv * D, avail);
@@ -109,18 +108,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int j = 0; j < KCH; ++j) {
             const int c = tid + NT * j;
+            int vr_row, vr_c;
+            R::vitem(c, vr_row, vr_c);
             kr[j] = buf_load16(rk, (uint32_t)((c / C16) * krow_b + 16 * (c % C16)));
-        }
-#pragma unroll
-        for (int j = 0; j < VCH; ++j) {
-            const int it = tid + NT * j, kp = it & 15, dq = it >> 4;
-            vr[j][0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                rv, (int)(2 * kp * krow_b + 8 * dq), 0, 0));
-            vr[j][1] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                rv, (int)((2 * kp + 1) * krow_b + 8 * dq), 0, 0));
+            vr[j] = buf_load16(rv, (uint32_t)(vr_row * krow_b + 16 * vr_c));
         }
     };
-    auto store_pair = [&](int64_t pr, bool own, const u32x4 (&kr)[KCH], const u32x2 (&vr)[VCH][2]) {
+    auto store_pair = [&](int64_t pr, bool own, const u32x4 (&kr)[KCH], const u32x4 (&vr)[KCH]) {
         uint16_t* Ks = ring + (int)(pr % NS) * R::SLOT;
         uint16_t* Vt = Ks + R::KPART;
         // recompute the thread's LDS offsets here rather than keep them live
@@ -130,20 +124,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int j = 0; j < KCH; ++j) {
             const int c = t + NT * j;
+            int vr_row, vr_c;
+            R::vitem(c, vr_row, vr_c);
             *(u32x4*)(Ks + R::kofs(c / C16, c % C16)) = kr[j];
-        }
-#pragma unroll
-        for (int j = 0; j < VCH; ++j) {
-            const int it = t + NT * j, kp = it & 15, dq = it >> 4;
-            const int key = 2 * kp, bb = key >> 4, lk = key & 15;
-            const int pos = bb * 4 + (lk & 3);           // within the 16-byte unit lk / 4
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const uint32_t w0 = vr[j][0][e], w1 = vr[j][1][e];
-                const int d0 = 4 * dq + 2 * e;
-                *(uint32_t*)(Vt + R::vofs(d0, lk >> 2) + pos) = (w0 & 0xffffu) | (w1 << 16);
-                *(uint32_t*)(Vt + R::vofs(d0 + 1, lk >> 2) + pos) = (w0 >> 16) | (w1 & 0xffff0000u);
-            }
+            *(u32x4*)(Vt + R::vofs16(vr_row, vr_c)) = vr[j];
         }
         if (own && writer) {
             const int64_t kbase = pr * 32;
@@ -153,13 +137,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int j = 0; j < KCH; ++j) {
                 const int c = t + NT * j;
+                int vr_row, vr_c;
+                R::vitem(c, vr_row, vr_c);
                 buf_store16(kr[j], ck, (uint32_t)((c / C16) * D * 2 + 16 * (c % C16)));
-            }
-#pragma unroll
-            for (int j = 0; j < VCH; ++j) {
-                const int it = t + NT * j, kp = it & 15, dq = it >> 4;
-                __builtin_amdgcn_raw_buffer_store_b64(vr[j][0], cv, (int)(2 * kp * D * 2 + 8 * dq), 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b64(vr[j][1], cv, (int)((2 * kp + 1) * D * 2 + 8 * dq), 0, 0);
+                buf_store16(vr[j], cv, (uint32_t)(vr_row * D * 2 + 16 * vr_c));
             }
         }
     };
@@ -209,7 +190,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
 
     u32x4 kreg[KCH];
-    u32x2 vreg[VCH][2];
+    u32x4 vreg[KCH];
     u32x4 qraw[2][NQ];
     bf16x8 qf[2][NQ];
     const bf16x8 kOnes = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
@@ -238,7 +219,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // with the full score of key STEPS kg + m (both lanes of a pair).  The
     // online softmax state (gm) is wave-uniform, gl is per lane (each key
     // counted twice); P goes to scalar registers as bf16 pairs, and lane l
-    // accumulates rows l + 64 r of V^T P with v_dot2_f32_bf16.
+    // accumulates rows l + 64 r of V^T P with v_dot2_f32_bf16, reading its
+    // V^T row four keys at a time by transposing LDS reads.
     constexpr int LPK = D / 8;                  // lanes per key (16-byte chunks of a row)
     constexpr int STEPS = 32 * LPK / 64;        // keys of the pair per lane group
     constexpr int RPL = D / 64;                 // V^T rows per lane
@@ -315,18 +297,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int j = 0; j < 16; ++j)
             pw[j] = (uint32_t)__builtin_amdgcn_readlane(wrd, LPK * ((2 * j) / STEPS) + 2 * ((2 * j) % STEPS));
-        const uint16_t* Vt = Ks + R::KPART;
+        // read i: this lane addresses key 4 i + (n >> 2), dims 16 (gq + 4 r) + 4 (n & 3),
+        // and receives keys 4 i .. 4 i + 3 of V^T row lane + 64 r.  One base
+        // per pair (opaque, so that the steps stay immediate offsets).
+        int vo = (int)(pr % NS) * R::SLOT + R::KPART + R::vofs_tr(n >> 2, gq, n & 3);
+        asm volatile("" : "+v"(vo));
+        const uint16_t* vb = ring + vo;
 #pragma unroll
         for (int r = 0; r < RPL; ++r) {
-            const int d = lane + 64 * r;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                // unit u of V^T row d: keys (4u, 4u+1), (4u+2, 4u+3), (16+4u, 17+4u), (18+4u, 19+4u)
-                const u32x4 vw = *(const u32x4*)(Vt + R::vofs(d, u));
-                const int jj[4] = {2 * u, 2 * u + 1, 8 + 2 * u, 9 + 2 * u};
+            for (int i = 0; i < 8; ++i) {
+                const s16x4 vv =
+                    lds_read_tr(vb + (i >> 1) * R::V_KEY8 + (i & 1) * R::V_KEY4 + 4 * r * R::V_DT);
+                const u32x2 vw = __builtin_bit_cast(u32x2, vv);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t x = vw[e], y = pw[jj[e]];
+                for (int e = 0; e < 2; ++e) {
+                    // through scalars: a bit_cast of a vector element directly
+                    // miscompiles (every dot2 then reads element 0)
+                    const uint32_t x = vw[e], y = pw[2 * i + e];
                     gacc[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x),
                                                               __builtin_bit_cast(bf16x2, y), gacc[r], false);
                 }
@@ -431,10 +419,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 pb[hd] = __builtin_bit_cast(bf16x8, pw);
                 lacc[hd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pb[hd], FIRST ? zero : lacc[hd], 0, 0, 0);
             }
-            const uint16_t* Vt = Ks + R::KPART;
+            // V^T operands by transposing reads: this lane addresses key row
+            // 4 gq + (n >> 2) of each block, dims 16 dt + 4 (n & 3).  One
+            // base per pair (opaque, so that the steps stay immediate offsets).
+            int vo = (int)(pr % NS) * R::SLOT + R::KPART + R::vofs_tr(4 * gq + (n >> 2), 0, n & 3);
+            asm volatile("" : "+v"(vo));
+            const uint16_t* vb = ring + vo;
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt) {
-                const bf16x8 vf = *(const bf16x8*)(Vt + R::vofs(16 * dt + n, gq));
+                const u32x2 w0 = __builtin_bit_cast(u32x2, lds_read_tr(vb + dt * R::V_DT));
+                const u32x2 w1 = __builtin_bit_cast(u32x2, lds_read_tr(vb + R::V_KEY16 + dt * R::V_DT));
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
 #pragma unroll
                 for (int hd = 0; hd < 2; ++hd)
                     oacc[hd][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[hd], FIRST ? zero : oacc[hd][dt],
