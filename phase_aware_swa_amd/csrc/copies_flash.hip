@@ -126,20 +126,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
     }
 
-    // staging of pairs (32 cache rows each): K chunk c = tid + 256 j -> (row c / C16, chunk c % C16),
-    // V item tid + 256 j -> (row, chunk) by PairTile::vitem
+    // staging of pairs (32 cache rows each): item tid + 256 j -> (row, chunk) by
+    // PairTile::kitem for K and PairTile::vitem for V; item + 256 is the same
+    // chunk 16 rows on (KCH is 2 only at d = 128)
+    static_assert(KCH == 1 || NT / C16 == 16, "staging step");
     auto load_pair = [&](int64_t pr, u32x4 (&kr)[KCH], u32x4 (&vr)[KCH]) {
         const int64_t kbase = pr * 32;
         const int64_t avail = (T - kbase) * D * 2;
         const rsrc_t rk = make_rsrc((const uint16_t*)a.k_cache + c_seq + kbase * D, avail);
         const rsrc_t rv = make_rsrc((const uint16_t*)a.v_cache + c_seq + kbase * D, avail);
+        int kr_row, kr_c, vr_row, vr_c;
+        R::kitem(tid, kr_row, kr_c);
+        R::vitem(tid, vr_row, vr_c);
 #pragma unroll
         for (int j = 0; j < KCH; ++j) {
-            const int c = tid + NT * j;
-            int vr_row, vr_c;
-            R::vitem(c, vr_row, vr_c);
-            kr[j] = buf_load16(rk, (uint32_t)((c / C16) * D * 2 + 16 * (c % C16)));
-            vr[j] = buf_load16(rv, (uint32_t)(vr_row * D * 2 + 16 * vr_c));
+            kr[j] = buf_load16(rk, (uint32_t)((kr_row + 16 * j) * D * 2 + 16 * kr_c));
+            vr[j] = buf_load16(rv, (uint32_t)((vr_row + 16 * j) * D * 2 + 16 * vr_c));
         }
     };
     auto store_pair = [&](int64_t pr, const u32x4 (&kr)[KCH], const u32x4 (&vr)[KCH]) {
@@ -147,13 +149,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         uint16_t* Vt = Ks + R::KPART;
         int t = tid;
         asm volatile("" : "+v"(t));
+        int kr_row, kr_c, vr_row, vr_c;
+        R::kitem(t, kr_row, kr_c);
+        R::vitem(t, vr_row, vr_c);
 #pragma unroll
         for (int j = 0; j < KCH; ++j) {
-            const int c = t + NT * j;
-            int vr_row, vr_c;
-            R::vitem(c, vr_row, vr_c);
-            *(u32x4*)(Ks + R::kofs(c / C16, c % C16)) = kr[j];
-            *(u32x4*)(Vt + R::vofs16(vr_row, vr_c)) = vr[j];
+            *(u32x4*)(Ks + R::kofs(kr_row, kr_c) + j * R::K_KEY16) = kr[j];
+            *(u32x4*)(Vt + R::vofs16(vr_row, vr_c) + j * R::V_KEY16) = vr[j];
         }
     };
 
@@ -165,13 +167,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // maxima and the accumulators
     auto attend = [&](auto first_tag, int64_t pr) {
         constexpr bool FIRST = decltype(first_tag)::value;
-        const uint16_t* Ks = ring + (int)(pr & (kNs - 1)) * R::SLOT;
+        // one K base per pair (opaque, so that the steps stay immediate offsets)
+        int ko = (int)(pr & (kNs - 1)) * R::SLOT + R::kofs(n, gq);
+        asm volatile("" : "+v"(ko));
+        const uint16_t* kb = ring + ko;
         const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
         f32x4 s[2][2];
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
-            const bf16x8 k0 = *(const bf16x8*)(Ks + R::kofs(n, 4 * i + gq));
-            const bf16x8 k1 = *(const bf16x8*)(Ks + R::kofs(16 + n, 4 * i + gq));
+            const bf16x8 k0 = *(const bf16x8*)(kb + i * R::K_STEP);
+            const bf16x8 k1 = *(const bf16x8*)(kb + i * R::K_STEP + R::K_KEY16);
 #pragma unroll
             for (int hd = 0; hd < 2; ++hd) {
                 s[hd][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[hd][i], i ? s[hd][0] : zero, 0, 0, 0);

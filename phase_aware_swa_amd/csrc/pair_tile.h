@@ -6,8 +6,12 @@
 // with keys 4gq..4gq+3 of the block; the P^T operand of O^T = V^T P^T over a
 // pair is then [block 0 keys 4gq..+3, block 1 keys 4gq..+3].
 //
-// K rows: 16-byte chunks XOR-swizzled by row, so the S^T operand reads
-// (16 rows x 16 bytes per 16 lanes) hit 16 distinct 16-byte bank groups.
+// K is stored by 16-byte chunk columns: chunk c = 4 i + q of key r at
+// 16-byte unit 128 i + 32 q + (r & 16) + ((r + 4 q) & 15).  The S^T operand
+// read of k-step i (lane (n, gq): key n of a block, chunk 4 i + gq) is then
+// one per-lane base plus the immediate 1024 i (+ 128 for block 1), and the
+// 16 lanes of a 16-byte access (16 keys, one chunk) hit 16 distinct 16-byte
+// bank groups; so do staging stores of 4 keys x 4 chunks.
 //
 // V is stored in 256-byte lines of 8 keys x 16 head dims,
 // [key / 8][d / 16][key % 8][d % 16], and read with ds_read_b64_tr_b16:
@@ -31,11 +35,22 @@ struct PairTile {
     static constexpr int KPART = 32 * D;    // bf16: K rows of the two blocks
     static constexpr int VPART = 32 * D;    // bf16: V rows of the two blocks
     static constexpr int SLOT = KPART + VPART;
-    // K: row = key of the pair (0..31); 16-byte chunks XOR-swizzled by row.
+    // K: element offset of 16-byte chunk c (dims 8c .. 8c + 7) of key r.
     __device__ static int kofs(int r, int c)
     {
-        const int sw = (D == 128) ? (r & 15) : ((r >> 1) & 7);
-        return r * D + ((c ^ sw) << 3);
+        const int q = c & 3;
+        return ((c >> 2) * 128 + q * 32 + (r & 16) + ((r + 4 * q) & 15)) * 8;
+    }
+    // Immediate steps of kofs: k-step i + 1 (chunk c + 4), key r + 16.
+    static constexpr int K_STEP = 1024, K_KEY16 = 128;
+    // Staging order of K chunks: item it -> key row, 16-byte chunk.  The 16
+    // lanes of one 16-byte LDS store cover 4 keys x 4 chunks, and a wave's
+    // global loads cover whole rows.
+    __device__ static void kitem(int it, int& r, int& c)
+    {
+        constexpr int LNQ = D == 128 ? 2 : 1;        // log2(D / 32)
+        r = ((it >> (4 + LNQ)) << 2) | ((it >> 2) & 3);
+        c = (((it >> 4) & ((1 << LNQ) - 1)) << 2) | (it & 3);
     }
     // V: element offset of head dims 16 dt + 4 q .. + 3 of key r (an 8-byte
     // transposing-read chunk), and of 16-byte chunk c (dims 8c .. 8c + 7).
