@@ -14,6 +14,10 @@
  *   - both streams' queries come from one shared projection followed by a
  *     per-stream elementwise scale-offset q * alpha + beta, [N] §2.2.
  *
+ * Either side of the attention ([N] §2.1-§2.2): the base stream's K/V come
+ * from the base input X at every position and both streams' queries from one
+ * shared W_Q; orthros_project computes them and writes K/V into the cache.
+ *
  * Modes ([N] §2.5, mode table): prefill has T_in = T-1 base-only tokens and
  * T_out = 1 copy (the last prompt position); decode processes one new base
  * token and one copy per step, the copy reading the whole history.
@@ -51,7 +55,7 @@
 extern "C" {
 #endif
 
-#define ORTHROS_ABI_VERSION 2
+#define ORTHROS_ABI_VERSION 3
 
 typedef enum {
     ORTHROS_OK = 0,
@@ -176,6 +180,45 @@ orthros_status orthros_copies(const orthros_desc* desc, int64_t T, int64_t T_out
                               const void* alpha_out, const void* beta_out,
                               const void* k_cache, const void* v_cache, int64_t cap,
                               void* o_out, void* stream);
+
+/* ---------------------------------------------------------- projections */
+
+/*
+ * The projections on either side of one layer's attention step ([N] §2.1:
+ * the base stream's K/V come from the layer's base input X for every
+ * position and are that layer's cache rows; §2.2: both streams' queries come
+ * from the one shared W_Q, then each stream's elementwise scale-offset).
+ * One launch, one pass over the stacked rows [X; X']:
+ *   q[b][t]       = (x[b][t] W_Q^T) * alpha + beta
+ *   q_out[b][i]   = (x_out[b][i] W_Q^T) * alpha_out + beta_out
+ *   k_cache[b][g][t] = (x[b][t] W_K^T) head g,  v_cache likewise with W_V
+ * bf16 storage only (ORTHROS_E_DTYPE otherwise); fp32 accumulation, outputs
+ * rounded to nearest even.  desc->window and softmax_scale are not used.
+ *
+ *   T          base rows per sequence, 1 <= T <= cap
+ *   T_out      copy rows per sequence, >= 0 (prefill: 1; PT/SFT: the copies)
+ *   d_model    the layer's input width, a multiple of 32 in [32, 65536]
+ *   x          device [B][T][d_model]       base input X
+ *   x_out      device [B][T_out][d_model]   copy inputs X' (may be NULL when T_out = 0)
+ *   w_q        device [Hq*d][d_model]       W_Q stored [out][in] (y = x W^T)
+ *   w_k, w_v   device [Hkv*d][d_model]
+ *   alpha, beta          device [Hq][d] or both NULL: no scale-offset on q
+ *   alpha_out, beta_out  device [Hq][d] or both NULL: none on q_out
+ *              (pass NULL to feed orthros_prefill / orthros_copies, which
+ *              apply the scale-offset themselves)
+ *   q          device [B][T][Hq][d]
+ *   q_out      device [B][T_out][Hq][d] (may be NULL when T_out = 0)
+ *   k_cache, v_cache     device [B][Hkv][cap][d]; slots [0, T) are written,
+ *              every other slot is left untouched
+ * Needs n_q_heads*d and n_kv_heads*d to be multiples of 128.
+ */
+orthros_status orthros_project(const orthros_desc* desc, int64_t T, int64_t T_out, int64_t d_model,
+                               const void* x, const void* x_out,
+                               const void* w_q, const void* w_k, const void* w_v,
+                               const void* alpha, const void* beta,
+                               const void* alpha_out, const void* beta_out,
+                               void* q, void* q_out, void* k_cache, void* v_cache, int64_t cap,
+                               void* stream);
 
 /* -------------------------------------------------------------- decode */
 

@@ -65,6 +65,8 @@ def lib():
         L.orthros_decode_step.restype = ctypes.c_int
         L.orthros_copies.argtypes = [dp, i64, i64, vp, vp, vp, vp, vp, vp, i64, vp, vp]
         L.orthros_copies.restype = ctypes.c_int
+        L.orthros_project.argtypes = [dp, i64, i64, i64] + [vp] * 13 + [i64, vp]
+        L.orthros_project.restype = ctypes.c_int
         L.orthros_status_str.argtypes = [ctypes.c_int]
         L.orthros_status_str.restype = ctypes.c_char_p
         L.orthros_last_error.argtypes = []
@@ -152,6 +154,16 @@ def copies(desc, T, q_out, out_pos, alpha_out, beta_out, k_cache, v_cache, o_out
         ctypes.byref(desc), T, q_out.shape[1] if q_out is not None else 0, _ptr(q_out), _ptr(out_pos),
         _ptr(alpha_out), _ptr(beta_out), _ptr(k_cache), _ptr(v_cache),
         k_cache.shape[2] if k_cache is not None else 0, _ptr(o_out), _stream(stream)))
+
+
+def project(desc, T, d_model, x, x_out, w_q, w_k, w_v, alpha, beta, alpha_out, beta_out, q, q_out, k_cache,
+            v_cache, stream=None):
+    """orthros_project; x [B,T,d_model], x_out [B,T_out,d_model] or None; alpha..beta_out may be None."""
+    T_out = x_out.shape[1] if x_out is not None else 0
+    _check(lib().orthros_project(
+        ctypes.byref(desc), T, T_out, d_model, _ptr(x), _ptr(x_out), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(alpha),
+        _ptr(beta), _ptr(alpha_out), _ptr(beta_out), _ptr(q), _ptr(q_out), _ptr(k_cache), _ptr(v_cache),
+        k_cache.shape[2] if k_cache is not None else 0, _stream(stream)))
 
 
 def abi_version():

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liborthros.so")
-SOURCES = ["api.hip", "swa_prefill.hip", "swa_ring.hip", "global_xattn.hip", "copies_flash.hip"]
+SOURCES = ["api.hip", "swa_prefill.hip", "swa_ring.hip", "global_xattn.hip", "copies_flash.hip", "project.hip"]
 # The attention kernels never produce or test NaNs in float arithmetic (masked
 # scores are -inf, running maxima start finite; an invalid copy position writes its
 # NaN as a bit pattern), so fmax needs no NaN quieting there.

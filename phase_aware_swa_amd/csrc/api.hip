@@ -336,6 +336,46 @@ orthros_status orthros_copies(const orthros_desc* desc, int64_t T, int64_t T_out
     return hip_status(orthros::launch_copies(p, (hipStream_t)stream), "copies kernel launch");
 }
 
+orthros_status orthros_project(const orthros_desc* desc, int64_t T, int64_t T_out, int64_t d_model,
+                               const void* x, const void* x_out, const void* w_q, const void* w_k, const void* w_v,
+                               const void* alpha, const void* beta, const void* alpha_out, const void* beta_out,
+                               void* q, void* q_out, void* k_cache, void* v_cache, int64_t cap, void* stream)
+{
+    g_err.clear();
+    orthros_status st = check_desc(desc);
+    if (st) return st;
+    if (desc->dtype != ORTHROS_BF16) return fail(ORTHROS_E_DTYPE, "orthros_project takes bf16 tensors only");
+    if ((st = check_T(desc, T, cap))) return st;
+    if (T_out < 0 || T_out > INT32_MAX)
+        return fail(ORTHROS_E_SHAPE, "T_out = %lld outside [0, 2^31)", (long long)T_out);
+    if (d_model < 32 || d_model > 65536 || d_model % 32)
+        return fail(ORTHROS_E_SHAPE, "d_model = %lld: must be a multiple of 32 in [32, 65536]", (long long)d_model);
+    const int64_t nq = (int64_t)desc->n_q_heads * desc->head_dim, nk = (int64_t)desc->n_kv_heads * desc->head_dim;
+    if (nq % 128 || nk % 128)
+        return fail(ORTHROS_E_SHAPE, "n_q_heads * head_dim (%lld) and n_kv_heads * head_dim (%lld) must be "
+                    "multiples of 128", (long long)nq, (long long)nk);
+    const int64_t rows = (int64_t)desc->batch * (T + T_out);
+    if (rows > kMaxElems / d_model || (int64_t)desc->batch * T_out > kMaxElems / nq)
+        return fail(ORTHROS_E_SHAPE, "tensor sizes overflow the library's 2^50-element bound");
+    if ((st = check_ptrs({x, w_q, w_k, w_v, q, k_cache, v_cache}))) return st;
+    if (T_out > 0 && (st = check_ptrs({x_out, q_out}))) return st;
+    if (!alpha != !beta || !alpha_out != !beta_out)
+        return fail(ORTHROS_E_NULL, "alpha and beta (and alpha_out and beta_out) must be given together");
+    for (const void* v : {alpha, beta, alpha_out, beta_out})
+        if (v && !aligned16(v)) return fail(ORTHROS_E_ALIGN, "a device pointer is not 16-byte aligned");
+    orthros::ProjParams p;
+    p.x = (const uint16_t*)x; p.xo = (const uint16_t*)x_out;
+    p.wq = (const uint16_t*)w_q; p.wk = (const uint16_t*)w_k; p.wv = (const uint16_t*)w_v;
+    p.alpha = (const uint16_t*)alpha; p.beta = (const uint16_t*)beta;
+    p.alpha_out = (const uint16_t*)alpha_out; p.beta_out = (const uint16_t*)beta_out;
+    p.q = (uint16_t*)q; p.q_out = (uint16_t*)q_out; p.k_cache = (uint16_t*)k_cache; p.v_cache = (uint16_t*)v_cache;
+    p.Mx = (int64_t)desc->batch * T; p.Mo = (int64_t)desc->batch * T_out;
+    p.T = T; p.cap = cap; p.K = d_model; p.tiles_b = 0;
+    p.Hq = desc->n_q_heads; p.Hkv = desc->n_kv_heads; p.D = desc->head_dim;
+    if (!orthros::project_applies(p)) return fail(ORTHROS_E_SHAPE, "shape not supported by the projection kernel");
+    return hip_status(orthros::launch_project(p, (hipStream_t)stream), "projection kernel launch");
+}
+
 orthros_status orthros_decode_step(const orthros_desc* desc, const void* q, const void* q_out,
                                    const void* k_new, const void* v_new, const void* alpha, const void* beta,
                                    const void* alpha_out, const void* beta_out, void* k_cache, void* v_cache,

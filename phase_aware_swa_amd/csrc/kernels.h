@@ -116,4 +116,29 @@ hipError_t launch_copies(const CopiesParams& p, hipStream_t s);
 bool copies_flash_applies(const CopiesParams& p);
 hipError_t launch_copies_flash(const CopiesParams& p, hipStream_t s);
 
+// The projections either side of the attention step (bf16): q and k/v of the
+// base rows X, q' of the copy rows X', one shared W_Q.
+struct ProjParams {
+    const uint16_t* x;          // [Mx][K], Mx = B * T
+    const uint16_t* xo;         // [Mo][K], Mo = B * T_out (may be null when Mo = 0)
+    const uint16_t* wq;         // [Hq*D][K]
+    const uint16_t* wk;         // [Hkv*D][K]
+    const uint16_t* wv;
+    const uint16_t* alpha;      // [Hq*D]; null (with beta) = no scale-offset
+    const uint16_t* beta;
+    const uint16_t* alpha_out;  // same, for the copy rows
+    const uint16_t* beta_out;
+    uint16_t* q;                // [Mx][Hq*D]
+    uint16_t* q_out;            // [Mo][Hq*D]
+    uint16_t* k_cache;          // [B][Hkv][cap][D]
+    uint16_t* v_cache;
+    int64_t Mx, Mo, T, cap, K;
+    int64_t tiles_b;            // set by the launcher
+    int32_t Hq, Hkv, D;
+};
+// Shapes the tiled kernel takes: Hq*D and Hkv*D multiples of 128, K a
+// multiple of 32.
+bool project_applies(const ProjParams& p);
+hipError_t launch_project(const ProjParams& p, hipStream_t s);
+
 }  // namespace orthros

@@ -39,6 +39,10 @@ WORKLOADS = {
                            head_dim=128, T=32768, T_out=4096, window=128),
     "gqa_8b_pt_16k": dict(kind="copies", dtype=torch.bfloat16, batch=1, n_q_heads=32, n_kv_heads=8,
                           head_dim=128, T=16384, T_out=16384, window=128),
+    # the projections either side of the 8B-class layer's attention (d_model
+    # 4096) over the 128K prefill: X of both sequences, one copy row each
+    "gqa_8b_project_128k": dict(kind="project", dtype=torch.bfloat16, batch=2, n_q_heads=32, n_kv_heads=8,
+                                head_dim=128, T=131072, T_out=1, d_model=4096, window=128),
 }
 
 # A bf16 NaN bit pattern written into cache slots that must never be read or
@@ -111,6 +115,28 @@ def copies_inputs(batch, n_q_heads, head_dim, T, T_out, dtype, seed, device="cpu
     else:
         pos = torch.randint(0, T, (batch, T_out), generator=g, device=device).to(torch.int32)
     return q_out, pos.contiguous()
+
+
+def project_inputs(batch, n_q_heads, n_kv_heads, head_dim, T, T_out, d_model, seed, device="cpu",
+                   dtype=torch.bfloat16, **_):
+    """Inputs of the projections: x [B,T,d_model] and x_out [B,T_out,d_model]
+    ~ N(0,1); w_q [Hq*d, d_model], w_k, w_v [Hkv*d, d_model] ~ N(0, 1/d_model)
+    (so each projected value is ~ N(0,1)); alpha, alpha_out ~ 1 + 0.1 N,
+    beta, beta_out ~ 0.1 N, each [Hq, d].  Drawn in this order."""
+    g = _gen(seed, device)
+    B, Hq, Hkv, d = batch, n_q_heads, n_kv_heads, head_dim
+    s = d_model ** -0.5
+    x = {}
+    x["x"] = _normal((B, T, d_model), g, device, dtype)
+    x["x_out"] = _normal((B, T_out, d_model), g, device, dtype)
+    x["w_q"] = _normal((Hq * d, d_model), g, device, dtype, std=s)
+    x["w_k"] = _normal((Hkv * d, d_model), g, device, dtype, std=s)
+    x["w_v"] = _normal((Hkv * d, d_model), g, device, dtype, std=s)
+    x["alpha"] = _normal((Hq, d), g, device, dtype, mean=1.0, std=0.1)
+    x["beta"] = _normal((Hq, d), g, device, dtype, std=0.1)
+    x["alpha_out"] = _normal((Hq, d), g, device, dtype, mean=1.0, std=0.1)
+    x["beta_out"] = _normal((Hq, d), g, device, dtype, std=0.1)
+    return x
 
 
 def decode_inputs(batch, n_q_heads, n_kv_heads, head_dim, dtype, seed, steps,

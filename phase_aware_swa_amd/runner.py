@@ -86,6 +86,32 @@ class Decode:
                             self.workspace, stream)
 
 
+class Project:
+    """Buffers for orthros_project: q [B,T,Hq,d], q_out [B,T_out,Hq,d] and
+    (unless given) caches of capacity cap filled with the sentinel."""
+
+    def __init__(self, cfg, x, k_cache=None, v_cache=None, cap=None, scale_offset=True):
+        self.desc = desc_for(cfg)
+        B, T, dm = x["x"].shape
+        T_out = x["x_out"].shape[1]
+        Hq, Hkv, d = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+        dev = x["x"].device
+        self.x, self.T, self.d_model = x, T, dm
+        self.so = scale_offset
+        self.q = torch.empty(B, T, Hq, d, dtype=torch.bfloat16, device=dev)
+        self.q_out = torch.empty(B, T_out, Hq, d, dtype=torch.bfloat16, device=dev)
+        cap = cap or T
+        self.k_cache = k_cache if k_cache is not None else empty_cache(B, Hkv, cap, d, torch.bfloat16, dev)
+        self.v_cache = v_cache if v_cache is not None else empty_cache(B, Hkv, cap, d, torch.bfloat16, dev)
+
+    def run(self, stream=None):
+        x = self.x
+        so = (x["alpha"], x["beta"], x["alpha_out"], x["beta_out"]) if self.so else (None,) * 4
+        binding.project(self.desc, self.T, self.d_model, x["x"], x["x_out"] if x["x_out"].shape[1] else None,
+                        x["w_q"], x["w_k"], x["w_v"], *so, self.q, self.q_out if self.q_out.shape[1] else None,
+                        self.k_cache, self.v_cache, stream)
+
+
 class Copies:
     """Buffers for orthros_copies over caches filled by a prior SWA pass.
 

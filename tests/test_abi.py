@@ -28,9 +28,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_text():
-    assert binding.abi_version() == 2
+    assert binding.abi_version() == 3
     text = open(HEADER).read()
-    assert "#define ORTHROS_ABI_VERSION 2" in text
+    assert "#define ORTHROS_ABI_VERSION 3" in text
     for code, name in binding.STATUS.items():
         assert binding.status_str(code) == name
         assert re.search(rf"\b{name}\s*=\s*{code}\b", text) or code == 0
@@ -129,3 +129,45 @@ def test_copies_rejects_bad_arguments(kw, status):
 def test_copies_rejects_bad_desc():
     assert copies_call(mk(dtype=5)) == -3
     assert copies_call(mk(head_dim=96)) == -2
+
+
+def project_call(desc, T=100, T_out=2, d_model=256, cap=100, ptr=FAKE, x_out=FAKE, q_out=FAKE, alpha=FAKE,
+                 beta=FAKE, alpha_out=FAKE, beta_out=FAKE):
+    p = ctypes.c_void_p(ptr)
+    v = ctypes.c_void_p
+    return binding.lib().orthros_project(ctypes.byref(desc), T, T_out, d_model, p, v(x_out), p, p, p, v(alpha),
+                                         v(beta), v(alpha_out), v(beta_out), p, v(q_out), p, p, cap, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), -2),
+    (dict(T_out=-1), -2),
+    (dict(cap=50), -5),
+    (dict(d_model=0), -2),
+    (dict(d_model=100), -2),          # not a multiple of 32
+    (dict(d_model=65536 + 32), -2),
+    (dict(ptr=0), -1),
+    (dict(x_out=0), -1),              # T_out > 0 needs the copy rows
+    (dict(q_out=0), -1),
+    (dict(alpha=0), -1),              # alpha without beta
+    (dict(beta_out=0), -1),
+    (dict(ptr=FAKE + 8), -8),
+    (dict(alpha=FAKE + 4, beta=FAKE + 4), -8),
+])
+def test_project_rejects_bad_arguments(kw, status):
+    assert project_call(mk(), **kw) == status
+    assert binding.lib().orthros_last_error().decode()
+
+
+def test_project_rejects_bad_desc():
+    assert project_call(mk(dtype=0)) == -3              # fp32: the projection is bf16 only
+    assert project_call(mk(dtype=9)) == -3
+    assert project_call(mk(n_q_heads=2, n_kv_heads=1, head_dim=64)) == -2    # Hq * d = 128 but Hkv * d = 64
+
+
+def test_project_accepts_optional_pointers():
+    """T_out = 0 with NULL copy rows, and NULL scale-offsets, pass the pointer
+    checks: a later check (alignment) is the one that fails, so nothing is
+    ever launched on these fake pointers."""
+    assert project_call(mk(), T_out=0, x_out=0, q_out=0, alpha=FAKE + 4, beta=FAKE + 4) == -8
+    assert project_call(mk(), alpha=0, beta=0, alpha_out=FAKE + 4, beta_out=FAKE + 4) == -8
