@@ -17,17 +17,21 @@
 // straight into k_cache / v_cache at slot t of (sequence, KV head) -- the
 // K/V never make a separate trip through HBM.
 //
-// Kernel design (one workgroup = 4 waves = one 256-row x 128-column tile):
+// Kernel design (one workgroup = NW waves = one 256-row x 32*NW-column tile;
+// the workload shape runs NW = 8, 256 x 256 tiles, one workgroup per CU):
 //   - C^T = W X^T on v_mfma_f32_16x16x32_bf16: the A operand is 16 weight
 //     rows (output columns), the B operand 16 token rows, so each lane ends
 //     with 4 consecutive output columns of one token row (8-byte stores);
 //     wave (wr, wc) owns rows 128 wr .. +127 and columns 64 wc .. +63, i.e.
-//     8 x 4 MFMA tiles, 32 MFMAs per 32-deep step against 12 LDS reads;
-//   - the K dimension (d_model) streams in 32-deep stages through 3 LDS
-//     slots (24 KB each) filled by buffer loads that write LDS directly
-//     (no register staging), two stages ahead of the MFMAs, one barrier per
-//     stage; each slot is its own LDS array and the stage loop is unrolled
-//     by 3, so every slot is known at compile time;
+//     8 x 4 MFMA tiles, 32 MFMAs per 32-deep step against 12 LDS reads, two
+//     waves per SIMD;
+//   - the K dimension (d_model) streams in 32-deep stages through NS LDS
+//     slots filled by buffer loads that write LDS directly (no register
+//     staging), NS - 1 stages ahead of the MFMAs, one barrier per stage.  The
+//     stage time is bounded by the loads' latency over the prefetch depth,
+//     so the depth is what the 160 KB of LDS buys (4 slots of 32 KB for the
+//     256-column tile).  The stage loop is unrolled by NS, so every slot is
+//     known at compile time;
 //   - LDS layout of a slot part (rows x 4 chunks of 16 bytes): chunk c of row
 //     r sits at unit 4r + (c ^ ((r >> 2) & 3)).  An MFMA operand read (16 rows,
 //     one chunk) then touches 16 distinct 16-byte bank groups, and every read
@@ -47,13 +51,9 @@ namespace orthros {
 namespace {
 
 constexpr int kBM = 256;                 // token rows per tile
-constexpr int kBN = 128;                 // output columns per tile
 constexpr int kBK = 32;                  // reduction depth per stage
 constexpr int kXU = kBM * 4;             // 16-byte units of a slot's X part
-constexpr int kWU = kBN * 4;             // 16-byte units of a slot's W part
-constexpr int kSlotU = kXU + kWU;        // 1536 units = 24 KB
-constexpr int kXLoads = kXU / 256;       // direct loads per lane per stage (X part): 4
-constexpr int kWLoads = kWU / 256;       // (W part): 2
+constexpr int kGroupM = 1;               // row blocks per tile-order group
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -83,6 +83,18 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voffset, int sof
 
 __device__ __forceinline__ int unit_of(int r, int c) { return 4 * r + (c ^ ((r >> 2) & 3)); }
 
+// s_waitcnt vmcnt(L * n) for a wave-uniform n in [0, NMAX] (the count is an
+// immediate of the instruction, hence the unrolled selection).
+template <int L, int NMAX, int I = 0>
+__device__ __forceinline__ void wait_stages(int n)
+{
+    if (n == I) {
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (L * I));
+        return;
+    }
+    if constexpr (I < NMAX) wait_stages<L, NMAX, I + 1>(n);
+}
+
 // One tile's columns and where they go.
 struct TileKind {
     const uint16_t* w;        // first weight row of the tile ([out][in])
@@ -90,16 +102,24 @@ struct TileKind {
     int col0;                 // first column within its own matrix (q: Hq*d, k/v: Hkv*d)
 };
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void project_kernel(ProjParams p,
-                                                                                                 int64_t tiles_a)
+template <int NW, int NS>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void project_kernel(ProjParams p, int64_t tiles_a)
 {
-    __shared__ __align__(16) uint16_t slot0[kSlotU * 8];
-    __shared__ __align__(16) uint16_t slot1[kSlotU * 8];
-    __shared__ __align__(16) uint16_t slot2[kSlotU * 8];
+    constexpr int NT = 64 * NW;              // threads
+    constexpr int kBN = 32 * NW;             // output columns per tile (64 per wave column)
+    constexpr int kWU = kBN * 4;             // 16-byte units of a slot's W part
+    constexpr int kSlotU = kXU + kWU;
+    constexpr int kXL = kXU / NT;            // direct loads per lane per stage (X part)
+    constexpr int kWL = kWU / NT;            // (W part)
+    constexpr int kL = kXL + kWL;
+    constexpr int NC = 4;                    // MFMA column tiles per wave
+    static_assert(kXU % NT == 0 && kWU % NT == 0 && NS >= 2 && (NS - 2) * kL <= 63, "tile shape");
+    __shared__ __align__(16) uint16_t slots[NS][kSlotU * 8];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wr = wv >> 1, wc = wv & 1;
+    const int wr = wv & 1, wc = wv >> 1;
     const int n = lane & 15, gq = lane >> 4;
     const int Nq = p.Hq * p.D, Nk = p.Hkv * p.D;
     const int64_t K = p.K;
@@ -110,9 +130,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool region_b = id >= tiles_a;
     const int ntiles_n = region_b ? Nq / kBN : (Nq + 2 * Nk) / kBN;
     const int64_t local = region_b ? id - tiles_a : id;
-    const int64_t row0 = (local / ntiles_n) * kBM;
-    const int colt = (int)(local % ntiles_n) * kBN;          // first column of the stacked [W_Q; W_K; W_V]
+    // tile order: groups of group_m row blocks; inside a group the column
+    // tile is the outer index, so the group's concurrent workgroups share
+    // each weight slice (and each row slice) through L2
     const int64_t M = region_b ? p.Mo : p.Mx;
+    const int64_t mblocks = (M + kBM - 1) / kBM;
+    const int64_t gsize = (int64_t)p.group_m * ntiles_n;
+    const int64_t grp = local / gsize, w_in = local - grp * gsize;
+    const int64_t gm = mblocks - grp * p.group_m < p.group_m ? mblocks - grp * p.group_m : p.group_m;
+    const int64_t row0 = (grp * p.group_m + w_in % gm) * kBM;
+    const int colt = (int)(w_in / gm) * kBN;                 // first column of the stacked [W_Q; W_K; W_V]
     const uint16_t* xrows = region_b ? p.xo : p.x;
     TileKind tk;
     if (colt < Nq) {
@@ -123,57 +150,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         tk = {p.wv + (int64_t)(colt - Nq - Nk) * K, 2, colt - Nq - Nk};
     }
 
-    // ---- direct-load addressing: lane l of load j writes unit 256 j + 64 wave + l of the part
+    // ---- direct-load addressing: lane l of load j writes unit NT j + 64 wave + l of the part
     const i32x4 rx = buffer_words(xrows + row0 * K, (M - row0) * K * 2);
     const i32x4 rw = buffer_words(tk.w, (int64_t)kBN * K * 2);
-    uint32_t xoff[kXLoads], woff[kWLoads];
+    uint32_t xoff[kXL], woff[kWL];
 #pragma unroll
-    for (int j = 0; j < kXLoads; ++j) {
-        const int u = 256 * j + 64 * wv + lane, r = u >> 2, c = (u & 3) ^ ((r >> 2) & 3);
+    for (int j = 0; j < kXL; ++j) {
+        const int u = NT * j + 64 * wv + lane, r = u >> 2, c = (u & 3) ^ ((r >> 2) & 3);
         xoff[j] = (uint32_t)(r * K * 2 + 16 * c);
     }
 #pragma unroll
-    for (int j = 0; j < kWLoads; ++j) {
-        const int u = 256 * j + 64 * wv + lane, r = u >> 2, c = (u & 3) ^ ((r >> 2) & 3);
+    for (int j = 0; j < kWL; ++j) {
+        const int u = NT * j + 64 * wv + lane, r = u >> 2, c = (u & 3) ^ ((r >> 2) & 3);
         woff[j] = (uint32_t)(r * K * 2 + 16 * c);
     }
     auto issue = [&](uint16_t* slot, int64_t t) {
         const int kb = (int)(t * kBK * 2);                   // byte offset of the stage along a row
 #pragma unroll
-        for (int j = 0; j < kXLoads; ++j) load_lds16(rx, xoff[j], kb, slot + (256 * j + 64 * wv) * 8);
+        for (int j = 0; j < kXL; ++j) load_lds16(rx, xoff[j], kb, slot + (NT * j + 64 * wv) * 8);
 #pragma unroll
-        for (int j = 0; j < kWLoads; ++j) load_lds16(rw, woff[j], kb, slot + (kXU + 256 * j + 64 * wv) * 8);
+        for (int j = 0; j < kWL; ++j) load_lds16(rw, woff[j], kb, slot + (kXU + NT * j + 64 * wv) * 8);
     };
 
     // ---- operand reads: token rows 128 wr + 16 ri + n, weight rows 64 wc + 16 ci + n, chunk gq
     const int xb = unit_of(128 * wr + n, gq) * 8;            // elements
     const int wb = (kXU + unit_of(64 * wc + n, gq)) * 8;
-    f32x4 acc[8][4];
+    f32x4 acc[8][NC];
 #pragma unroll
     for (int ri = 0; ri < 8; ++ri)
 #pragma unroll
-        for (int ci = 0; ci < 4; ++ci) acc[ri][ci] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ci = 0; ci < NC; ++ci) acc[ri][ci] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](const uint16_t* slot) {
-        bf16x8 wf[4];
+        bf16x8 wf[NC];
 #pragma unroll
-        for (int ci = 0; ci < 4; ++ci) wf[ci] = *(const bf16x8*)(slot + wb + ci * 64 * 8);
+        for (int ci = 0; ci < NC; ++ci) wf[ci] = *(const bf16x8*)(slot + wb + ci * 64 * 8);
 #pragma unroll
         for (int ri = 0; ri < 8; ++ri) {
             const bf16x8 xf = *(const bf16x8*)(slot + xb + ri * 64 * 8);
 #pragma unroll
-            for (int ci = 0; ci < 4; ++ci)
+            for (int ci = 0; ci < NC; ++ci)
                 acc[ri][ci] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[ci], xf, acc[ri][ci], 0, 0, 0);
         }
     };
-    // stage t computes from slot t % 3 and refills slot (t + 2) % 3 (read at t - 1)
+    // stage t computes from slot t % NS and refills slot (t + NS - 1) % NS (read at t - 1)
     const int64_t nk = K / kBK;
     auto step = [&](uint16_t* cur, uint16_t* refill, int64_t t) {
         if (t >= nk) return;
-        // this lane's loads of stage t are done when at most stage t + 1's remain
-        if (t + 1 < nk)
-            __builtin_amdgcn_s_waitcnt(0x0F70 | (kXLoads + kWLoads));   // vmcnt(6)
-        else
-            __builtin_amdgcn_s_waitcnt(0x0F70);                          // vmcnt(0)
+        // this lane's loads of stage t are done when at most the stages after
+        // it that were issued (up to NS - 2 of them) remain
+        const int64_t after = nk - 1 - t < NS - 2 ? nk - 1 - t : NS - 2;
+        wait_stages<kL, NS - 2>((int)after);
         // A bare barrier: every wave has waited for its own loads of stage t
         // above, and each wave's reads of the slot refilled next were consumed
         // by its MFMAs before it got here.  (__syncthreads' release fence
@@ -181,15 +207,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (t + 2 < nk) issue(refill, t + 2);
+        if (t + NS - 1 < nk) issue(refill, t + NS - 1);
         compute(cur);
     };
-    issue(slot0, 0);
-    if (nk > 1) issue(slot1, 1);
-    for (int64_t t = 0; t < nk; t += 3) {
-        step(slot0, slot2, t);
-        step(slot1, slot0, t + 1);
-        step(slot2, slot1, t + 2);
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < nk) issue(slots[s], s);
+    for (int64_t t = 0; t < nk; t += NS) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) step(slots[s], slots[(s + NS - 1) % NS], t + s);
     }
 
     // ---- epilogue: lane (n, gq) holds columns 4 gq .. + 3 of row n of each 16 x 16 tile
@@ -198,7 +224,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int64_t row = row0 + 128 * wr + 16 * ri + n;
         if (row >= M) continue;
 #pragma unroll
-        for (int ci = 0; ci < 4; ++ci) {
+        for (int ci = 0; ci < NC; ++ci) {
             const int col = tk.col0 + 64 * wc + 16 * ci + 4 * gq;   // within its own matrix
             float v[4] = {acc[ri][ci][0], acc[ri][ci][1], acc[ri][ci][2], acc[ri][ci][3]};
             uint16_t* dst;
@@ -225,21 +251,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 }  // namespace
 
+template <int NW, int NS>
+hipError_t launch_project_t(const ProjParams& p, hipStream_t s)
+{
+    constexpr int BN = 32 * NW;
+    const int Nq = p.Hq * p.D, Nk = p.Hkv * p.D;
+    const int64_t tiles_a = (p.Mx + kBM - 1) / kBM * ((Nq + 2 * Nk) / BN);
+    ProjParams q = p;
+    q.tiles_b = (p.Mo + kBM - 1) / kBM * (Nq / BN);
+    q.group_m = kGroupM;
+    const int64_t total = tiles_a + q.tiles_b;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL((project_kernel<NW, NS>), dim3((unsigned)total), dim3(64 * NW), 0, s, q, tiles_a);
+    return hipGetLastError();
+}
+
 bool project_applies(const ProjParams& p)
 {
-    return p.D > 0 && (p.Hq * p.D) % kBN == 0 && (p.Hkv * p.D) % kBN == 0 && p.K >= kBK && p.K % kBK == 0;
+    return p.D > 0 && (p.Hq * p.D) % 128 == 0 && (p.Hkv * p.D) % 128 == 0 && p.K >= kBK && p.K % kBK == 0;
 }
 
 hipError_t launch_project(const ProjParams& p, hipStream_t s)
 {
-    const int Nq = p.Hq * p.D, Nk = p.Hkv * p.D;
-    const int64_t tiles_a = (p.Mx + kBM - 1) / kBM * ((Nq + 2 * Nk) / kBN);
-    ProjParams q = p;
-    q.tiles_b = (p.Mo + kBM - 1) / kBM * (Nq / kBN);
-    const int64_t total = tiles_a + q.tiles_b;
-    if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL(project_kernel, dim3((unsigned)total), dim3(256), 0, s, q, tiles_a);
-    return hipGetLastError();
+    // 256-column tiles (8 waves, one workgroup per CU, 4 slots) when no tile
+    // would straddle the query / key / value columns; else 128-column tiles
+    // (4 waves, two workgroups per CU, 3 slots)
+    if ((p.Hq * p.D) % 256 == 0 && (p.Hkv * p.D) % 256 == 0) return launch_project_t<8, 4>(p, s);
+    return launch_project_t<4, 3>(p, s);
 }
 
 }  // namespace orthros
