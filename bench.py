@@ -17,7 +17,12 @@ orthros_swa_prefill and orthros_global_xattn are timed too, as a
 breakdown.  The fp64 CPU oracle is timed on a bounded sample of the same
 workload on this machine's host cores (cpu_baseline).
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill|swa|xattn|copies|decode|copy]
+The projections either side of the attention (orthros_project: the shared
+W_Q over the base and copy rows, K/V written into the cache; d_model 4096)
+are timed over the same 128K batch as an MFMA-bound breakdown leg.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W]
+                  [--only prefill|swa|xattn|copies|project|decode|copy]
 """
 import argparse
 import hashlib
@@ -52,6 +57,13 @@ def prefill_bytes(B, T, Hq, Hkv, d, es=2):
     (which also serves the copy's key reads: one pass over K/V), plus the
     copy's query read and its output written."""
     return swa_bytes(B, T, Hq, Hkv, d, es) + 2 * B * Hq * d * es
+
+
+def project_flops(c):
+    """Algorithmic flops of orthros_project: 2 d_model per output element;
+    base rows against W_Q, W_K and W_V, copy rows against W_Q."""
+    nq, nk = c["n_q_heads"] * c["head_dim"], c["n_kv_heads"] * c["head_dim"]
+    return 2 * c["d_model"] * c["batch"] * (c["T"] * (nq + 2 * nk) + c["T_out"] * nq)
 
 
 def xattn_bytes(B, pos_plus_1, Hkv, d, es=2):
@@ -145,7 +157,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all",
-                    choices=["all", "prefill", "swa", "xattn", "copies", "decode", "copy"])
+                    choices=["all", "prefill", "swa", "xattn", "copies", "project", "decode", "copy"])
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -157,7 +169,7 @@ def main():
     import torch
 
     from phase_aware_swa_amd import inputs
-    from phase_aware_swa_amd.runner import Copies, Decode, Prefill
+    from phase_aware_swa_amd.runner import Copies, Decode, Prefill, Project
 
     torch.cuda.set_device(0)
     out = {}
@@ -235,6 +247,23 @@ def main():
             out[name]["roofline"] = result_copies
             del pre, cp, xc, q_out, pos
             torch.cuda.empty_cache()
+
+    if args.only in ("all", "project"):
+        # the projections either side of the attention over the 128K batch: MFMA-bound
+        pcfg = dict(inputs.WORKLOADS["gqa_8b_project_128k"])
+        xp = inputs.project_inputs(seed=9, device="cuda", **pcfg)
+        pr = Project(pcfg, xp, cap=pcfg["T"])
+        n_p = max(3, args.steps // 4)
+        sec, _ = timed(pr.run, n_p, args.warmup)
+        t = sec / n_p
+        fl = project_flops(pcfg)
+        out["project"] = {"kernel": "orthros_project (project_kernel<8, 4>)", "workload": "gqa_8b_project_128k",
+                          "us": t * 1e6, "flops": fl, "TFLOPs": fl / t / 1e12,
+                          "roofline": {"bound": "mfma", "achieved": fl / t / 1e12, "peak": BF16_PEAK_TFLOPS,
+                                       "unit": "TFLOP/s", "frac": fl / t / 1e12 / BF16_PEAK_TFLOPS,
+                                       "traffic": None, "kernel": "orthros_project at gqa_8b_project_128k"}}
+        del pr, xp
+        torch.cuda.empty_cache()
 
     if args.only in ("all", "decode"):
         dcfg = dict(inputs.WORKLOADS["gqa_8b_decode_b16"])

@@ -134,7 +134,6 @@ struct ProjParams {
     uint16_t* v_cache;
     int64_t Mx, Mo, T, cap, K;
     int64_t tiles_b;            // set by the launcher
-    int32_t group_m;            // row blocks per tile-order group (set by the launcher)
     int32_t Hq, Hkv, D;
 };
 // Shapes the tiled kernel takes: Hq*D and Hkv*D multiples of 128, K a

@@ -53,7 +53,6 @@ namespace {
 constexpr int kBM = 256;                 // token rows per tile
 constexpr int kBK = 32;                  // reduction depth per stage
 constexpr int kXU = kBM * 4;             // 16-byte units of a slot's X part
-constexpr int kGroupM = 1;               // row blocks per tile-order group
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -112,8 +111,8 @@ void project_kernel(ProjParams p, int64_t tiles_a)
     constexpr int kSlotU = kXU + kWU;
     constexpr int kXL = kXU / NT;            // direct loads per lane per stage (X part)
     constexpr int kWL = kWU / NT;            // (W part)
-    constexpr int kL = kXL + kWL;
     constexpr int NC = 4;                    // MFMA column tiles per wave
+    constexpr int kL = kXL + kWL;            // loads per lane per stage
     static_assert(kXU % NT == 0 && kWU % NT == 0 && NS >= 2 && (NS - 2) * kL <= 63, "tile shape");
     __shared__ __align__(16) uint16_t slots[NS][kSlotU * 8];
 
@@ -130,16 +129,9 @@ void project_kernel(ProjParams p, int64_t tiles_a)
     const bool region_b = id >= tiles_a;
     const int ntiles_n = region_b ? Nq / kBN : (Nq + 2 * Nk) / kBN;
     const int64_t local = region_b ? id - tiles_a : id;
-    // tile order: groups of group_m row blocks; inside a group the column
-    // tile is the outer index, so the group's concurrent workgroups share
-    // each weight slice (and each row slice) through L2
+    const int64_t row0 = (local / ntiles_n) * kBM;
+    const int colt = (int)(local % ntiles_n) * kBN;          // first column of the stacked [W_Q; W_K; W_V]
     const int64_t M = region_b ? p.Mo : p.Mx;
-    const int64_t mblocks = (M + kBM - 1) / kBM;
-    const int64_t gsize = (int64_t)p.group_m * ntiles_n;
-    const int64_t grp = local / gsize, w_in = local - grp * gsize;
-    const int64_t gm = mblocks - grp * p.group_m < p.group_m ? mblocks - grp * p.group_m : p.group_m;
-    const int64_t row0 = (grp * p.group_m + w_in % gm) * kBM;
-    const int colt = (int)(w_in / gm) * kBN;                 // first column of the stacked [W_Q; W_K; W_V]
     const uint16_t* xrows = region_b ? p.xo : p.x;
     TileKind tk;
     if (colt < Nq) {
@@ -259,7 +251,6 @@ hipError_t launch_project_t(const ProjParams& p, hipStream_t s)
     const int64_t tiles_a = (p.Mx + kBM - 1) / kBM * ((Nq + 2 * Nk) / BN);
     ProjParams q = p;
     q.tiles_b = (p.Mo + kBM - 1) / kBM * (Nq / BN);
-    q.group_m = kGroupM;
     const int64_t total = tiles_a + q.tiles_b;
     if (total == 0) return hipSuccess;
     hipLaunchKernelGGL((project_kernel<NW, NS>), dim3((unsigned)total), dim3(64 * NW), 0, s, q, tiles_a);
