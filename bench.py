@@ -22,7 +22,11 @@ W_Q over the base and copy rows, K/V written into the cache; d_model 4096)
 are timed over the same 128K batch as an MFMA-bound breakdown leg.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
-                  [--only prefill|swa|xattn|copies|project|decode|copy]
+                  [--only prefill|swa|xattn|copies|project|decode|layers|copy]
+
+The multi-layer decode leg (layers) runs one decode step over a stack of 36
+resident layers (batch 4, lengths U[8192, 32768]; and batch 1, lengths
+U[1024, 4096], where launches matter), eager and as one captured HIP graph.
 """
 import argparse
 import hashlib
@@ -157,7 +161,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all",
-                    choices=["all", "prefill", "swa", "xattn", "copies", "project", "decode", "copy"])
+                    choices=["all", "prefill", "swa", "xattn", "copies", "project", "decode", "layers", "copy"])
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -169,7 +173,7 @@ def main():
     import torch
 
     from phase_aware_swa_amd import inputs
-    from phase_aware_swa_amd.runner import Copies, Decode, Prefill, Project
+    from phase_aware_swa_amd.runner import Copies, Decode, LayerStack, Prefill, Project
 
     torch.cuda.set_device(0)
     out = {}
@@ -263,6 +267,48 @@ def main():
                                        "unit": "TFLOP/s", "frac": fl / t / 1e12 / BF16_PEAK_TFLOPS,
                                        "traffic": None, "kernel": "orthros_project at gqa_8b_project_128k"}}
         del pr, xp
+        torch.cuda.empty_cache()
+
+    for lname in ("gqa_8b_decode_36l_b4", "gqa_8b_decode_36l_b1_short"):
+        if args.only not in ("all", "layers"):
+            break
+        # one decode step over 36 resident layers: eager launches vs one HIP graph
+        lcfg = dict(inputs.WORKLOADS[lname])
+        nl, ns = lcfg["layers"], lcfg["steps"]
+        layers = [inputs.decode_inputs(seed=100 + l, device="cuda", **lcfg) for l in range(nl)]
+        len0 = [x["cache_len"].clone() for x in layers]
+        stack = LayerStack(lcfg, layers, ns)
+        stack.set_inputs(0)
+        graph = stack.capture()
+
+        def reset():
+            for x, l0 in zip(layers, len0):
+                x["cache_len"].copy_(l0)
+
+        def eager_pass():
+            for _ in range(ns):
+                stack.step()
+
+        def graph_pass():
+            for _ in range(ns):
+                graph.replay()
+
+        res = {}
+        for name, fn in (("eager", eager_pass), ("graph", graph_pass)):
+            reset()
+            fn()                                   # warm-up pass
+            reset()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            res[name] = (time.perf_counter() - t0) / ns * 1e6
+        lens = torch.stack([l0.double() for l0 in len0])
+        step_bytes = float(((lens + ns / 2).sum() * lcfg["n_kv_heads"] * lcfg["head_dim"] * 2 * 2).item())
+        out["decode_layers_" + lname] = {"workload": lname, "layers": nl, "steps": ns,
+                                "eager_us_per_step": res["eager"], "graph_us_per_step": res["graph"],
+                                "bytes_per_step": step_bytes, "GBps_graph": step_bytes / (res["graph"] * 1e-6) / 1e9}
+        del stack, graph, layers
         torch.cuda.empty_cache()
 
     if args.only in ("all", "decode"):

@@ -39,6 +39,13 @@ WORKLOADS = {
                            head_dim=128, T=32768, T_out=4096, window=128),
     "gqa_8b_pt_16k": dict(kind="copies", dtype=torch.bfloat16, batch=1, n_q_heads=32, n_kv_heads=8,
                           head_dim=128, T=16384, T_out=16384, window=128),
+    # decode over a stack of 36 resident layers with short histories, where
+    # the per-layer step is short enough for launch overhead to matter
+    "gqa_8b_decode_36l_b4": dict(kind="decode_layers", dtype=torch.bfloat16, batch=4, n_q_heads=32, n_kv_heads=8,
+                                 head_dim=128, window=128, len_lo=8192, len_hi=32768, steps=64, layers=36),
+    "gqa_8b_decode_36l_b1_short": dict(kind="decode_layers", dtype=torch.bfloat16, batch=1, n_q_heads=32,
+                                       n_kv_heads=8, head_dim=128, window=128, len_lo=1024, len_hi=4096, steps=64,
+                                       layers=36),
     # the projections either side of the 8B-class layer's attention (d_model
     # 4096) over the 128K prefill: X of both sequences, one copy row each
     "gqa_8b_project_128k": dict(kind="project", dtype=torch.bfloat16, batch=2, n_q_heads=32, n_kv_heads=8,

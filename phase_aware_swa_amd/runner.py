@@ -86,6 +86,46 @@ class Decode:
                             self.workspace, stream)
 
 
+class LayerStack:
+    """Decode state of a stack of resident layers (one model's layers, each
+    with its own cache, lengths, workspace and step inputs) for the
+    multi-layer decode step.
+
+    layers: list of inputs.decode_inputs dicts already on the device (the
+    step inputs of layer l at step s are x["q"][s] etc.); steps: how many
+    steps the stack will run (bounds each layer's lengths).  set_inputs(s)
+    copies step s's inputs into fixed per-layer buffers; step() runs every
+    layer's orthros_decode_step in order on the current stream, reading those
+    buffers; capture() records one step() into a HIP graph, whose replay()
+    then runs the whole multi-layer step as one graph launch (every launch's
+    arguments are fixed; the step inputs change through the buffers, the
+    lengths through the device arrays the step itself advances).
+    """
+
+    def __init__(self, cfg, layers, steps):
+        self.xs = layers
+        # each layer's own bound of its lengths over `steps` steps (its cache capacity)
+        self.decs = [Decode(cfg, x["k_cache"], x["v_cache"], x["cache_len"],
+                            int(x["cache_len"].max().item()) + steps - 1, x["alpha"], x["beta"], x["alpha_out"],
+                            x["beta_out"]) for x in layers]
+        self.buf = [{k: torch.empty_like(x[k][0]) for k in ("q", "q_out", "k_new", "v_new")} for x in layers]
+
+    def set_inputs(self, s):
+        for x, b in zip(self.xs, self.buf):
+            for k, t in b.items():
+                t.copy_(x[k][s])
+
+    def step(self):
+        for dec, b in zip(self.decs, self.buf):
+            dec.step(b["q"], b["q_out"], b["k_new"], b["v_new"])
+
+    def capture(self):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step()
+        return g
+
+
 class Project:
     """Buffers for orthros_project: q [B,T,Hq,d], q_out [B,T_out,Hq,d] and
     (unless given) caches of capacity cap filled with the sentinel."""
