@@ -99,7 +99,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int64_t q_seq = (int64_t)b * T_out * a.Hq * D + (int64_t)h0 * D;
     const int64_t c_seq = ((int64_t)b * a.Hkv + g) * a.cap * D;
 
-    // the copies' queries q' * alpha' + beta' as MFMA B operands:
+    // the copies' queries (q' * alpha' + beta') * qscale as MFMA B operands
+    // (the score scale, log2(e) included, is folded in here, once per
+    // workgroup, so that S comes out of the MFMAs in exp2 units):
     // lane (n, gq) holds copy c0 + n, head dims 32 i + 8 gq .. + 7
     bf16x8 qf[2][NQ];
     {
@@ -119,8 +121,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const uint32_t w = qw[e], aw = av[e], bw = bv[e];
-                    r[e] = pack_bf16x2(__builtin_fmaf(bf16_lo(w), bf16_lo(aw), bf16_lo(bw)),
-                                       __builtin_fmaf(bf16_hi(w), bf16_hi(aw), bf16_hi(bw)));
+                    r[e] = pack_bf16x2(__builtin_fmaf(bf16_lo(w), bf16_lo(aw), bf16_lo(bw)) * qs,
+                                       __builtin_fmaf(bf16_hi(w), bf16_hi(aw), bf16_hi(bw)) * qs);
                 }
                 qf[hd][i] = __builtin_bit_cast(bf16x8, r);
             }
@@ -163,8 +165,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f32x4 oacc[2][ND];
     f32x4 lacc[2];
     float m_run[2];
+    f32x4 negm[2];      // -m_run of the lane's copy, the first S MFMA's accumulator after pair 0
     // one pair against both heads; FIRST: pair 0, which starts the running
-    // maxima and the accumulators
+    // maxima and the accumulators.  After it, S comes out of the MFMAs
+    // already shifted by the running maximum (exp2 units), so the
+    // probabilities are plain exp2 of the scores.
     auto attend = [&](auto first_tag, int64_t pr) {
         constexpr bool FIRST = decltype(first_tag)::value;
         // one K base per pair (opaque, so that the steps stay immediate offsets)
@@ -179,8 +184,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const bf16x8 k1 = *(const bf16x8*)(kb + i * R::K_STEP + R::K_KEY16);
 #pragma unroll
             for (int hd = 0; hd < 2; ++hd) {
-                s[hd][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[hd][i], i ? s[hd][0] : zero, 0, 0, 0);
-                s[hd][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[hd][i], i ? s[hd][1] : zero, 0, 0, 0);
+                const f32x4 c = FIRST ? zero : negm[hd];
+                s[hd][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[hd][i], i ? s[hd][0] : c, 0, 0, 0);
+                s[hd][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[hd][i], i ? s[hd][1] : c, 0, 0, 0);
             }
         }
         // s[.][0][r]: key 32 pr + 4 gq + r, s[.][1][r]: key 32 pr + 16 + 4 gq + r; copy c0 + n
@@ -199,19 +205,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         bf16x8 pb[2];
 #pragma unroll
         for (int hd = 0; hd < 2; ++hd) {
-            const f32x4 s0 = s[hd][0], s1 = s[hd][1];
-            float lmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                               fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-            lmax *= qs;
+            f32x4 s0 = s[hd][0], s1 = s[hd][1];
+            const float lmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                                     fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
             if constexpr (FIRST) {
+                // scores in exp2 units; their row maximum starts the running maximum
                 float rmax = fmaxf(lmax, __shfl_xor(lmax, 16));
                 m_run[hd] = fmaxf(rmax, __shfl_xor(rmax, 32));
-            } else if (__any(lmax > m_run[hd] + kMargin)) {
+                s0 -= m_run[hd];
+                s1 -= m_run[hd];
+                negm[hd] = f32x4{-m_run[hd], -m_run[hd], -m_run[hd], -m_run[hd]};
+            } else if (__any(lmax > kMargin)) {
+                // scores already relative to m_run: raise it by the row's excess
                 float rmax = fmaxf(lmax, __shfl_xor(lmax, 16));
                 rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
-                const float m_new = fmaxf(m_run[hd], rmax);
-                const float corr = fast_exp2(m_run[hd] - m_new);
-                m_run[hd] = m_new;
+                const float up = fmaxf(rmax, 0.f);
+                const float corr = fast_exp2(-up);
+                m_run[hd] += up;
+                negm[hd] = f32x4{-m_run[hd], -m_run[hd], -m_run[hd], -m_run[hd]};
+                s0 -= up;
+                s1 -= up;
                 lacc[hd] *= corr;
 #pragma unroll
                 for (int i = 0; i < ND; ++i) oacc[hd][i] *= corr;
@@ -219,8 +232,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             float p[8];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                p[r] = fast_exp2(__builtin_fmaf(s0[r], qs, -m_run[hd]));
-                p[4 + r] = fast_exp2(__builtin_fmaf(s1[r], qs, -m_run[hd]));
+                p[r] = fast_exp2(s0[r]);
+                p[4 + r] = fast_exp2(s1[r]);
             }
             const u32x4 pw4 = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                                pack_bf16x2(p[6], p[7])};
