@@ -163,6 +163,8 @@ def main():
     ap.add_argument("--only", default="all",
                     choices=["all", "prefill", "swa", "xattn", "copies", "project", "decode", "layers", "copy"])
     ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--skip", nargs="*", default=[], choices=["copies", "project", "layers"],
+                    help="legs to leave out of a full run (e.g. to keep a profiled run's trace small)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -227,7 +229,7 @@ def main():
         del run, x
         torch.cuda.empty_cache()
 
-    if args.only in ("all", "copies"):
+    if args.only in ("all", "copies") and "copies" not in args.skip:
         # output copies at many positions (SFT answer span, PT every position): MFMA-bound
         for name in ("gqa_8b_sft_32k", "gqa_8b_pt_16k"):
             ccfg = dict(inputs.WORKLOADS[name])
@@ -252,7 +254,7 @@ def main():
             del pre, cp, xc, q_out, pos
             torch.cuda.empty_cache()
 
-    if args.only in ("all", "project"):
+    if args.only in ("all", "project") and "project" not in args.skip:
         # the projections either side of the attention over the 128K batch: MFMA-bound
         pcfg = dict(inputs.WORKLOADS["gqa_8b_project_128k"])
         xp = inputs.project_inputs(seed=9, device="cuda", **pcfg)
@@ -270,7 +272,7 @@ def main():
         torch.cuda.empty_cache()
 
     for lname in ("gqa_8b_decode_36l_b4", "gqa_8b_decode_36l_b1_short"):
-        if args.only not in ("all", "layers"):
+        if args.only not in ("all", "layers") or "layers" in args.skip:
             break
         # one decode step over 36 resident layers: eager launches vs one HIP graph
         lcfg = dict(inputs.WORKLOADS[lname])
