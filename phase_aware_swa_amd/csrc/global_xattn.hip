@@ -415,18 +415,33 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* ws_part, const 
         if (lane == 0) wmax[wv] = mx;
         __syncthreads();
         const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-        // this thread's split group: weighted sums of 4 head-dim values and of l
+        // this thread's split group: weighted sums of 4 head-dim values and of
+        // l, eight splits per round with every load of the round issued first
+        // (one L2 round trip per round, not per split); a round's splits past
+        // s1 read split s1 again with weight 0
         float n0 = 0.f, n1 = 0.f, n2 = 0.f, n3 = 0.f, den = 0.f;
-        for (int s = s0 + gp; s <= s1; s += NG) {
-            const float* ps = pk + (int64_t)s * (D + 2);
-            const float f = fast_exp2(ps[0] - M);
-            const float2 a = *(const float2*)(ps + 2 + 4 * d4);
-            const float2 c = *(const float2*)(ps + 4 + 4 * d4);
-            den += f * ps[1];
-            n0 += f * a.x;
-            n1 += f * a.y;
-            n2 += f * c.x;
-            n3 += f * c.y;
+        constexpr int RB = 8;
+        for (int s = s0 + gp; s <= s1; s += NG * RB) {
+            float ml[RB][2];
+            float2 a[RB], c[RB];
+#pragma unroll
+            for (int k = 0; k < RB; ++k) {
+                const int sk = s + NG * k <= s1 ? s + NG * k : s1;
+                const float* ps = pk + (int64_t)sk * (D + 2);
+                ml[k][0] = ps[0];
+                ml[k][1] = ps[1];
+                a[k] = *(const float2*)(ps + 2 + 4 * d4);
+                c[k] = *(const float2*)(ps + 4 + 4 * d4);
+            }
+#pragma unroll
+            for (int k = 0; k < RB; ++k) {
+                const float f = s + NG * k <= s1 ? fast_exp2(ml[k][0] - M) : 0.f;
+                den += f * ml[k][1];
+                n0 += f * a[k].x;
+                n1 += f * a[k].y;
+                n2 += f * c[k].x;
+                n3 += f * c[k].y;
+            }
         }
         red[gp][4 * d4] = n0;
         red[gp][4 * d4 + 1] = n1;
