@@ -53,6 +53,8 @@ namespace {
 constexpr int kBM = 256;                 // token rows per tile
 constexpr int kBK = 32;                  // reduction depth per stage
 constexpr int kXU = kBM * 4;             // 16-byte units of a slot's X part
+constexpr int kWideNS = 4;               // LDS slots of the 256-column form
+constexpr bool kWideFB = true;           // its operand fragments double-buffered in registers
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -101,7 +103,7 @@ struct TileKind {
     int col0;                 // first column within its own matrix (q: Hq*d, k/v: Hkv*d)
 };
 
-template <int NW, int NS>
+template <int NW, int NS, bool FB>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void project_kernel(ProjParams p, int64_t tiles_a)
 {
@@ -205,9 +207,61 @@ void project_kernel(ProjParams p, int64_t tiles_a)
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
         if (s < nk) issue(slots[s], s);
-    for (int64_t t = 0; t < nk; t += NS) {
+    if constexpr (!FB) {
+        for (int64_t t = 0; t < nk; t += NS) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) step(slots[s], slots[(s + NS - 1) % NS], t + s);
+            for (int s = 0; s < NS; ++s) step(slots[s], slots[(s + NS - 1) % NS], t + s);
+        }
+    } else {
+        // FB: the fragments a stage needs first (its 4 weight fragments and its
+        // first 2 row fragments) double-buffered in registers.  Step t waits
+        // for stage t + 1 and reads that prefix (set (t + 1) % 2) while the
+        // MFMAs of stage t run on set t % 2 and on its other row fragments,
+        // read during those MFMAs; so no stage starts with the LDS read
+        // latency.  The slot refilled at step t held stage t - 1, whose
+        // fragments every wave read before it left step t - 1.  The launcher
+        // takes this form only when nk is a multiple of NS, so the loop has no
+        // partial group and the reads no branch around them (at a branch the
+        // compiler would wait for every outstanding LDS read); the last step
+        // reads a stale slot it never uses.
+        static_assert(NS % 2 == 0 && NS >= 3, "fragment sets alternate with the slots");
+        constexpr int XPRE = 2;
+        bf16x8 wfb[2][NC], xfb[2][XPRE];
+        auto read_frags = [&](int fs, const uint16_t* slot) {
+#pragma unroll
+            for (int ci = 0; ci < NC; ++ci) wfb[fs][ci] = *(const bf16x8*)(slot + wb + ci * 64 * 8);
+#pragma unroll
+            for (int ri = 0; ri < XPRE; ++ri) xfb[fs][ri] = *(const bf16x8*)(slot + xb + ri * 64 * 8);
+        };
+        auto sync_stage = [&](int64_t u) {      // stage u (if any) landed in every wave's view
+            const int64_t after = nk - 1 - u < NS - 2 ? nk - 1 - u : NS - 2;
+            wait_stages<kL, NS - 2>((int)after);  // nothing to wait for when u = nk
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        auto step_fb = [&](int fs, const uint16_t* cur, const uint16_t* next, uint16_t* refill, int64_t t) {
+            sync_stage(t + 1);
+            if (t + NS - 1 < nk) issue(refill, t + NS - 1);
+            read_frags(fs ^ 1, next);
+            // keep this stage's MFMAs after the next stage's reads are issued
+            // (the scheduler would otherwise hoist them and serialise the two)
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ri = 0; ri < 8; ++ri) {
+                const bf16x8 xf = ri < XPRE ? xfb[fs][ri < XPRE ? ri : 0] : *(const bf16x8*)(cur + xb + ri * 64 * 8);
+#pragma unroll
+                for (int ci = 0; ci < NC; ++ci)
+                    acc[ri][ci] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfb[fs][ci], xf, acc[ri][ci], 0, 0, 0);
+            }
+        };
+        sync_stage(0);
+        read_frags(0, slots[0]);
+        for (int64_t t = 0; t < nk; t += NS) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                step_fb(s & 1, slots[s], slots[(s + 1) % NS], slots[(s + NS - 1) % NS], t + s);
+        }
     }
 
     // ---- epilogue: lane (n, gq) holds columns 4 gq .. + 3 of row n of each 16 x 16 tile
@@ -243,7 +297,7 @@ void project_kernel(ProjParams p, int64_t tiles_a)
 
 }  // namespace
 
-template <int NW, int NS>
+template <int NW, int NS, bool FB>
 hipError_t launch_project_t(const ProjParams& p, hipStream_t s)
 {
     constexpr int BN = 32 * NW;
@@ -253,7 +307,7 @@ hipError_t launch_project_t(const ProjParams& p, hipStream_t s)
     q.tiles_b = (p.Mo + kBM - 1) / kBM * (Nq / BN);
     const int64_t total = tiles_a + q.tiles_b;
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL((project_kernel<NW, NS>), dim3((unsigned)total), dim3(64 * NW), 0, s, q, tiles_a);
+    hipLaunchKernelGGL((project_kernel<NW, NS, FB>), dim3((unsigned)total), dim3(64 * NW), 0, s, q, tiles_a);
     return hipGetLastError();
 }
 
@@ -267,8 +321,11 @@ hipError_t launch_project(const ProjParams& p, hipStream_t s)
     // 256-column tiles (8 waves, one workgroup per CU, 4 slots) when no tile
     // would straddle the query / key / value columns; else 128-column tiles
     // (4 waves, two workgroups per CU, 3 slots)
-    if ((p.Hq * p.D) % 256 == 0 && (p.Hkv * p.D) % 256 == 0) return launch_project_t<8, 4>(p, s);
-    return launch_project_t<4, 3>(p, s);
+    if ((p.Hq * p.D) % 256 == 0 && (p.Hkv * p.D) % 256 == 0) {
+        if (kWideFB && (p.K / kBK) % kWideNS == 0) return launch_project_t<8, kWideNS, true>(p, s);
+        return launch_project_t<8, kWideNS, false>(p, s);
+    }
+    return launch_project_t<4, 3, false>(p, s);
 }
 
 }  // namespace orthros
