@@ -15,11 +15,12 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liborthros.so")
-SOURCES = ["api.hip", "swa_prefill.hip", "swa_ring.hip", "global_xattn.hip", "copies_flash.hip", "project.hip"]
+SOURCES = ["api.hip", "swa_prefill.hip", "swa_ring.hip", "global_xattn.hip", "copies_flash.hip", "project.hip", "xattn_lds.hip"]
 # The attention kernels never produce or test NaNs in float arithmetic (masked
 # scores are -inf, running maxima start finite; an invalid copy position writes its
 # NaN as a bit pattern), so fmax needs no NaN quieting there.
-EXTRA = {"swa_ring.hip": ["-fno-honor-nans"], "copies_flash.hip": ["-fno-honor-nans"]}
+EXTRA = {"swa_ring.hip": ["-fno-honor-nans"], "copies_flash.hip": ["-fno-honor-nans"],
+         "xattn_lds.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 
 CFLAGS = [

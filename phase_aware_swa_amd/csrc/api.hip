@@ -102,7 +102,8 @@ bool fused_prefill(const orthros_desc* d)
 Split prefill_split(const orthros_desc* d, int64_t T)
 {
     Split s;
-    s.chunk = pick_chunk(T, streams_of(d), kPrefillTargetWgs);
+    const bool lds = orthros::xattn_lds_applies(dt_of(d), d->n_q_heads, d->n_kv_heads);
+    s.chunk = pick_chunk(T, streams_of(d), lds ? orthros::kXattnLdsTargetWgs : kPrefillTargetWgs);
     s.n_split = (int)((T + s.chunk - 1) / s.chunk);
     s.bytes = len_bytes(d) + (size_t)d->batch * d->n_q_heads * s.n_split * (d->head_dim + 2) * 4;
     return s;

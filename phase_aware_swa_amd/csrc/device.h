@@ -65,6 +65,32 @@ __device__ __forceinline__ void buf_store8(u32x2 v, rsrc_t r, uint32_t off)
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)off, 0, 0);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor words for [base, base + bytes) (raw buffer, no swizzle;
+// out-of-range loads return zeros), as 4 scalar registers.
+__device__ __forceinline__ i32x4 buffer_words(const void* base, int64_t bytes)
+{
+    const uint64_t a = (uint64_t)base;
+    const int64_t nb = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
+    return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)(uint32_t)nb, 0x00020000};
+}
+
+// 16 bytes per lane from the buffer at voffset + soffset into LDS at
+// lds + 16 * lane.  Written as inline asm so that the compiler inserts no
+// wait of its own for it: it would otherwise wait for every such load before
+// any LDS read, since it cannot tell the slots apart.  Completion is waited
+// for explicitly (vmcnt); M0 holds the LDS address.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voffset, int soffset, const uint16_t* lds)
+{
+    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)lds;
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voffset), "s"(rsrc), "s"(soffset), "s"(m0)
+                 : "memory", "m0");
+}
+
 // DPP lane movement inside a row of 16 lanes.  Every pattern used here
 // reads a lane of the same row, so bound_ctrl never applies; written this
 // way (old = 0, bound_ctrl set) the compiler folds the move into the DPP

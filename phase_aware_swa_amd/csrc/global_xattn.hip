@@ -520,6 +520,7 @@ hipError_t decode_by_hg(const DecodeParams& p, hipStream_t st)
 
 hipError_t launch_xattn(const XattnParams& p, hipStream_t st)
 {
+    if (xattn_lds_applies(p.dt, p.Hq, p.Hkv)) return launch_xattn_lds(p, st);
     if (p.dt == Dt::F32) return p.D == 64 ? xattn_by_hg<float, 64>(p, st) : xattn_by_hg<float, 128>(p, st);
     return p.D == 64 ? xattn_by_hg<uint16_t, 64>(p, st) : xattn_by_hg<uint16_t, 128>(p, st);
 }

@@ -95,6 +95,12 @@ hipError_t launch_swa_ring_fused(const SwaParams& p, const XattnParams& x, hipSt
 hipError_t launch_xattn(const XattnParams& p, hipStream_t s);
 // LSE merge of bf16 prefill partials [B][Hq][1][n_split][D+2] into o_out.
 hipError_t launch_merge(const XattnParams& p, hipStream_t s);
+// The LDS-streamed MFMA form of the prefill cross-attention (bf16, groups of
+// 4 query heads), then the LSE merge.  One workgroup per CU; its chunks want
+// about kXattnLdsTargetWgs workgroups in all.
+inline bool xattn_lds_applies(Dt dt, int Hq, int Hkv) { return dt == Dt::BF16 && (Hq / Hkv) % 4 == 0; }
+constexpr int64_t kXattnLdsTargetWgs = 512;
+hipError_t launch_xattn_lds(const XattnParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 
 // Output copies at many positions per sequence (no workspace).

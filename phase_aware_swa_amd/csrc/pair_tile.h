@@ -56,6 +56,21 @@ struct PairTile {
     // transposing-read chunk), and of 16-byte chunk c (dims 8c .. 8c + 7).
     __device__ static int vofs_tr(int r, int dt, int q) { return (r >> 3) * 8 * D + dt * 128 + (r & 7) * 16 + 4 * q; }
     __device__ static int vofs16(int r, int c) { return (r >> 3) * 8 * D + (c >> 1) * 128 + (r & 7) * 16 + 8 * (c & 1); }
+    // Inverse maps for loads that write LDS in lane order: the key row r and
+    // 16-byte chunk c held by 16-byte unit u of the K part (kofs) and of the
+    // V part (vofs16) of a slot.
+    __device__ static void k_unit(int u, int& r, int& c)
+    {
+        const int q = (u >> 5) & 3;
+        r = (u & 16) | (((u & 15) - 4 * q) & 15);
+        c = 4 * (u >> 7) + q;
+    }
+    __device__ static void v_unit(int u, int& r, int& c)
+    {
+        const int w = u % D;
+        r = 8 * (u / D) + ((w >> 1) & 7);
+        c = 2 * (w >> 4) + (w & 1);
+    }
     // Immediate steps of vofs_tr: dt + 1 is one line on, key r + 16
     // (r < 16) two 8-key groups on, and key r + 4 (r & 7 < 4) half a line.
     static constexpr int V_DT = 128, V_KEY16 = 16 * D, V_KEY8 = 8 * D, V_KEY4 = 64;

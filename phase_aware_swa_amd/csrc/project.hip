@@ -56,32 +56,6 @@ constexpr int kXU = kBM * 4;             // 16-byte units of a slot's X part
 constexpr int kWideNS = 4;               // LDS slots of the 256-column form
 constexpr bool kWideFB = true;           // its operand fragments double-buffered in registers
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor words for [base, base + bytes) (raw buffer, no swizzle;
-// out-of-range loads return zeros), as 4 scalar registers.
-__device__ __forceinline__ i32x4 buffer_words(const void* base, int64_t bytes)
-{
-    const uint64_t a = (uint64_t)base;
-    const int64_t nb = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
-    return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)(uint32_t)nb, 0x00020000};
-}
-
-// 16 bytes per lane from the buffer at voffset + soffset into LDS at
-// lds + 16 * lane.  Written as inline asm so that the compiler inserts no
-// wait of its own for it: it would otherwise wait for every such load before
-// any LDS read, since it cannot tell the slots apart.  Completion is waited
-// for explicitly (vmcnt); M0 holds the LDS address.
-__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voffset, int soffset, const uint16_t* lds)
-{
-    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)lds;
-    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-                 :
-                 : "v"(voffset), "s"(rsrc), "s"(soffset), "s"(m0)
-                 : "memory", "m0");
-}
-
 __device__ __forceinline__ int unit_of(int r, int c) { return 4 * r + (c ^ ((r >> 2) & 3)); }
 
 // s_waitcnt vmcnt(L * n) for a wave-uniform n in [0, NMAX] (the count is an
