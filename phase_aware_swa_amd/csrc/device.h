@@ -69,12 +69,17 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer descriptor words for [base, base + bytes) (raw buffer, no swizzle;
-// out-of-range loads return zeros), as 4 scalar registers.
+// out-of-range loads return zeros), as 4 scalar registers.  base and bytes
+// must be the same for every lane of the wave: they are taken from the first
+// active lane (the compiler's divergence analysis can lose track of uniform
+// values joined after a divergent branch, and these words must be scalar).
 __device__ __forceinline__ i32x4 buffer_words(const void* base, int64_t bytes)
 {
     const uint64_t a = (uint64_t)base;
     const int64_t nb = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
-    return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)(uint32_t)nb, 0x00020000};
+    return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)),
+                 __builtin_amdgcn_readfirstlane((int)(uint32_t)nb), 0x00020000};
 }
 
 // 16 bytes per lane from the buffer at voffset + soffset into LDS at
@@ -89,6 +94,28 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voffset, int sof
                  :
                  : "v"(voffset), "s"(rsrc), "s"(soffset), "s"(m0)
                  : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima);
+// vmcnt is 6 bits, split over the immediate's bits 3:0 and 15:14.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// s_waitcnt vmcnt(L * n) for a wave-uniform n >= 0 (the count is an
+// immediate of the instruction, hence the unrolled selection); n above NMAX
+// waits for vmcnt(L * NMAX), which is more than needed, never less.
+template <int L, int NMAX, int I = 0>
+__device__ __forceinline__ void wait_stages(int n)
+{
+    if (n == I || (I == NMAX && n > NMAX)) {
+        wait_vmcnt<L * I>();
+        return;
+    }
+    if constexpr (I < NMAX) wait_stages<L, NMAX, I + 1>(n);
 }
 
 // DPP lane movement inside a row of 16 lanes.  Every pattern used here

@@ -96,8 +96,8 @@ hipError_t launch_xattn(const XattnParams& p, hipStream_t s);
 // LSE merge of bf16 prefill partials [B][Hq][1][n_split][D+2] into o_out.
 hipError_t launch_merge(const XattnParams& p, hipStream_t s);
 // The LDS-streamed MFMA form of the prefill cross-attention (bf16, groups of
-// 4 query heads), then the LSE merge.  One workgroup per CU; its chunks want
-// about kXattnLdsTargetWgs workgroups in all.
+// 4 query heads): a persistent kernel, one workgroup per CU, then the LSE
+// merge.  Its key chunks aim at about kXattnLdsTargetWgs items in all.
 inline bool xattn_lds_applies(Dt dt, int Hq, int Hkv) { return dt == Dt::BF16 && (Hq / Hkv) % 4 == 0; }
 constexpr int64_t kXattnLdsTargetWgs = 512;
 hipError_t launch_xattn_lds(const XattnParams& p, hipStream_t s);

@@ -58,18 +58,6 @@ constexpr bool kWideFB = true;           // its operand fragments double-buffere
 
 __device__ __forceinline__ int unit_of(int r, int c) { return 4 * r + (c ^ ((r >> 2) & 3)); }
 
-// s_waitcnt vmcnt(L * n) for a wave-uniform n in [0, NMAX] (the count is an
-// immediate of the instruction, hence the unrolled selection).
-template <int L, int NMAX, int I = 0>
-__device__ __forceinline__ void wait_stages(int n)
-{
-    if (n == I) {
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (L * I));
-        return;
-    }
-    if constexpr (I < NMAX) wait_stages<L, NMAX, I + 1>(n);
-}
-
 // One tile's columns and where they go.
 struct TileKind {
     const uint16_t* w;        // first weight row of the tile ([out][in])

@@ -1,6 +1,6 @@
-// xattn_lds.hip -- the output copy's full-history cross-attention in prefill
-// for bf16 and groups of 4 query heads per KV head, for gfx950: the cache
-// streams through LDS by direct loads and the contractions run on MFMA.
+// xattn_lds.hip -- the output copy's full-history cross-attention in
+// prefill for bf16 and groups of 4 query heads per KV head, for gfx950: the
+// cache streams through LDS by direct loads and the contractions run on MFMA.
 //
 // "Orthros:阶段感知异构注意力精读笔记" §2.3 Eq. (5): the copy at original
 // position P attends over every cached key j <= P (§2.4: the mask follows the
@@ -8,25 +8,40 @@
 //
 // One query per head over the whole cache is a pure stream of K/V bytes
 // (about 2 flop per byte per head), so the design is about keeping HBM busy:
-//   - the keys of one (sequence, KV head) are cut into chunks (split-K); a
-//     workgroup owns one chunk and serves the 4 query heads of a 4-head
-//     block at once, so every K/V byte is read from HBM once;
-//   - the chunk streams through two 64 KB LDS slots in stages of 4 (d = 128)
-//     or 8 (d = 64) 32-key pairs, by buffer loads that write LDS directly
-//     (16 per lane per stage, no register staging): while one stage is
-//     consumed the next is in flight, one barrier per stage.  The LDS holds
-//     one workgroup per CU, which is what the streaming needs;
+//   - the keys of one (sequence, KV head) are cut into chunks (split-K); an
+//     item is one chunk of one (sequence, KV head, 4-head block): the 4
+//     query heads of the block are served at once, so every K/V byte is read
+//     from HBM once;
+//   - the kernel is persistent: one workgroup per CU walks the items
+//     k = blockIdx, blockIdx + grid, ... of the sequences' concatenated item
+//     lists (each wave holds one sequence per lane and finds an item's
+//     sequence with one ballot over the lanes' prefix sums);
+//   - an item's keys stream through two 64 KB LDS slots in stages of 4
+//     (d = 128) or 8 (d = 64) 32-key pairs, by buffer loads that write LDS
+//     directly (16 per lane per stage, no register staging).  The stage
+//     sequence runs on across items, and stage t + 2 is issued into stage
+//     t's slot as soon as every wave is done with it, while stage t + 1 is
+//     still landing in the other slot: the load queue never runs dry, and a
+//     new item costs no pipeline refill.  The item's query rows and their
+//     scale-offsets come the same way into a small double-buffered LDS area;
+//   - the waits are explicit vmcnt counts: each wave counts what it issued
+//     after a stage's loads (the next stage's loads and rows, partial
+//     stores), and vector memory operations retire in issue order, so the
+//     stage's wait lets exactly those stay in flight;
 //   - each load instruction fills 1 KB of a slot in lane order, so each lane
 //     fetches the cache chunk that belongs at its 16-byte unit of the pair
 //     layout (PairTile's inverse maps); the stage's buffer range ends at the
-//     chunk's last key, so keys past it land as zeros;
-//   - wave w consumes the stage's pairs w (and 4 + w at d = 64):
-//     S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 with the 4
-//     heads' queries as columns 0..3 of the B operand (the other 12 are
-//     zero: the MFMAs are idle most of the time either way), V^T from the
-//     transposing LDS read, online softmax in exp2 units with a lazy rescale;
-//   - the 4 waves' states merge through LDS into one (max, sum, weighted sum
-//     of values) partial per head, in the layout the LSE merge reads.
+//     item's last key, so keys past it land as zeros;
+//   - pair p of a stage is consumed by wave p % 4: S^T = K Q^T and
+//     O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 with the 4 heads' queries as
+//     columns 0..3 of the B operand (the other 12 are zero: the MFMAs are
+//     idle most of the time either way), V^T from the transposing LDS read,
+//     online softmax per column in exp2 units with a lazy rescale;
+//   - at an item's last stage the 4 waves' states merge through LDS into one
+//     (max, sum, weighted sum of values) partial per head, in the layout the
+//     LSE merge reads.
+
+#include <atomic>
 
 #include "device.h"
 #include "kernels.h"
@@ -35,42 +50,91 @@
 namespace orthros {
 namespace {
 
-constexpr int kStageBytes = 65536;                 // one LDS slot
-constexpr int kLoads = kStageBytes / (256 * 16);   // direct loads per lane per stage
 constexpr float kMargin = 8.0f;                    // lazy-rescale margin, log2 units
+constexpr int kStageBytes = 65536;                 // one LDS slot
+
+// s_waitcnt lgkmcnt(0) alone: this wave's LDS accesses are done.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+__device__ __forceinline__ void block_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ int64_t readlane64(int64_t x, int l)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), l);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// One item: chunk s of stream j = (KV head g, 4-head block hb) of sequence b,
+// keys lo .. hi (hi <= P, the copy's position), nst stages.
+struct Item {
+    int b, g, hb, s, nst;
+    int64_t lo, hi;
+};
 
 template <int D>
-__global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams p, int b0, PosBlock pos)
+__global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams a, int b0, int nb, PosBlock pos)
 {
     using R = PairTile<D>;
-    constexpr int PPW = 128 / D;          // pairs per wave per stage
-    constexpr int SK = 128 * PPW;         // keys per stage
+    constexpr int NP = 128 / D * 4;       // pairs per stage: 64 KB
+    constexpr int SK = 32 * NP;           // keys per stage
     constexpr int PAIRB = 32 * D * 2;     // bytes of one pair's K (or V) rows in the cache
     constexpr int JP = D / 32;            // loads per lane per pair: JH of K, then JH of V
     constexpr int JH = JP / 2;
+    constexpr int LPS = NP * JP;          // direct loads per lane per stage
     constexpr int NQ = D / 32, ND = D / 16;
-    constexpr int SLOTE = kStageBytes / 2;  // slot size in bf16 elements
-    static_assert(4 * PPW * JP == kLoads && 4 * PPW * R::SLOT == SLOTE, "stage shape");
+    constexpr int SLOTE = NP * R::SLOT;   // slot size in bf16 elements
+    // the item's rows in LDS: 4 head rows of each of q_out, alpha_out, beta_out
+    constexpr int NREG = 3;
+    constexpr int HRE = 4 * D;            // elements per region
+    constexpr int NST = D / 64 + 1;       // partial stores per wave and item
+    static_assert(SLOTE * 2 == kStageBytes && LPS == 16, "stage shape");
     __shared__ __align__(16) uint16_t lds[2 * SLOTE];
+    __shared__ __align__(16) uint16_t qa[2][NREG * HRE];
+    __shared__ __align__(16) float red[4][4][D + 2];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, gq = lane >> 4;
-    const int s = blockIdx.x;
-    const int hblocks = (p.Hq / p.Hkv) / 4;
-    const int g = blockIdx.y / hblocks, hb = blockIdx.y % hblocks;
-    const int bi = blockIdx.z, b = b0 + bi;
-    const int64_t P = pos.v[bi];
-    if (s == 0 && blockIdx.y == 0 && tid == 0) p.ws_len[b] = (int32_t)P;
-    const int64_t lo = (int64_t)s * p.chunk;
-    if (lo > P) return;
-    const int64_t hi = lo + p.chunk - 1 < P ? lo + p.chunk - 1 : P;
-    const int nst = (int)((hi - lo) / SK) + 1;
-    const int h0 = g * (p.Hq / p.Hkv) + hb * 4;
+    const int hblocks = (a.Hq / a.Hkv) / 4;
+    const int S = a.Hkv * hblocks;        // streams (items per chunk index) of a sequence
+    const uint16_t* k_cache = (const uint16_t*)a.k_cache;
+    const uint16_t* v_cache = (const uint16_t*)a.v_cache;
 
-    const int64_t crow = ((int64_t)b * p.Hkv + g) * p.cap * D;
-    const uint16_t* kc = (const uint16_t*)p.k_cache + crow;
-    const uint16_t* vc = (const uint16_t*)p.v_cache + crow;
+    // lane i < nb: sequence b0 + i, its copy position and its item count
+    const int64_t Lv = lane < nb ? pos.v[lane] : -1;
+    const int cnt = lane < nb ? (int)(Lv / a.chunk + 1) * S : 0;
+    if (blockIdx.x == 0 && tid < nb) a.ws_len[b0 + tid] = (int32_t)Lv;
+    int incl = cnt;      // inclusive prefix sum over the lanes
+#pragma unroll
+    for (int x = 1; x < 64; x <<= 1) {
+        const int t = __shfl_up(incl, x);
+        if (lane >= x) incl += t;
+    }
+    const int excl = incl - cnt;
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    const int nwg = gridDim.x;
+
+    auto item_of = [&](int k, Item& it) {
+        const uint64_t m = __ballot(lane < nb && excl <= k);
+        const int bl = __popcll(m) - 1;
+        it.b = b0 + bl;
+        const int64_t L = readlane64(Lv, bl);
+        const int nch = (int)(L / a.chunk) + 1;
+        const int r = k - __builtin_amdgcn_readlane(excl, bl);
+        const int j = r / nch;
+        it.s = r - j * nch;
+        it.g = j / hblocks;
+        it.hb = j - it.g * hblocks;
+        it.lo = (int64_t)it.s * a.chunk;
+        it.hi = it.lo + a.chunk - 1 < L ? it.lo + a.chunk - 1 : L;
+        it.nst = (int)((it.hi - it.lo) / SK) + 1;
+    };
 
     // byte offset, inside one pair's rows, of the chunk this lane fetches for
     // the 16-byte unit 256 jj + 64 wv + lane of the pair's K and V parts
@@ -83,60 +147,83 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams p, int b0, P
         R::v_unit(256 * jj + 64 * wv + lane, r, c);
         voff[jj] = (uint32_t)((r * D + 8 * c) * 2);
     }
-    // stage st -> slot st & 1: load j of wave wv fills units 256 j + 64 wv ..
-    // + 63 of the slot, i.e. part (j % JP) of pair j / JP
-    auto issue = [&](int st) {
-        const int64_t k0 = lo + (int64_t)st * SK;
-        const int64_t avail = (hi - k0 + 1) * D * 2;
-        const i32x4 rk = buffer_words(kc + k0 * D, avail);
-        const i32x4 rv = buffer_words(vc + k0 * D, avail);
-        const uint16_t* dst = lds + (st & 1) * SLOTE + 64 * wv * 8;
+    // stage st of item `it` into slot `sl`: load j of wave wv fills units
+    // 256 j + 64 wv .. + 63 of the slot, i.e. part (j % JP) of pair j / JP
+    auto issue = [&](const Item& it, int st, int sl) {
+        const int64_t crow = ((int64_t)it.b * a.Hkv + it.g) * a.cap * D;
+        const int64_t k0 = it.lo + (int64_t)st * SK;
+        const int64_t avail = (it.hi - k0 + 1) * D * 2;
+        const i32x4 rk = buffer_words(k_cache + crow + k0 * D, avail);
+        const i32x4 rv = buffer_words(v_cache + crow + k0 * D, avail);
+        const uint16_t* dst = lds + sl * SLOTE + 64 * wv * 8;
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j) {
+        for (int j = 0; j < LPS; ++j) {
             const int pp = j / JP, jj = j % JP;
             if (jj < JH) load_lds16(rk, koff[jj] + pp * PAIRB, 0, dst + 256 * j * 8);
             else load_lds16(rv, voff[jj - JH] + pp * PAIRB, 0, dst + 256 * j * 8);
         }
     };
+    // the item's query rows and scale-offsets into qa[q]: region i by wave
+    // i, one load instruction of D / 2 lanes each
+    auto issue_rows = [&](const Item& it, int q) {
+        if (wv >= NREG) return;
+        const int h0 = it.g * (a.Hq / a.Hkv) + it.hb * 4;
+        const uint16_t* src = wv == 0 ? (const uint16_t*)a.q_out + ((int64_t)it.b * a.Hq + h0) * D
+                            : (wv == 1 ? (const uint16_t*)a.alpha_out : (const uint16_t*)a.beta_out) +
+                                  (int64_t)h0 * D;
+        const i32x4 rs = buffer_words(src, HRE * 2);
+        if (lane < HRE / 8) load_lds16(rs, 16 * lane, 0, &qa[q][wv * HRE]);
+    };
 
-    // the 4 heads' scale-offset queries, times qscale (the score scale with
-    // log2(e): scores come out of the MFMAs in exp2 units), as B operands:
-    // lane (n, gq) holds head h0 + n (n < 4; zero otherwise), dims 32 i + 8 gq .. + 7
-    bf16x8 qf[NQ];
-    {
-        const float qs = p.qscale;
-        const int h = h0 + (n < 4 ? n : 0);
-        const uint16_t* qrow = (const uint16_t*)p.q_out + ((int64_t)b * p.Hq + h) * D;
-        const uint16_t* al = (const uint16_t*)p.alpha_out + (int64_t)h * D;
-        const uint16_t* be = (const uint16_t*)p.beta_out + (int64_t)h * D;
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-            const int d0 = 32 * i + 8 * gq;
-            const u32x4 qw = *(const u32x4*)(qrow + d0);
-            const u32x4 av = *(const u32x4*)(al + d0);
-            const u32x4 bv = *(const u32x4*)(be + d0);
-            u32x4 r;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t w = qw[e], aw = av[e], bw = bv[e];
-                r[e] = pack_bf16x2(__builtin_fmaf(bf16_lo(w), bf16_lo(aw), bf16_lo(bw)) * qs,
-                                   __builtin_fmaf(bf16_hi(w), bf16_hi(aw), bf16_hi(bw)) * qs);
-                r[e] = n < 4 ? r[e] : 0u;
-            }
-            qf[i] = __builtin_bit_cast(bf16x8, r);
+    int kc = blockIdx.x;          // the item being consumed, and its stage
+    if (kc >= total) return;
+    Item ci;
+    item_of(kc, ci);
+    int sc = 0, qc = 0;           // qc: parity of ci's row area
+    Item ii = ci;                 // the item being issued, its next stage and row area
+    int ki = kc, si = 0, qi = 0;
+    bool more = true;             // the issue cursor has stages left
+    auto advance_issue = [&]() {
+        if (++si < ii.nst) return;
+        ki += nwg;
+        if (ki >= total) {
+            more = false;
+            return;
         }
-    }
+        item_of(ki, ii);
+        si = 0;
+        qi ^= 1;
+    };
+    // vector memory instructions this wave issued after the loads (and
+    // rows) of the stage in slot 0 / 1: the stage's wait lets exactly those
+    // stay in flight
+    int after0 = 0, after1 = 0;
+    const int rows_w = wv < NREG ? 1 : 0;
+    auto issue_next = [&](int sl) {
+        issue(ii, si, sl);
+        const int k = LPS + (si == 0 ? rows_w : 0);
+        if (sl == 0) {
+            after0 = 0;
+            after1 += k;
+        } else {
+            after1 = 0;
+            after0 += k;
+        }
+        if (si == 0) issue_rows(ii, qi);
+        advance_issue();
+    };
+    issue_next(0);
+    if (more) issue_next(1);
 
     const bf16x8 kOnes = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
     const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 qf[NQ];
     f32x4 oacc[ND];
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt) oacc[dt] = zero;
     f32x4 lacc = zero;
-    float m_run = kNegBig;      // lane (n, .): the running maximum of head h0 + n
+    float m_run = kNegBig;        // lane (n, .): the running maximum of head n of the block
 
-    // one pair of the stage in `slot`: keys key0 .. key0 + 31
-    auto attend = [&](const uint16_t* slot, int pp, int64_t key0) {
+    // one pair of the stage in `slot`: keys key0 .. key0 + 31, the last admissible hi
+    auto attend = [&](const uint16_t* slot, int pp, int64_t key0, int64_t hi) {
         int ko = pp * R::SLOT + R::kofs(n, gq);
         asm volatile("" : "+v"(ko));
         const uint16_t* kb = slot + ko;
@@ -148,7 +235,7 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams p, int b0, P
             s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[i], s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[i], s1, 0, 0, 0);
         }
-        // s0[r]: key key0 + 4 gq + r, s1[r]: key key0 + 16 + 4 gq + r (head h0 + n)
+        // s0[r]: key key0 + 4 gq + r, s1[r]: key key0 + 16 + 4 gq + r (column n)
         if (key0 + 31 > hi) {
             const int lim = (int)(hi - key0) - 4 * gq;
 #pragma unroll
@@ -190,57 +277,121 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams p, int b0, P
         }
     };
 
-    issue(0);
-    for (int st = 0; st < nst; ++st) {
-        // this wave's loads of stage st have landed; after the barrier every
-        // wave's have, and every wave is done with stage st - 1's slot
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if (st + 1 < nst) issue(st + 1);
-        const uint16_t* slot = lds + (st & 1) * SLOTE;
+    for (int t = 0;; ++t) {
+        // this wave's loads of stage t (and, at an item's first stage, its
+        // rows) have landed -- what it issued after them may still be in
+        // flight; after the barrier every wave's have
+        wait_stages<1, LPS + 1 + NST>((t & 1) ? after1 : after0);
+        block_barrier();
+        const uint16_t* slot = lds + (t & 1) * SLOTE;
+        if (sc == 0) {
+            // a new item: its scale-offset queries (times qscale, the score
+            // scale with log2(e), so scores come out of the MFMAs in exp2
+            // units) as B operands -- lane (n, gq) holds head n of the
+            // block (n < 4; zero otherwise), dims 32 i + 8 gq .. + 7 -- and
+            // fresh softmax states
+            const float qs = a.qscale;
+            const uint16_t* qr = qa[qc] + (n & 3) * D;
 #pragma unroll
-        for (int t = 0; t < PPW; ++t) {
-            const int pp = wv * PPW + t;
-            const int64_t key0 = lo + (int64_t)st * SK + 32 * pp;
-            if (key0 <= hi) attend(slot, pp, key0);
+            for (int i = 0; i < NQ; ++i) {
+                const int d0 = 32 * i + 8 * gq;
+                const u32x4 qw = *(const u32x4*)(qr + d0);
+                const u32x4 av = *(const u32x4*)(qr + HRE + d0);
+                const u32x4 bv = *(const u32x4*)(qr + 2 * HRE + d0);
+                u32x4 r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t w = qw[e], aw = av[e], bw = bv[e];
+                    r[e] = pack_bf16x2(__builtin_fmaf(bf16_lo(w), bf16_lo(aw), bf16_lo(bw)) * qs,
+                                       __builtin_fmaf(bf16_hi(w), bf16_hi(aw), bf16_hi(bw)) * qs);
+                    r[e] = n < 4 ? r[e] : 0u;
+                }
+                qf[i] = __builtin_bit_cast(bf16x8, r);
+            }
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt) oacc[dt] = zero;
+            lacc = zero;
+            m_run = kNegBig;
         }
-    }
+        // pair pp of the stage goes to wave pp % 4
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+            const int64_t key0 = ci.lo + (int64_t)sc * SK + 32 * pp;
+            if ((pp & 3) == wv && key0 <= ci.hi) attend(slot, pp, key0, ci.hi);
+        }
+        if (++sc < ci.nst) {
+            // every wave is done with slot t & 1: stage t + 2 goes there
+            // while stage t + 1 may still be landing in the other slot
+            block_barrier();
+            if (more) issue_next(t & 1);
+            continue;
+        }
 
-    // merge the 4 waves' states (fixed order) into the partials of the
-    // chunk: out[head][{max, sum, sum of weighted values}]
-    __syncthreads();
-    float (*red)[4][D + 2] = (float (*)[4][D + 2])lds;    // [wave][head][D + 2]
-    if (n < 4) {
+        // the item's last stage: merge the 4 waves' states (fixed order)
+        // into its partials out[head][{max, sum, sum of weighted values}];
+        // wave w writes head w of the block with NST store instructions
+        if (n < 4) {
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt)
+            for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) red[wv][n][2 + 16 * dt + 4 * gq + r] = oacc[dt][r];
-        if (gq == 0) {
-            red[wv][n][0] = m_run;
-            red[wv][n][1] = lacc[0];
+                for (int r = 0; r < 4; ++r) red[wv][n][2 + 16 * dt + 4 * gq + r] = oacc[dt][r];
+            if (gq == 0) {
+                red[wv][n][0] = m_run;
+                red[wv][n][1] = lacc[0];
+            }
         }
-    }
-    __syncthreads();
-    const int64_t part_stride = (int64_t)p.n_split * (D + 2);
-    float* out = p.ws_part + ((int64_t)b * p.Hq + h0) * part_stride + (int64_t)s * (D + 2);
-    for (int idx = tid; idx < 4 * (D + 1); idx += 256) {
-        const int hh = idx / (D + 1), d = idx % (D + 1);   // d == D: the (max, sum) pair
-        float M = red[0][hh][0];
+        wait_lgkm0();
+        block_barrier();
+        {
+            const int h0 = ci.g * (a.Hq / a.Hkv) + ci.hb * 4;
+            float* o = a.ws_part + ((int64_t)ci.b * a.Hq + h0 + wv) * a.n_split * (D + 2) +
+                       (int64_t)ci.s * (D + 2);
+            float mw[4], M = kNegBig;
 #pragma unroll
-        for (int w = 1; w < 4; ++w) M = fmaxf(M, red[w][hh][0]);
-        float sum = 0.f;
+            for (int w = 0; w < 4; ++w) {
+                mw[w] = red[w][wv][0];
+                M = fmaxf(M, mw[w]);
+            }
+            float f[4];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) sum += fast_exp2(red[w][hh][0] - M) * (d < D ? red[w][hh][2 + d] : red[w][hh][1]);
-        float* o = out + hh * part_stride;
-        if (d < D) {
-            o[2 + d] = sum;
-        } else {
-            o[0] = M;
-            o[1] = sum;
+            for (int w = 0; w < 4; ++w) f[w] = fast_exp2(mw[w] - M);
+#pragma unroll
+            for (int h = 0; h < D / 64; ++h) {
+                const int d = lane + 64 * h;
+                float sum = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) sum += f[w] * red[w][wv][2 + d];
+                o[2 + d] = sum;
+            }
+            float l = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) l += f[w] * red[w][wv][1];
+            if (lane == 0) *(float2*)o = make_float2(M, l);
+            after0 += NST;
+            after1 += NST;
         }
+        kc += nwg;
+        if (kc >= total) break;
+        item_of(kc, ci);
+        sc = 0;
+        qc ^= 1;
+        block_barrier();
+        if (more) issue_next(t & 1);
     }
+}
+
+// Compute units of the current device (one persistent workgroup each),
+// looked up once per device.
+int cu_count()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
 }
 
 }  // namespace
@@ -248,13 +399,18 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams p, int b0, P
 hipError_t launch_xattn_lds(const XattnParams& p, hipStream_t st)
 {
     const int hblocks = (p.Hq / p.Hkv) / 4;
+    const int ncu = cu_count();
     for (int b0 = 0; b0 < p.B; b0 += kPosPerLaunch) {
         const int nb = p.B - b0 < kPosPerLaunch ? p.B - b0 : kPosPerLaunch;
         PosBlock pos;
-        for (int i = 0; i < nb; ++i) pos.v[i] = p.pos[b0 + i];
-        const dim3 grid((unsigned)p.n_split, (unsigned)(p.Hkv * hblocks), (unsigned)nb);
-        if (p.D == 64) hipLaunchKernelGGL((xattn_lds_kernel<64>), grid, dim3(256), 0, st, p, b0, pos);
-        else hipLaunchKernelGGL((xattn_lds_kernel<128>), grid, dim3(256), 0, st, p, b0, pos);
+        for (int i = 0; i < kPosPerLaunch; ++i) pos.v[i] = i < nb ? p.pos[b0 + i] : 0;
+        // items of this launch, at most (every position at T - 1)
+        const int64_t max_items = (int64_t)nb * p.Hkv * hblocks * p.n_split;
+        const unsigned grid = (unsigned)(max_items < ncu ? max_items : ncu);
+        if (p.D == 64)
+            hipLaunchKernelGGL((xattn_lds_kernel<64>), dim3(grid), dim3(256), 0, st, p, b0, nb, pos);
+        else
+            hipLaunchKernelGGL((xattn_lds_kernel<128>), dim3(grid), dim3(256), 0, st, p, b0, nb, pos);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -55,6 +55,34 @@ def test_decode_steps_parity(Hq, Hkv, d, w, dtype):
     assert torch.equal(bits(dec.v_cache.cpu()), bits(vc))
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_decode_lengths_at_stage_and_chunk_edges(d):
+    """bf16, 4-head groups (the LDS-streamed kernel): lengths whose new key L
+    is the first or last key of a 128- or 256-key stage and of a 256-key
+    chunk, and one that leaves the last chunk a single key; 3 steps each."""
+    lens = [0, 127, 128, 255, 256, 511, 1023, 4095]
+    steps = 3
+    Hq, Hkv, w = 8, 2, 128
+    dtype = torch.bfloat16
+    say(f"decode edges d={d} lens={lens}")
+    xc, cap = small_decode_inputs(len(lens), Hq, Hkv, d, dtype, lens, steps, seed=25 + d)
+    cfg = dict(batch=len(lens), n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=w, dtype=dtype)
+    x = to_dev(xc)
+    dec = Decode(cfg, x["k_cache"], x["v_cache"], x["cache_len"], max(lens) + steps, x["alpha"], x["beta"],
+                 x["alpha_out"], x["beta_out"])
+    kc, vc, lc = xc["k_cache"].clone(), xc["v_cache"].clone(), xc["cache_len"].clone()
+    for s in range(steps):
+        dec.step(x["q"][s], x["q_out"][s], x["k_new"][s], x["v_new"][s])
+        torch.cuda.synchronize()
+        o, o_out = oracle.decode_step(xc["q"][s], xc["q_out"][s], xc["k_new"][s], xc["v_new"][s], xc["alpha"],
+                                      xc["beta"], xc["alpha_out"], xc["beta_out"], w, kc, vc, lc)
+        assert_parity(dec.o, o, dtype, f"o step {s}")
+        assert_parity(dec.o_out, o_out, dtype, f"o_out step {s}")
+    assert torch.equal(dec.cache_len.cpu(), lc)
+    assert torch.equal(bits(dec.k_cache.cpu()), bits(kc))
+    assert torch.equal(bits(dec.v_cache.cpu()), bits(vc))
+
+
 def test_decode_length_beyond_hint_is_left_alone():
     """A sequence whose length exceeds max_len_hint gets NaN outputs, no cache
     write and no length update; the others step normally."""
