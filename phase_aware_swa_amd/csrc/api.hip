@@ -86,7 +86,7 @@ size_t len_bytes(const orthros_desc* d)
     return ((size_t)d->batch * 4 + kLenBytesAlign - 1) / kLenBytesAlign * kLenBytesAlign;
 }
 
-struct Split { int chunk, n_split; size_t bytes; };
+struct Split { int chunk, n_split, rec; bool lds; size_t bytes; };
 
 orthros::Dt dt_of(const orthros_desc* d) { return d->dtype == ORTHROS_F32 ? orthros::Dt::F32 : orthros::Dt::BF16; }
 
@@ -105,7 +105,9 @@ Split prefill_split(const orthros_desc* d, int64_t T)
     const bool lds = orthros::xattn_lds_applies(dt_of(d), d->n_q_heads, d->n_kv_heads);
     s.chunk = pick_chunk(T, streams_of(d), lds ? orthros::kXattnLdsTargetWgs : kPrefillTargetWgs);
     s.n_split = (int)((T + s.chunk - 1) / s.chunk);
-    s.bytes = len_bytes(d) + (size_t)d->batch * d->n_q_heads * s.n_split * (d->head_dim + 2) * 4;
+    s.rec = d->head_dim + (lds ? orthros::kXattnLdsRecPad : 2);
+    s.lds = lds;
+    s.bytes = len_bytes(d) + (size_t)d->batch * d->n_q_heads * s.n_split * s.rec * 4;
     return s;
 }
 
@@ -115,7 +117,9 @@ Split fused_split(const orthros_desc* d, int64_t T)
     Split s;
     s.chunk = 32 * r.tps;
     s.n_split = r.n_seg;
-    s.bytes = len_bytes(d) + (size_t)d->batch * d->n_q_heads * s.n_split * (d->head_dim + 2) * 4;
+    s.rec = d->head_dim + 2;
+    s.lds = false;
+    s.bytes = len_bytes(d) + (size_t)d->batch * d->n_q_heads * s.n_split * s.rec * 4;
     return s;
 }
 
@@ -131,9 +135,17 @@ Split decode_split(const orthros_desc* d, int64_t max_len)
 {
     Split s;
     const int64_t keys = max_len + 1;
-    s.chunk = pick_chunk(keys, streams_of(d), kDecodeTargetWgs);
+    // the LDS-streamed kernel: about kXattnLdsDecodeItems items, chunks a
+    // whole number of 128-key stages
+    int64_t want = (keys * streams_of(d) + orthros::kXattnLdsDecodeItems - 1) / orthros::kXattnLdsDecodeItems;
+    want = want < (int64_t(1) << 24) ? want : (int64_t(1) << 24);
+    const bool lds = orthros::xattn_lds_applies(dt_of(d), d->n_q_heads, d->n_kv_heads) && d->head_dim == 128 &&
+                     want >= orthros::kXattnLdsDecodeMinChunk;
+    s.lds = lds;
+    s.chunk = lds ? (int)((want + 127) / 128 * 128) : pick_chunk(keys, streams_of(d), kDecodeTargetWgs);
     s.n_split = (int)((keys + s.chunk - 1) / s.chunk);
-    s.bytes = len_bytes(d) + (size_t)d->batch * d->n_q_heads * 2 * s.n_split * (d->head_dim + 2) * 4;
+    s.rec = d->head_dim + (lds ? orthros::kXattnLdsRecPad : 2);
+    s.bytes = len_bytes(d) + (size_t)d->batch * d->n_q_heads * 2 * s.n_split * s.rec * 4;
     return s;
 }
 
@@ -223,7 +235,7 @@ orthros::XattnParams xattn_params(const orthros_desc* d, const Split& sp, const 
     p.pos = out_pos;
     p.cap = cap;
     p.B = d->batch; p.Hq = d->n_q_heads; p.Hkv = d->n_kv_heads; p.D = d->head_dim;
-    p.chunk = sp.chunk; p.n_split = sp.n_split;
+    p.chunk = sp.chunk; p.n_split = sp.n_split; p.rec = sp.rec;
     p.qscale = qscale_of(d);
     p.dt = dt_of(d);
     return p;
@@ -411,7 +423,7 @@ orthros_status orthros_decode_step(const orthros_desc* desc, const void* q, cons
     p.cap = cap; p.max_len = max_len_hint;
     p.B = desc->batch; p.Hq = desc->n_q_heads; p.Hkv = desc->n_kv_heads; p.D = desc->head_dim;
     p.window = desc->window;
-    p.chunk = sp.chunk; p.n_split = sp.n_split;
+    p.chunk = sp.chunk; p.n_split = sp.n_split; p.rec = sp.rec; p.lds = sp.lds ? 1 : 0;
     p.qscale = qscale_of(desc);
     p.dt = desc->dtype == ORTHROS_F32 ? orthros::Dt::F32 : orthros::Dt::BF16;
     return hip_status(orthros::launch_decode(p, (hipStream_t)stream), "decode kernel launch");

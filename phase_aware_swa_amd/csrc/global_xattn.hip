@@ -382,8 +382,8 @@ __global__ __launch_bounds__(256) void copies_simple_kernel(CopiesParams p)
 template <typename E, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const float* ws_part, const int32_t* ws_len,
                                                     int32_t* cache_len, int64_t max_len, int window,
-                                                    int Hq, int chunk, int n_split, int kinds,
-                                                    E* o_out, E* o)
+                                                    int Hq, int chunk, int n_split, int rec,
+                                                    int kinds, E* o_out, E* o)
 {
     constexpr int TPR = D / 4;            // threads per head-dim row
     constexpr int NG = 256 / TPR;         // split groups
@@ -393,7 +393,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* ws_part, const 
     const int b = blockIdx.x / Hq, h = blockIdx.x % Hq;
     const int gp = tid / TPR, d4 = tid % TPR;
     const int64_t L = ws_len[b];
-    const int64_t kind_stride = (int64_t)n_split * (D + 2);
+    const int64_t kind_stride = (int64_t)n_split * rec;
+    const int aoff = rec - D;             // the weighted values' offset in a record
     const float* part = ws_part + ((int64_t)b * Hq + h) * kinds * kind_stride;
     const int64_t row = ((int64_t)b * Hq + h) * D;
     if (L < 0 || L > max_len) {
@@ -409,7 +410,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* ws_part, const 
         const float* pk = part + kind * kind_stride;
         // M = max over splits
         float mx = kNegBig;
-        for (int s = s0 + tid; s <= s1; s += 256) mx = fmaxf(mx, pk[(int64_t)s * (D + 2)]);
+        for (int s = s0 + tid; s <= s1; s += 256) mx = fmaxf(mx, pk[(int64_t)s * rec]);
 #pragma unroll
         for (int x = 32; x > 0; x >>= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
         if (lane == 0) wmax[wv] = mx;
@@ -427,11 +428,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* ws_part, const 
 #pragma unroll
             for (int k = 0; k < RB; ++k) {
                 const int sk = s + NG * k <= s1 ? s + NG * k : s1;
-                const float* ps = pk + (int64_t)sk * (D + 2);
+                const float* ps = pk + (int64_t)sk * rec;
                 ml[k][0] = ps[0];
                 ml[k][1] = ps[1];
-                a[k] = *(const float2*)(ps + 2 + 4 * d4);
-                c[k] = *(const float2*)(ps + 4 + 4 * d4);
+                a[k] = *(const float2*)(ps + aoff + 4 * d4);
+                c[k] = *(const float2*)(ps + aoff + 2 + 4 * d4);
             }
 #pragma unroll
             for (int k = 0; k < RB; ++k) {
@@ -479,7 +480,8 @@ hipError_t launch_xattn_t(const XattnParams& p, hipStream_t st)
     int64_t max_len = 0;
     for (int b = 0; b < p.B; ++b) max_len = p.pos[b] > max_len ? p.pos[b] : max_len;
     hipLaunchKernelGGL((merge_kernel<E, D>), dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part, p.ws_len,
-                       (int32_t*)nullptr, max_len, 0, p.Hq, p.chunk, p.n_split, 1, (E*)p.o_out, (E*)nullptr);
+                       (int32_t*)nullptr, max_len, 0, p.Hq, p.chunk, p.n_split, p.rec, 1, (E*)p.o_out,
+                       (E*)nullptr);
     return hipGetLastError();
 }
 
@@ -491,9 +493,7 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t st)
                        st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((merge_kernel<E, D>), dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part, p.ws_len,
-                       p.cache_len, p.max_len, p.window, p.Hq, p.chunk, p.n_split, 2, (E*)p.o_out, (E*)p.o);
-    return hipGetLastError();
+    return launch_decode_merge(p, st);
 }
 
 template <typename E, int D>
@@ -548,19 +548,38 @@ hipError_t launch_merge(const XattnParams& p, hipStream_t st)
 {
     int64_t max_len = 0;
     for (int b = 0; b < p.B; ++b) max_len = p.pos[b] > max_len ? p.pos[b] : max_len;
-    if (p.D == 64)
-        hipLaunchKernelGGL((merge_kernel<uint16_t, 64>), dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part, p.ws_len,
-                           (int32_t*)nullptr, max_len, 0, p.Hq, p.chunk, p.n_split, 1, (uint16_t*)p.o_out,
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part, p.ws_len, (int32_t*)nullptr,
+                           max_len, 0, p.Hq, p.chunk, p.n_split, p.rec, 1, (uint16_t*)p.o_out,
                            (uint16_t*)nullptr);
-    else
-        hipLaunchKernelGGL((merge_kernel<uint16_t, 128>), dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part,
-                           p.ws_len, (int32_t*)nullptr, max_len, 0, p.Hq, p.chunk, p.n_split, 1,
-                           (uint16_t*)p.o_out, (uint16_t*)nullptr);
+    };
+    if (p.D == 64) go(merge_kernel<uint16_t, 64>);
+    else go(merge_kernel<uint16_t, 128>);
+    return hipGetLastError();
+}
+
+template <typename E, int D>
+void decode_merge_t(const DecodeParams& p, hipStream_t st)
+{
+    hipLaunchKernelGGL((merge_kernel<E, D>), dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part, p.ws_len, p.cache_len,
+                       p.max_len, p.window, p.Hq, p.chunk, p.n_split, p.rec, 2, (E*)p.o_out, (E*)p.o);
+}
+
+hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t st)
+{
+    if (p.dt == Dt::F32) {
+        if (p.D == 64) decode_merge_t<float, 64>(p, st);
+        else decode_merge_t<float, 128>(p, st);
+    } else {
+        if (p.D == 64) decode_merge_t<uint16_t, 64>(p, st);
+        else decode_merge_t<uint16_t, 128>(p, st);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st)
 {
+    if (p.lds) return launch_decode_lds(p, st);
     if (p.dt == Dt::F32) return p.D == 64 ? decode_by_hg<float, 64>(p, st) : decode_by_hg<float, 128>(p, st);
     return p.D == 64 ? decode_by_hg<uint16_t, 64>(p, st) : decode_by_hg<uint16_t, 128>(p, st);
 }

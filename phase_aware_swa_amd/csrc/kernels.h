@@ -39,11 +39,15 @@ struct XattnParams {
     const void* v_cache;
     void* o_out;          // [B][Hq][D]
     int32_t* ws_len;      // workspace: per-sequence last key index
-    float* ws_part;       // workspace: partials [B][Hq][1][n_split][D+2]
+    float* ws_part;       // workspace: partials [B][Hq][1][n_split][rec]
     const int64_t* pos;   // host [B]: copy positions
     int64_t cap;
     int32_t B, Hq, Hkv, D;
     int32_t chunk, n_split;
+    // stride of a partial record in floats: (max, sum, ..., weighted values
+    // at rec - D); D + 2, except on the LDS-streamed kernel (D +
+    // kXattnLdsRecPad: the values start on a 128-byte line)
+    int32_t rec;
     float qscale;
     Dt dt;
 };
@@ -63,10 +67,12 @@ struct DecodeParams {
     void* o;              // [B][Hq][D]
     void* o_out;
     int32_t* ws_len;      // workspace: per-sequence length seen by this step
-    float* ws_part;       // workspace: partials [B][Hq][2][n_split][D+2]
+    float* ws_part;       // workspace: partials [B][Hq][2][n_split][rec]
     int64_t cap, max_len;
     int32_t B, Hq, Hkv, D, window;
     int32_t chunk, n_split;
+    int32_t rec;          // as in XattnParams
+    int32_t lds;          // nonzero: the LDS-streamed kernel (chosen with the split)
     float qscale;
     Dt dt;
 };
@@ -93,15 +99,29 @@ hipError_t launch_swa_ring(const SwaParams& p, hipStream_t s);
 // n_seg); the LSE merge follows.  x.k_cache / v_cache are not read.
 hipError_t launch_swa_ring_fused(const SwaParams& p, const XattnParams& x, hipStream_t s);
 hipError_t launch_xattn(const XattnParams& p, hipStream_t s);
-// LSE merge of bf16 prefill partials [B][Hq][1][n_split][D+2] into o_out.
+// LSE merge of bf16 prefill partials [B][Hq][1][n_split][rec] into o_out.
 hipError_t launch_merge(const XattnParams& p, hipStream_t s);
 // The LDS-streamed MFMA form of the prefill cross-attention (bf16, groups of
 // 4 query heads): a persistent kernel, one workgroup per CU, then the LSE
 // merge.  Its key chunks aim at about kXattnLdsTargetWgs items in all.
 inline bool xattn_lds_applies(Dt dt, int Hq, int Hkv) { return dt == Dt::BF16 && (Hq / Hkv) % 4 == 0; }
 constexpr int64_t kXattnLdsTargetWgs = 512;
+constexpr int kXattnLdsRecPad = 32;   // floats before the values in a partial record
 hipError_t launch_xattn_lds(const XattnParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+// The decode step on the LDS-streamed kernel (bf16, groups of 4 query heads,
+// d = 128): append, the copy and the base token in one streaming pass, then
+// the LSE merge of both kinds (which advances cache_len).  Its key chunks (a
+// multiple of 128 keys) aim at about kXattnLdsDecodeItems items per step, and
+// it is taken only when that gives chunks of at least kXattnLdsDecodeMinChunk
+// keys: smaller steps go to the lane-parallel kernel, whose many resident
+// workgroups hide latency better than a per-CU pipeline with short items.
+constexpr int64_t kXattnLdsDecodeItems = 8192;
+constexpr int kXattnLdsDecodeMinChunk = 1536;
+hipError_t launch_decode_lds(const DecodeParams& p, hipStream_t s);
+// LSE merge of decode partials [B][Hq][2][n_split][rec] into o_out and o,
+// then cache_len[b] += 1 for every valid sequence.
+hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t s);
 
 // Output copies at many positions per sequence (no workspace).
 struct CopiesParams {

@@ -38,10 +38,11 @@
 //     idle most of the time either way), V^T from the transposing LDS read,
 //     online softmax per column in exp2 units with a lazy rescale;
 //   - at an item's last stage the 4 waves' states merge through LDS into one
-//     (max, sum, weighted sum of values) partial per head, in the layout the
-//     LSE merge reads.
+//     (max, sum, weighted sum of values) record per head, in the layout the
+//     LSE merge reads, padded so that the values start on a 128-byte line.
 
 #include <atomic>
+#include <type_traits>
 
 #include "device.h"
 #include "kernels.h"
@@ -50,11 +51,11 @@
 namespace orthros {
 namespace {
 
-constexpr float kMargin = 8.0f;                    // lazy-rescale margin, log2 units
-constexpr int kStageBytes = 65536;                 // one LDS slot
-
 // s_waitcnt lgkmcnt(0) alone: this wave's LDS accesses are done.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+constexpr float kMargin = 8.0f;                    // lazy-rescale margin, log2 units
+constexpr int kStageBytes = 65536;                 // one LDS slot
 
 __device__ __forceinline__ void block_barrier()
 {
@@ -71,15 +72,25 @@ __device__ __forceinline__ int64_t readlane64(int64_t x, int l)
 }
 
 // One item: chunk s of stream j = (KV head g, 4-head block hb) of sequence b,
-// keys lo .. hi (hi <= P, the copy's position), nst stages.
+// keys lo .. hi (hi <= P, the copy's position), nst stages.  In decode, P is
+// the cache length L and `win` marks the chunks that hold keys of the base
+// token's window [wlo, L].
 struct Item {
     int b, g, hb, s, nst;
-    int64_t lo, hi;
+    int64_t lo, hi, wlo;
+    bool win;
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams a, int b0, int nb, PosBlock pos)
+// PT = XattnParams: prefill, the copy's positions by value in `pos`.
+// PT = DecodeParams: a decode step, L = cache_len[b] read on the device (the
+// new token's K/V are already in slot L), and the base token's 4 heads ride
+// along as query columns 4..7 of the same MFMAs (their keys are a subset of
+// the copy's), leaving a second partial per head for the chunks that hold
+// its window.
+template <int D, typename PT>
+__global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, PosBlock pos)
 {
+    constexpr bool DEC = std::is_same<PT, DecodeParams>::value;
     using R = PairTile<D>;
     constexpr int NP = 128 / D * 4;       // pairs per stage: 64 KB
     constexpr int SK = 32 * NP;           // keys per stage
@@ -89,14 +100,17 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams a, int b0, i
     constexpr int LPS = NP * JP;          // direct loads per lane per stage
     constexpr int NQ = D / 32, ND = D / 16;
     constexpr int SLOTE = NP * R::SLOT;   // slot size in bf16 elements
-    // the item's rows in LDS: 4 head rows of each of q_out, alpha_out, beta_out
-    constexpr int NREG = 3;
+    // the item's rows in LDS: 4 head rows of each of q_out, alpha_out,
+    // beta_out (then q, alpha, beta of the base token in decode)
+    constexpr int NREG = DEC ? 6 : 3;
     constexpr int HRE = 4 * D;            // elements per region
-    constexpr int NST = D / 64 + 1;       // partial stores per wave and item
+    constexpr int NST = D / 64 + 1;       // partial store instructions per wave, item and kind
+    constexpr int REC = D + kXattnLdsRecPad, AOFF = kXattnLdsRecPad;   // partial record layout
+    constexpr int NH = DEC ? 8 : 4;       // live query columns
     static_assert(SLOTE * 2 == kStageBytes && LPS == 16, "stage shape");
     __shared__ __align__(16) uint16_t lds[2 * SLOTE];
     __shared__ __align__(16) uint16_t qa[2][NREG * HRE];
-    __shared__ __align__(16) float red[4][4][D + 2];
+    __shared__ __align__(16) float red[4][NH][D + 2];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -107,9 +121,18 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams a, int b0, i
     const uint16_t* v_cache = (const uint16_t*)a.v_cache;
 
     // lane i < nb: sequence b0 + i, its copy position and its item count
-    const int64_t Lv = lane < nb ? pos.v[lane] : -1;
-    const int cnt = lane < nb ? (int)(Lv / a.chunk + 1) * S : 0;
-    if (blockIdx.x == 0 && tid < nb) a.ws_len[b0 + tid] = (int32_t)Lv;
+    int64_t Lv = -1;
+    if constexpr (DEC) {
+        // a length outside [0, max_len] gives the sequence no items (the
+        // merge turns it into NaN outputs and leaves cache_len alone)
+        const int64_t Lraw = lane < nb ? (int64_t)a.cache_len[b0 + lane] : -1;
+        if (blockIdx.x == 0 && tid < nb) a.ws_len[b0 + tid] = (int32_t)Lraw;
+        Lv = Lraw >= 0 && Lraw <= a.max_len ? Lraw : -1;
+    } else {
+        Lv = lane < nb ? pos.v[lane] : -1;
+        if (blockIdx.x == 0 && tid < nb) a.ws_len[b0 + tid] = (int32_t)Lv;
+    }
+    const int cnt = Lv >= 0 ? (int)(Lv / a.chunk + 1) * S : 0;
     int incl = cnt;      // inclusive prefix sum over the lanes
 #pragma unroll
     for (int x = 1; x < 64; x <<= 1) {
@@ -134,6 +157,12 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams a, int b0, i
         it.lo = (int64_t)it.s * a.chunk;
         it.hi = it.lo + a.chunk - 1 < L ? it.lo + a.chunk - 1 : L;
         it.nst = (int)((it.hi - it.lo) / SK) + 1;
+        it.wlo = 0;
+        it.win = false;
+        if constexpr (DEC) {
+            it.wlo = L - a.window + 1 > 0 ? L - a.window + 1 : 0;
+            it.win = it.s >= (int)(it.wlo / a.chunk);
+        }
     };
 
     // byte offset, inside one pair's rows, of the chunk this lane fetches for
@@ -164,15 +193,24 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams a, int b0, i
         }
     };
     // the item's query rows and scale-offsets into qa[q]: region i by wave
-    // i, one load instruction of D / 2 lanes each
-    auto issue_rows = [&](const Item& it, int q) {
-        if (wv >= NREG) return;
+    // i % 4, one load instruction of D / 2 lanes each
+    auto row_src = [&](const Item& it, int r) -> const uint16_t* {
         const int h0 = it.g * (a.Hq / a.Hkv) + it.hb * 4;
-        const uint16_t* src = wv == 0 ? (const uint16_t*)a.q_out + ((int64_t)it.b * a.Hq + h0) * D
-                            : (wv == 1 ? (const uint16_t*)a.alpha_out : (const uint16_t*)a.beta_out) +
-                                  (int64_t)h0 * D;
-        const i32x4 rs = buffer_words(src, HRE * 2);
-        if (lane < HRE / 8) load_lds16(rs, 16 * lane, 0, &qa[q][wv * HRE]);
+        const int64_t qrow = ((int64_t)it.b * a.Hq + h0) * D;
+        if constexpr (DEC) {
+            if (r == 3) return (const uint16_t*)a.q + qrow;
+            if (r == 4) return (const uint16_t*)a.alpha + (int64_t)h0 * D;
+            if (r == 5) return (const uint16_t*)a.beta + (int64_t)h0 * D;
+        }
+        return r == 0 ? (const uint16_t*)a.q_out + qrow
+                      : (r == 1 ? (const uint16_t*)a.alpha_out : (const uint16_t*)a.beta_out) + (int64_t)h0 * D;
+    };
+    auto issue_rows = [&](const Item& it, int q) {
+#pragma unroll
+        for (int r = wv; r < NREG; r += 4) {
+            const i32x4 rs = buffer_words(row_src(it, r), HRE * 2);
+            if (lane < HRE / 8) load_lds16(rs, 16 * lane, 0, &qa[q][r * HRE]);
+        }
     };
 
     int kc = blockIdx.x;          // the item being consumed, and its stage
@@ -198,7 +236,7 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams a, int b0, i
     // rows) of the stage in slot 0 / 1: the stage's wait lets exactly those
     // stay in flight
     int after0 = 0, after1 = 0;
-    const int rows_w = wv < NREG ? 1 : 0;
+    const int rows_w = (NREG - wv + 3) / 4;   // row loads this wave issues
     auto issue_next = [&](int sl) {
         issue(ii, si, sl);
         const int k = LPS + (si == 0 ? rows_w : 0);
@@ -223,7 +261,7 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams a, int b0, i
     float m_run = kNegBig;        // lane (n, .): the running maximum of head n of the block
 
     // one pair of the stage in `slot`: keys key0 .. key0 + 31, the last admissible hi
-    auto attend = [&](const uint16_t* slot, int pp, int64_t key0, int64_t hi) {
+    auto attend = [&](const uint16_t* slot, int pp, int64_t key0, int64_t hi, int64_t wlo, bool win) {
         int ko = pp * R::SLOT + R::kofs(n, gq);
         asm volatile("" : "+v"(ko));
         const uint16_t* kb = slot + ko;
@@ -242,6 +280,19 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams a, int b0, i
             for (int r = 0; r < 4; ++r) {
                 if (r > lim) s0[r] = -INFINITY;
                 if (16 + r > lim) s1[r] = -INFINITY;
+            }
+        }
+        if constexpr (DEC) {
+            // the base token's columns 4..7: keys below its window
+            if (win && key0 < wlo) {
+                const int lim = wlo - key0 < 64 ? (int)(wlo - key0) - 4 * gq : 64;
+                if ((n >> 2) == 1) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (r < lim) s0[r] = -INFINITY;
+                        if (16 + r < lim) s1[r] = -INFINITY;
+                    }
+                }
             }
         }
         float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
@@ -281,17 +332,19 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams a, int b0, i
         // this wave's loads of stage t (and, at an item's first stage, its
         // rows) have landed -- what it issued after them may still be in
         // flight; after the barrier every wave's have
-        wait_stages<1, LPS + 1 + NST>((t & 1) ? after1 : after0);
+        wait_stages<1, LPS + 2 + 4 * NST>((t & 1) ? after1 : after0);
         block_barrier();
         const uint16_t* slot = lds + (t & 1) * SLOTE;
         if (sc == 0) {
             // a new item: its scale-offset queries (times qscale, the score
             // scale with log2(e), so scores come out of the MFMAs in exp2
             // units) as B operands -- lane (n, gq) holds head n of the
-            // block (n < 4; zero otherwise), dims 32 i + 8 gq .. + 7 -- and
-            // fresh softmax states
+            // block (n < 4; in decode, n = 4..7: the base token's head
+            // n - 4 when the item holds keys of its window; zero
+            // otherwise), dims 32 i + 8 gq .. + 7 -- and fresh softmax states
             const float qs = a.qscale;
-            const uint16_t* qr = qa[qc] + (n & 3) * D;
+            const bool live = (n >> 2) == 0 || (DEC && (n >> 2) == 1 && ci.win);
+            const uint16_t* qr = qa[qc] + (DEC && (n >> 2) == 1 ? 3 * HRE : 0) + (n & 3) * D;
 #pragma unroll
             for (int i = 0; i < NQ; ++i) {
                 const int d0 = 32 * i + 8 * gq;
@@ -304,7 +357,7 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams a, int b0, i
                     const uint32_t w = qw[e], aw = av[e], bw = bv[e];
                     r[e] = pack_bf16x2(__builtin_fmaf(bf16_lo(w), bf16_lo(aw), bf16_lo(bw)) * qs,
                                        __builtin_fmaf(bf16_hi(w), bf16_hi(aw), bf16_hi(bw)) * qs);
-                    r[e] = n < 4 ? r[e] : 0u;
+                    r[e] = live ? r[e] : 0u;
                 }
                 qf[i] = __builtin_bit_cast(bf16x8, r);
             }
@@ -317,7 +370,7 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams a, int b0, i
 #pragma unroll
         for (int pp = 0; pp < NP; ++pp) {
             const int64_t key0 = ci.lo + (int64_t)sc * SK + 32 * pp;
-            if ((pp & 3) == wv && key0 <= ci.hi) attend(slot, pp, key0, ci.hi);
+            if ((pp & 3) == wv && key0 <= ci.hi) attend(slot, pp, key0, ci.hi, ci.wlo, ci.win);
         }
         if (++sc < ci.nst) {
             // every wave is done with slot t & 1: stage t + 2 goes there
@@ -327,10 +380,17 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams a, int b0, i
             continue;
         }
 
-        // the item's last stage: merge the 4 waves' states (fixed order)
-        // into its partials out[head][{max, sum, sum of weighted values}];
-        // wave w writes head w of the block with NST store instructions
-        if (n < 4) {
+        // the item's last stage: every wave is done with slot t & 1, so
+        // stage t + 2 goes there first and two stages stay in flight while
+        // the 4 waves' states merge (fixed order) into the item's partial
+        // records (max, sum, 30 unused, weighted values: kXattnLdsRec
+        // floats, so that each store of 64 values covers two whole 128-byte
+        // lines); wave w writes head w of the block with NST store
+        // instructions per kind (decode: the copy, then the base token for
+        // chunks that hold keys of its window)
+        block_barrier();
+        if (more) issue_next(t & 1);
+        if (n < NH) {
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
@@ -344,39 +404,64 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(XattnParams a, int b0, i
         block_barrier();
         {
             const int h0 = ci.g * (a.Hq / a.Hkv) + ci.hb * 4;
-            float* o = a.ws_part + ((int64_t)ci.b * a.Hq + h0 + wv) * a.n_split * (D + 2) +
-                       (int64_t)ci.s * (D + 2);
-            float mw[4], M = kNegBig;
+            const int nkind = DEC && ci.win ? 2 : 1;
+            for (int kind = 0; kind < nkind; ++kind) {
+                const int col = 4 * kind + wv;
+                const int64_t head = (int64_t)ci.b * a.Hq + h0 + wv;
+                float* o = a.ws_part + ((DEC ? 2 * head + kind : head) * a.n_split + ci.s) * REC;
+                float mw[4], M = kNegBig;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                mw[w] = red[w][wv][0];
-                M = fmaxf(M, mw[w]);
+                for (int w = 0; w < 4; ++w) {
+                    mw[w] = red[w][col][0];
+                    M = fmaxf(M, mw[w]);
+                }
+                float f[4];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) f[w] = fast_exp2(mw[w] - M);
+#pragma unroll
+                for (int h = 0; h < D / 64; ++h) {
+                    const int d = lane + 64 * h;
+                    float sum = 0.f;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) sum += f[w] * red[w][col][2 + d];
+                    o[AOFF + d] = sum;
+                }
+                float l = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) l += f[w] * red[w][col][1];
+                if (lane == 0) *(float2*)o = make_float2(M, l);
             }
-            float f[4];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) f[w] = fast_exp2(mw[w] - M);
-#pragma unroll
-            for (int h = 0; h < D / 64; ++h) {
-                const int d = lane + 64 * h;
-                float sum = 0.f;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) sum += f[w] * red[w][wv][2 + d];
-                o[2 + d] = sum;
-            }
-            float l = 0.f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) l += f[w] * red[w][wv][1];
-            if (lane == 0) *(float2*)o = make_float2(M, l);
-            after0 += NST;
-            after1 += NST;
+            after0 += NST * nkind;
+            after1 += NST * nkind;
         }
         kc += nwg;
         if (kc >= total) break;
         item_of(kc, ci);
         sc = 0;
         qc ^= 1;
-        block_barrier();
-        if (more) issue_next(t & 1);
+    }
+}
+
+// Decode: the new base token's K/V rows into slot L = cache_len[b] of each
+// KV head's cache stream (bit-exact copies), one workgroup per sequence.  A
+// length outside [0, max_len] writes nothing (the host guarantees
+// max_len + 1 <= cap, so slot L is inside the cache).
+template <int D>
+__global__ __launch_bounds__(256) void decode_append_kernel(DecodeParams p)
+{
+    const int b = blockIdx.x;
+    const int64_t L = p.cache_len[b];
+    if (L < 0 || L > p.max_len) return;
+    constexpr int UPR = D / 8;                  // 16-byte units per row
+    const int units = p.Hkv * UPR;
+    for (int u = threadIdx.x; u < 2 * units; u += blockDim.x) {
+        const bool isv = u >= units;
+        const int uu = isv ? u - units : u;
+        const int g = uu / UPR, c = uu - g * UPR;
+        const int64_t row = (int64_t)b * p.Hkv + g;
+        const uint4* src = (const uint4*)((const uint16_t*)(isv ? p.v_new : p.k_new) + row * D) + c;
+        uint4* dst = (uint4*)((uint16_t*)(isv ? p.v_cache : p.k_cache) + (row * p.cap + L) * D) + c;
+        *dst = *src;
     }
 }
 
@@ -398,6 +483,7 @@ int cu_count()
 
 hipError_t launch_xattn_lds(const XattnParams& p, hipStream_t st)
 {
+    if (p.rec != p.D + kXattnLdsRecPad) return hipErrorInvalidValue;
     const int hblocks = (p.Hq / p.Hkv) / 4;
     const int ncu = cu_count();
     for (int b0 = 0; b0 < p.B; b0 += kPosPerLaunch) {
@@ -408,13 +494,36 @@ hipError_t launch_xattn_lds(const XattnParams& p, hipStream_t st)
         const int64_t max_items = (int64_t)nb * p.Hkv * hblocks * p.n_split;
         const unsigned grid = (unsigned)(max_items < ncu ? max_items : ncu);
         if (p.D == 64)
-            hipLaunchKernelGGL((xattn_lds_kernel<64>), dim3(grid), dim3(256), 0, st, p, b0, nb, pos);
+            hipLaunchKernelGGL((xattn_lds_kernel<64, XattnParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, pos);
         else
-            hipLaunchKernelGGL((xattn_lds_kernel<128>), dim3(grid), dim3(256), 0, st, p, b0, nb, pos);
+            hipLaunchKernelGGL((xattn_lds_kernel<128, XattnParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, pos);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return launch_merge(p, st);
+}
+
+hipError_t launch_decode_lds(const DecodeParams& p, hipStream_t st)
+{
+    if (p.D != 128 || p.rec != p.D + kXattnLdsRecPad) return hipErrorInvalidValue;
+    // the new token's K/V into slot L first: the streaming kernel reads
+    // every key of [0, L] from the cache
+    hipLaunchKernelGGL((decode_append_kernel<128>), dim3(p.B), dim3(256), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int hblocks = (p.Hq / p.Hkv) / 4;
+    const int ncu = cu_count();
+    PosBlock unused{};
+    for (int b0 = 0; b0 < p.B; b0 += kPosPerLaunch) {
+        const int nb = p.B - b0 < kPosPerLaunch ? p.B - b0 : kPosPerLaunch;
+        // items of this launch, at most (every length at max_len)
+        const int64_t max_items = (int64_t)nb * p.Hkv * hblocks * p.n_split;
+        const unsigned grid = (unsigned)(max_items < ncu ? max_items : ncu);
+        hipLaunchKernelGGL((xattn_lds_kernel<128, DecodeParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, unused);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return launch_decode_merge(p, st);
 }
 
 }  // namespace orthros

@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import assert_parity, bits, say, to_dev
+from gpu_util import assert_parity, bits, say, to_cpu, to_dev
 from phase_aware_swa_amd import inputs
 from phase_aware_swa_amd.runner import Decode, Prefill
 
@@ -57,9 +57,10 @@ def test_decode_steps_parity(Hq, Hkv, d, w, dtype):
 
 @pytest.mark.parametrize("d", [128, 64])
 def test_decode_lengths_at_stage_and_chunk_edges(d):
-    """bf16, 4-head groups (the LDS-streamed kernel): lengths whose new key L
-    is the first or last key of a 128- or 256-key stage and of a 256-key
-    chunk, and one that leaves the last chunk a single key; 3 steps each."""
+    """bf16, 4-head groups, short histories (the lane-parallel kernel):
+    lengths whose new key L is the first or last key of a 128- or 256-key
+    block and of a 256-key chunk, and one that leaves the last chunk a single
+    key; 3 steps each."""
     lens = [0, 127, 128, 255, 256, 511, 1023, 4095]
     steps = 3
     Hq, Hkv, w = 8, 2, 128
@@ -83,13 +84,69 @@ def test_decode_lengths_at_stage_and_chunk_edges(d):
     assert torch.equal(bits(dec.v_cache.cpu()), bits(vc))
 
 
-def test_decode_length_beyond_hint_is_left_alone():
+def test_decode_lds_kernel_long_histories():
+    """bf16, 32/8 heads, d128, w128, 32 sequences with histories up to 70K
+    keys: large enough that the step runs on the LDS-streamed kernel (chunks
+    of about 2200 keys).  Lengths include 0, the edges of a 128-key stage and of a chunk,
+    and a window that straddles a chunk boundary; the unused cache slots hold
+    the NaN sentinel; one sequence's length is past the hint.  Two steps
+    against the oracle, caches and lengths in full."""
+    B, Hq, Hkv, d, w, steps = 32, 32, 8, 128, 128, 2
+    cfg = dict(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=w, dtype=torch.bfloat16,
+               len_lo=66000, len_hi=70000, steps=steps)
+    say("decode lds long histories: generate")
+    x = inputs.decode_inputs(seed=31, device="cuda", **cfg)
+    edges = [0, 1, 127, 128, 4095, 4096, 4100, 8191, 65535, 65536]
+    lens = x["cache_len"].clone()
+    lens[:len(edges)] = torch.tensor(edges, dtype=torch.int32, device="cuda")
+    slot = torch.arange(x["cap"], device="cuda")
+    unused = (slot[None, :] >= lens[:, None].long())[:, None, :].expand(B, Hkv, x["cap"])
+    inputs.fill_sentinel(x["k_cache"], unused)
+    inputs.fill_sentinel(x["v_cache"], unused)
+    # sequence 10 is past the hint: NaN outputs, its cache and length untouched
+    big = 10
+    max_hint = int(torch.cat([lens[:big], lens[big + 1:]]).max()) + steps - 1
+    lens[big] = max_hint + 1
+    x["cache_len"] = lens
+    xc = to_cpu(x)
+    dec = Decode(cfg, x["k_cache"], x["v_cache"], x["cache_len"], max_hint, x["alpha"], x["beta"],
+                 x["alpha_out"], x["beta_out"])
+    from phase_aware_swa_amd import binding
+    from phase_aware_swa_amd.runner import desc_for
+    # the LDS-streamed kernel's workspace: chunks of whole 128-key stages for
+    # about 8192 items, records of d + 32 floats
+    keys = max_hint + 1
+    chunk = -(-(-(-keys * B * Hkv // 8192)) // 128) * 128
+    assert chunk >= 2048
+    n_split = -(-keys // chunk)
+    assert binding.decode_workspace_size(desc_for(cfg), max_hint) == 256 + B * Hq * 2 * n_split * (d + 32) * 4
+    kc, vc, lc = xc["k_cache"], xc["v_cache"], xc["cache_len"].clone()
+    for s in range(steps):
+        say(f"decode lds long histories: step {s}")
+        dec.step(x["q"][s], x["q_out"][s], x["k_new"][s], x["v_new"][s])
+        torch.cuda.synchronize()
+        keep = [t_[big].clone() for t_ in (kc, vc, lc)]
+        lc[big] = 0          # the oracle steps it from an empty history; restored below
+        o, o_out = oracle.decode_step(xc["q"][s], xc["q_out"][s], xc["k_new"][s], xc["v_new"][s], xc["alpha"],
+                                      xc["beta"], xc["alpha_out"], xc["beta_out"], w, kc, vc, lc)
+        kc[big], vc[big], lc[big] = keep
+        ok = torch.arange(B) != big
+        assert_parity(dec.o[ok], o[ok], torch.bfloat16, f"o step {s}")
+        assert_parity(dec.o_out[ok], o_out[ok], torch.bfloat16, f"o_out step {s}")
+        assert torch.isnan(dec.o[big].float()).all() and torch.isnan(dec.o_out[big].float()).all()
+    assert torch.equal(dec.cache_len.cpu(), lc)
+    assert torch.equal(bits(dec.k_cache.cpu()), bits(kc))
+    assert torch.equal(bits(dec.v_cache.cpu()), bits(vc))
+
+
+@pytest.mark.parametrize("Hq", [4, 8], ids=["G2", "G4"])
+def test_decode_length_beyond_hint_is_left_alone(Hq):
     """A sequence whose length exceeds max_len_hint gets NaN outputs, no cache
     write and no length update; the others step normally."""
     lens = [10, 60]
-    xc, cap = small_decode_inputs(2, 4, 2, 128, torch.bfloat16, lens, 1, seed=22)
-    cfg = dict(batch=2, n_q_heads=4, n_kv_heads=2, head_dim=128, window=128, dtype=torch.bfloat16)
-    say("decode beyond hint")
+    xc, cap = small_decode_inputs(2, Hq, 2, 128, torch.bfloat16, lens, 1, seed=22)
+    cfg = dict(batch=2, n_q_heads=Hq, n_kv_heads=2, head_dim=128, window=128, dtype=torch.bfloat16)
+    say(f"decode beyond hint Hq={Hq}")
     x = to_dev(xc)
     dec = Decode(cfg, x["k_cache"], x["v_cache"], x["cache_len"], 40, x["alpha"], x["beta"], x["alpha_out"],
                  x["beta_out"])
