@@ -376,7 +376,13 @@ def main():
                                     "traffic": measured_traffic("traffic_global_xattn_gqa_8b_128k.md"),
                                     "kernel": "orthros_global_xattn (split-K + merge)"}
     if "decode" in out:
-        result["decode_us_per_step"] = out["decode"]["us_per_step"]
+        dd = out["decode"]
+        result["decode_us_per_step"] = dd["us_per_step"]
+        result["roofline_decode"] = {"bound": "hbm", "achieved": dd["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": dd["GBps"] / HBM_PEAK_GBS,
+                                     "traffic": measured_traffic("traffic_decode_gqa_8b_b16.md"),
+                                     "kernel": "orthros_decode_step: decode_append_kernel + "
+                                               "xattn_lds_kernel<128, DecodeParams> + merge_kernel (per step)"}
     result["kernels"] = out
     print(json.dumps(result), flush=True)
 
