@@ -84,19 +84,22 @@ def test_decode_lengths_at_stage_and_chunk_edges(d):
     assert torch.equal(bits(dec.v_cache.cpu()), bits(vc))
 
 
-def test_decode_lds_kernel_long_histories():
+@pytest.mark.parametrize("B,len_lo,len_hi,steps", [(32, 66000, 70000, 2), (80, 20000, 24000, 1)],
+                         ids=["B32-70K", "B80-24K-two-launches"])
+def test_decode_lds_kernel_long_histories(B, len_lo, len_hi, steps):
     """bf16, 32/8 heads, d128, w128, 32 sequences with histories up to 70K
-    keys: large enough that the step runs on the LDS-streamed kernel (chunks
-    of about 2200 keys).  Lengths include 0, the edges of a 128-key stage and of a chunk,
+    keys, or 80 (two launches of 64 and 16 sequences) up to 24K: large
+    enough that the step runs on the LDS-streamed kernel (chunks of about
+    2200 and 1700 keys).  Lengths include 0, the edges of a 128-key stage and of a chunk,
     and a window that straddles a chunk boundary; the unused cache slots hold
     the NaN sentinel; one sequence's length is past the hint.  Two steps
     against the oracle, caches and lengths in full."""
-    B, Hq, Hkv, d, w, steps = 32, 32, 8, 128, 128, 2
+    Hq, Hkv, d, w = 32, 8, 128, 128
     cfg = dict(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=w, dtype=torch.bfloat16,
-               len_lo=66000, len_hi=70000, steps=steps)
+               len_lo=len_lo, len_hi=len_hi, steps=steps)
     say("decode lds long histories: generate")
     x = inputs.decode_inputs(seed=31, device="cuda", **cfg)
-    edges = [0, 1, 127, 128, 4095, 4096, 4100, 8191, 65535, 65536]
+    edges = [0, 1, 127, 128, 4095, 4096, 4100, 8191, len_lo - 1, len_lo]
     lens = x["cache_len"].clone()
     lens[:len(edges)] = torch.tensor(edges, dtype=torch.int32, device="cuda")
     slot = torch.arange(x["cap"], device="cuda")
@@ -117,9 +120,10 @@ def test_decode_lds_kernel_long_histories():
     # about 8192 items, records of d + 32 floats
     keys = max_hint + 1
     chunk = -(-(-(-keys * B * Hkv // 8192)) // 128) * 128
-    assert chunk >= 2048
+    assert chunk >= 1536
     n_split = -(-keys // chunk)
-    assert binding.decode_workspace_size(desc_for(cfg), max_hint) == 256 + B * Hq * 2 * n_split * (d + 32) * 4
+    len_bytes = -(-B * 4 // 256) * 256         # the per-sequence lengths, 256-byte aligned
+    assert binding.decode_workspace_size(desc_for(cfg), max_hint) == len_bytes + B * Hq * 2 * n_split * (d + 32) * 4
     kc, vc, lc = xc["k_cache"], xc["v_cache"], xc["cache_len"].clone()
     for s in range(steps):
         say(f"decode lds long histories: step {s}")
