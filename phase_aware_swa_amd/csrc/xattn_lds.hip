@@ -13,9 +13,11 @@
 //     query heads of the block are served at once, so every K/V byte is read
 //     from HBM once;
 //   - the kernel is persistent: one workgroup per CU walks the items
-//     k = blockIdx, blockIdx + grid, ... of the sequences' concatenated item
-//     lists (each wave holds one sequence per lane and finds an item's
-//     sequence with one ballot over the lanes' prefix sums);
+//     k = blockIdx, blockIdx + grid, ... of an order that lists every
+//     stream's full chunks before the streams' (possibly short) last
+//     chunks, which balances the workgroups' bytes (each wave holds one
+//     sequence per lane and finds an item's sequence with one ballot over
+//     the lanes' prefix sums);
 //   - an item's keys stream through two 64 KB LDS slots in stages of 4
 //     (d = 128) or 8 (d = 64) 32-key pairs, by buffer loads that write LDS
 //     directly (16 per lane per stage, no register staging).  The stage
@@ -132,26 +134,46 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, Po
         Lv = lane < nb ? pos.v[lane] : -1;
         if (blockIdx.x == 0 && tid < nb) a.ws_len[b0 + tid] = (int32_t)Lv;
     }
-    const int cnt = Lv >= 0 ? (int)(Lv / a.chunk + 1) * S : 0;
-    int incl = cnt;      // inclusive prefix sum over the lanes
+    // Item order: every stream's full chunks first (chunks 0 .. nch - 2, by
+    // sequence, stream, chunk), then every stream's last chunk, which may be
+    // short.  Round-robin over that order gives each workgroup an equal
+    // count of full items to within one, and the short last chunks go first
+    // to the workgroups that drew one full item fewer.
+    const int nchv = Lv >= 0 ? (int)(Lv / a.chunk) + 1 : 0;   // chunks per stream of sequence b0 + lane
+    const int cntF = nchv > 0 ? (nchv - 1) * S : 0;
+    const int cntT = nchv > 0 ? S : 0;
+    int inclF = cntF, inclT = cntT;      // inclusive prefix sums over the lanes
 #pragma unroll
     for (int x = 1; x < 64; x <<= 1) {
-        const int t = __shfl_up(incl, x);
-        if (lane >= x) incl += t;
+        const int tf = __shfl_up(inclF, x), tt = __shfl_up(inclT, x);
+        if (lane >= x) {
+            inclF += tf;
+            inclT += tt;
+        }
     }
-    const int excl = incl - cnt;
-    const int total = __builtin_amdgcn_readlane(incl, 63);
+    const int exclF = inclF - cntF, exclT = inclT - cntT;
+    const int nfull = __builtin_amdgcn_readlane(inclF, 63);
+    const int total = nfull + __builtin_amdgcn_readlane(inclT, 63);
     const int nwg = gridDim.x;
 
     auto item_of = [&](int k, Item& it) {
-        const uint64_t m = __ballot(lane < nb && excl <= k);
+        // the item's sequence: the last lane whose exclusive prefix is <= k
+        const bool full = k < nfull;
+        const int kk = full ? k : k - nfull;
+        const uint64_t m = __ballot(lane < nb && (full ? exclF : exclT) <= kk);
         const int bl = __popcll(m) - 1;
         it.b = b0 + bl;
         const int64_t L = readlane64(Lv, bl);
         const int nch = (int)(L / a.chunk) + 1;
-        const int r = k - __builtin_amdgcn_readlane(excl, bl);
-        const int j = r / nch;
-        it.s = r - j * nch;
+        const int r = kk - __builtin_amdgcn_readlane(full ? exclF : exclT, bl);
+        int j;
+        if (full) {
+            j = r / (nch - 1);
+            it.s = r - j * (nch - 1);
+        } else {
+            j = r;
+            it.s = nch - 1;
+        }
         it.g = j / hblocks;
         it.hb = j - it.g * hblocks;
         it.lo = (int64_t)it.s * a.chunk;
