@@ -362,7 +362,13 @@ def main():
                               "kernel": "orthros_prefill: swa_ring_kernel<128, true> (+ merge_kernel)",
                               "algorithmic_bytes": s["bytes"],
                               "mfma_algorithmic_TFLOPs": s["TFLOPs"],
-                              "mfma_algorithmic_frac": s["TFLOPs"] / BF16_PEAK_TFLOPS}
+                              "mfma_algorithmic_frac": s["TFLOPs"] / BF16_PEAK_TFLOPS,
+                              # the attainable roofline min(MFMA peak, intensity x HBM peak) at this
+                              # step's algorithmic intensity, and the fraction of it reached
+                              "intensity_flop_per_byte": s["flops"] / s["bytes"],
+                              "attainable_TFLOPs": min(BF16_PEAK_TFLOPS, s["flops"] / s["bytes"] * HBM_PEAK_GBS / 1e3),
+                              "attainable_frac": s["TFLOPs"] / min(BF16_PEAK_TFLOPS,
+                                                                   s["flops"] / s["bytes"] * HBM_PEAK_GBS / 1e3)}
     if "swa" in out:
         s = out["swa"]
         result["roofline_swa"] = {"bound": "hbm", "achieved": s["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
