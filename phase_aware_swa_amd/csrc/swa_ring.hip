@@ -321,14 +321,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     };
 
-    {   // prologue: the first tile's window, one pair at a time (the halo is not owned)
+    {   // prologue: the first tile's window (the halo pairs are not owned),
+        // every pair's loads in flight at once
+        constexpr int NPRO = (kRingMaxWindow - 1 + 31) / 32 + 1;   // pairs of a window, at most
+        static_assert(NPRO <= NS, "ring slots");
         const int64_t q0 = (int64_t)t_begin * 32;
         const int64_t lo = q0 - W + 1 > 0 ? q0 - W + 1 : 0;
+        const int64_t p0 = lo >> 5, p1 = q0 >> 5;
         load_q(q0 + 16 * sub, qraw);
-        for (int64_t pr = lo >> 5; pr <= (q0 >> 5); ++pr) {
-            load_pair(pr, kreg, vreg);
-            store_pair(pr, pr == (q0 >> 5), kreg, vreg);
-        }
+        u32x4 kp[NPRO][KCH], vp[NPRO][KCH];
+#pragma unroll
+        for (int i = 0; i < NPRO; ++i)
+            if (p0 + i <= p1) load_pair(p0 + i, kp[i], vp[i]);
+#pragma unroll
+        for (int i = 0; i < NPRO; ++i)
+            if (p0 + i <= p1) store_pair(p0 + i, p0 + i == p1, kp[i], vp[i]);
         scale_offset(qraw, qf);
         __syncthreads();
     }
