@@ -84,17 +84,19 @@ def test_decode_lengths_at_stage_and_chunk_edges(d):
     assert torch.equal(bits(dec.v_cache.cpu()), bits(vc))
 
 
-@pytest.mark.parametrize("B,len_lo,len_hi,steps", [(32, 66000, 70000, 2), (80, 20000, 24000, 1)],
-                         ids=["B32-70K", "B80-24K-two-launches"])
-def test_decode_lds_kernel_long_histories(B, len_lo, len_hi, steps):
-    """bf16, 32/8 heads, d128, w128, 32 sequences with histories up to 70K
-    keys, or 80 (two launches of 64 and 16 sequences) up to 24K: large
-    enough that the step runs on the LDS-streamed kernel (chunks of about
-    2200 and 1700 keys).  Lengths include 0, the edges of a 128-key stage and of a chunk,
-    and a window that straddles a chunk boundary; the unused cache slots hold
-    the NaN sentinel; one sequence's length is past the hint.  Two steps
+@pytest.mark.parametrize("B,len_lo,len_hi,steps,w", [(32, 66000, 70000, 2, 128), (80, 20000, 24000, 1, 128),
+                                                   (32, 66000, 70000, 1, 5000)],
+                         ids=["B32-70K", "B80-24K-two-launches", "B32-70K-window-over-chunks"])
+def test_decode_lds_kernel_long_histories(B, len_lo, len_hi, steps, w):
+    """bf16, 32/8 heads, d128: 32 sequences with histories up to 70K keys,
+    or 80 (two launches of 64 and 16 sequences) up to 24K -- large enough
+    that the step runs on the LDS-streamed kernel (chunks of about 2200 and
+    1700 keys).  Lengths include 0 and the edges of a 128-key stage and of a
+    chunk; the base token's window straddles a chunk boundary (w = 128) or
+    spans several chunks (w = 5000).  Unused cache slots hold the NaN
+    sentinel, and one sequence's length is past the hint.  Every step
     against the oracle, caches and lengths in full."""
-    Hq, Hkv, d, w = 32, 8, 128, 128
+    Hq, Hkv, d = 32, 8, 128
     cfg = dict(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=w, dtype=torch.bfloat16,
                len_lo=len_lo, len_hi=len_hi, steps=steps)
     say("decode lds long histories: generate")
