@@ -161,7 +161,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all",
-                    choices=["all", "prefill", "swa", "xattn", "copies", "project", "decode", "layers", "copy"])
+                    choices=["all", "prefill", "swa", "xattn", "copies", "project", "decode", "layers", "copy",
+                             "ceilings"])
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--skip", nargs="*", default=[], choices=["copies", "project", "layers"],
                     help="legs to leave out of a full run (e.g. to keep a profiled run's trace small)")
@@ -187,6 +188,33 @@ def main():
         dst = torch.empty_like(src)
         sec, _ = timed(lambda: dst.copy_(src), args.steps, args.warmup)
         print(json.dumps({"copy_bytes_each_way": n, "copy_GBps": 2 * n * args.steps / sec / 1e9}), flush=True)
+        return
+
+    def practical_ceilings():
+        """HBM rates that plain library kernels reach on this machine over 4 GiB:
+        PyTorch's copy (read + write), a bf16 matrix-vector product (the
+        fastest read-only library stream found: reductions such as sum reach
+        only about 4 TB/s) and fill (write only).  Context for the rooflines,
+        which price against the 8 TB/s vendor figure."""
+        n = 4 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(0)
+        mat = a.view(torch.bfloat16).view(-1, 4096)
+        vec = torch.ones(4096, 1, device="cuda", dtype=torch.bfloat16)
+        out = {}
+        sec, _ = timed(lambda: b.copy_(a), 5, 2)
+        out["copy_read_plus_write_GBps"] = 2 * n * 5 / sec / 1e9
+        sec, _ = timed(lambda: mat @ vec, 5, 2)
+        out["read_only_gemv_GBps"] = n * 5 / sec / 1e9
+        sec, _ = timed(lambda: b.fill_(1), 5, 2)
+        out["write_only_fill_GBps"] = n * 5 / sec / 1e9
+        del a, b, mat, vec
+        torch.cuda.empty_cache()
+        return out
+
+    if args.only == "ceilings":
+        print(json.dumps({"hbm_practical": practical_ceilings()}), flush=True)
         return
 
     cfg = dict(inputs.WORKLOADS["gqa_8b_prefill_128k"])
@@ -389,6 +417,8 @@ def main():
                                      "traffic": measured_traffic("traffic_decode_gqa_8b_b16.md"),
                                      "kernel": "orthros_decode_step: decode_append_kernel + "
                                                "xattn_lds_kernel<128, DecodeParams> + merge_kernel (per step)"}
+    if args.only == "all":
+        result["hbm_practical"] = practical_ceilings()
     result["kernels"] = out
     print(json.dumps(result), flush=True)
 
