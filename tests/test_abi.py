@@ -95,6 +95,36 @@ def test_decode_bad_arguments():
     assert call(cap=100, hint=50, wsb=8) == -6
 
 
+@pytest.mark.parametrize("B,hint,lds", [(16, 132095, True), (4, 32767, False), (1, 4095, False)],
+                         ids=["B16-128K-lds", "B4-32K-lane", "B1-4K-lane"])
+def test_decode_workspace_layout(B, hint, lds):
+    """The decode workspace: 256-byte-aligned lengths, then two kinds of split
+    partials per (sequence, query head).  Long steps (bf16, 4-head groups,
+    d128, at least 1536-key chunks at about 8192 items) take the LDS-streamed
+    kernel's chunks -- a whole number of 128-key stages -- and records of
+    d + 32 floats; shorter ones the lane kernel's power-of-two chunks (>= 256
+    keys, about 8192 workgroups) and records of d + 2 floats.  A workspace one
+    byte short is rejected before anything runs."""
+    Hq, Hkv, d = 32, 8, 128
+    desc = mk(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=128, dtype=binding.BF16)
+    keys, streams = hint + 1, B * Hkv
+    want = -(-keys * streams // 8192)
+    if lds:
+        assert want >= 1536
+        chunk, rec = -(-want // 128) * 128, d + 32
+    else:
+        chunk, rec = 256, d + 2
+        while chunk < want:
+            chunk *= 2
+    n_split = -(-keys // chunk)
+    need = -(-B * 4 // 256) * 256 + B * Hq * 2 * n_split * rec * 4
+    assert binding.decode_workspace_size(desc, hint) == need
+    p = ctypes.c_void_p(FAKE)
+    st = binding.lib().orthros_decode_step(ctypes.byref(desc), p, p, p, p, p, p, p, p, p, p, hint + 1, p, hint, p, p,
+                                           p, need - 1, None)
+    assert st == -6
+
+
 def test_workspace_sizes():
     d = mk()
     w1 = binding.prefill_workspace_size(d, 1000)
