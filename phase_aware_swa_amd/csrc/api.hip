@@ -78,7 +78,7 @@ int64_t streams_of(const orthros_desc* d)
 }
 
 constexpr int64_t kPrefillTargetWgs = 2048;
-constexpr int64_t kDecodeTargetWgs = 8192;
+constexpr int64_t kDecodeTargetWgs = 16384;
 constexpr size_t kLenBytesAlign = 256;
 
 size_t len_bytes(const orthros_desc* d)

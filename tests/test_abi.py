@@ -103,7 +103,7 @@ def test_decode_workspace_layout(B, hint, lds):
     d128, at least 1536-key chunks at about 8192 items) take the LDS-streamed
     kernel's chunks -- a whole number of 128-key stages -- and records of
     d + 32 floats; shorter ones the lane kernel's power-of-two chunks (>= 256
-    keys, about 8192 workgroups) and records of d + 2 floats.  A workspace one
+    keys, about 16384 workgroups) and records of d + 2 floats.  A workspace one
     byte short is rejected before anything runs."""
     Hq, Hkv, d = 32, 8, 128
     desc = mk(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=128, dtype=binding.BF16)
@@ -114,7 +114,7 @@ def test_decode_workspace_layout(B, hint, lds):
         chunk, rec = -(-want // 128) * 128, d + 32
     else:
         chunk, rec = 256, d + 2
-        while chunk < want:
+        while chunk < -(-keys * streams // 16384):
             chunk *= 2
     n_split = -(-keys // chunk)
     need = -(-B * 4 // 256) * 256 + B * Hq * 2 * n_split * rec * 4
