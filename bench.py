@@ -155,6 +155,27 @@ def cpu_baseline(cfg, x_dev, one_thread_rows=128):
                       f"one thread: Eq. (4) for {one_thread_rows} tokens x {Hq} heads"}
 
 
+def cpu_baseline_decode(cfg, xd, len0, steps=2):
+    """The fp64 oracle on the decode workload: `steps` consecutive steps
+    from the starting lengths (every sequence's base token over its window
+    and its copy over the whole history), on this machine's host cores."""
+    import oracle
+    kc, vc = xd["k_cache"].cpu(), xd["v_cache"].cpu()
+    lc = len0.cpu().to(dtype=len0.dtype).clone()
+    a = {k: xd[k].cpu() for k in ("alpha", "beta", "alpha_out", "beta_out")}
+    nthreads = oracle.default_threads()
+    s = time.perf_counter()
+    for i in range(steps):
+        oracle.decode_step(xd["q"][i].cpu(), xd["q_out"][i].cpu(), xd["k_new"][i].cpu(), xd["v_new"][i].cpu(),
+                           a["alpha"], a["beta"], a["alpha_out"], a["beta_out"], cfg["window"], kc, vc, lc,
+                           nthreads=nthreads)
+    t = (time.perf_counter() - s) / steps
+    return {"value": t * 1e6, "unit": "us/step", "cores": nthreads, "kind": "oracle",
+            "sample": f"fp64 oracle, {nthreads} threads, the first {steps} steps of the workload (batch "
+                      f"{cfg['batch']}, every sequence's window and whole-history copy), "
+                      f"{t:.2f} s per step"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -372,6 +393,8 @@ def main():
         out["decode"] = {"workload": "gqa_8b_decode_b16", "us_per_step": us, "steps": nsteps,
                          "bytes_per_step": step_bytes, "GBps": step_bytes / (us * 1e-6) / 1e9,
                          "p50_us": per[len(per) // 2], "p99_us": per[min(len(per) - 1, (99 * len(per)) // 100)]}
+        if args.only == "all" and not args.no_cpu_baseline:
+            out["decode"]["cpu_baseline"] = cpu_baseline_decode(dcfg, xd, len0)
         if result is None:
             result = {"metric": METRIC, "value": us, "unit": "us/step", "n_gpus": 1, "steps": nsteps,
                       "warmup": 1, "ms_per_step": us / 1e3, "higher_is_better": False, "scaling": "weak",
