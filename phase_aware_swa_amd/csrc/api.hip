@@ -135,14 +135,16 @@ Split decode_split(const orthros_desc* d, int64_t max_len)
 {
     Split s;
     const int64_t keys = max_len + 1;
-    // the LDS-streamed kernel: about kXattnLdsDecodeItems items, chunks a
-    // whole number of 128-key stages
+    // the LDS-streamed kernel: about kXattnLdsDecodeItems items, the chunk
+    // the power of two nearest (geometrically) to what that asks for
     int64_t want = (keys * streams_of(d) + orthros::kXattnLdsDecodeItems - 1) / orthros::kXattnLdsDecodeItems;
     want = want < (int64_t(1) << 24) ? want : (int64_t(1) << 24);
     const bool lds = orthros::xattn_lds_applies(dt_of(d), d->n_q_heads, d->n_kv_heads) && d->head_dim == 128 &&
                      want >= orthros::kXattnLdsDecodeMinChunk;
+    int64_t lds_chunk = 1024;
+    while (lds_chunk * 3 / 2 < want) lds_chunk <<= 1;
     s.lds = lds;
-    s.chunk = lds ? (int)((want + 127) / 128 * 128) : pick_chunk(keys, streams_of(d), kDecodeTargetWgs);
+    s.chunk = lds ? (int)lds_chunk : pick_chunk(keys, streams_of(d), kDecodeTargetWgs);
     s.n_split = (int)((keys + s.chunk - 1) / s.chunk);
     s.rec = d->head_dim + (lds ? orthros::kXattnLdsRecPad : 2);
     s.bytes = len_bytes(d) + (size_t)d->batch * d->n_q_heads * 2 * s.n_split * s.rec * 4;

@@ -112,9 +112,9 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 // The decode step on the LDS-streamed kernel (bf16, groups of 4 query heads,
 // d = 128): append, the copy and the base token in one streaming pass, then
 // the LSE merge of both kinds (which advances cache_len).  Its key chunks (a
-// multiple of 128 keys) aim at about kXattnLdsDecodeItems items per step, and
-// it is taken only when that gives chunks of at least kXattnLdsDecodeMinChunk
-// keys: smaller steps go to the lane-parallel kernel, whose many resident
+// power of two, at least 2048 keys) aim at about kXattnLdsDecodeItems items
+// per step, and it is taken only when that asks for chunks of at least
+// kXattnLdsDecodeMinChunk keys: smaller steps go to the lane-parallel kernel, whose many resident
 // workgroups hide latency better than a per-CU pipeline with short items.
 constexpr int64_t kXattnLdsDecodeItems = 8192;
 constexpr int kXattnLdsDecodeMinChunk = 1536;

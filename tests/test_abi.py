@@ -101,7 +101,7 @@ def test_decode_workspace_layout(B, hint, lds):
     """The decode workspace: 256-byte-aligned lengths, then two kinds of split
     partials per (sequence, query head).  Long steps (bf16, 4-head groups,
     d128, at least 1536-key chunks at about 8192 items) take the LDS-streamed
-    kernel's chunks -- a whole number of 128-key stages -- and records of
+    kernel's chunks -- the power of two nearest that -- and records of
     d + 32 floats; shorter ones the lane kernel's power-of-two chunks (>= 256
     keys, about 16384 workgroups) and records of d + 2 floats.  A workspace one
     byte short is rejected before anything runs."""
@@ -111,7 +111,9 @@ def test_decode_workspace_layout(B, hint, lds):
     want = -(-keys * streams // 8192)
     if lds:
         assert want >= 1536
-        chunk, rec = -(-want // 128) * 128, d + 32
+        chunk, rec = 1024, d + 32
+        while chunk * 3 // 2 < want:
+            chunk *= 2
     else:
         chunk, rec = 256, d + 2
         while chunk < -(-keys * streams // 16384):

@@ -90,8 +90,7 @@ def test_decode_lengths_at_stage_and_chunk_edges(d):
 def test_decode_lds_kernel_long_histories(B, len_lo, len_hi, steps, w):
     """bf16, 32/8 heads, d128: 32 sequences with histories up to 70K keys,
     or 80 (two launches of 64 and 16 sequences) up to 24K -- large enough
-    that the step runs on the LDS-streamed kernel (chunks of about 2200 and
-    1700 keys).  Lengths include 0 and the edges of a 128-key stage and of a
+    that the step runs on the LDS-streamed kernel (2048-key chunks).  Lengths include 0 and the edges of a 128-key stage and of a
     chunk; the base token's window straddles a chunk boundary (w = 128) or
     spans several chunks (w = 5000).  Unused cache slots hold the NaN
     sentinel, and one sequence's length is past the hint.  Every step
@@ -118,11 +117,14 @@ def test_decode_lds_kernel_long_histories(B, len_lo, len_hi, steps, w):
                  x["alpha_out"], x["beta_out"])
     from phase_aware_swa_amd import binding
     from phase_aware_swa_amd.runner import desc_for
-    # the LDS-streamed kernel's workspace: chunks of whole 128-key stages for
-    # about 8192 items, records of d + 32 floats
+    # the LDS-streamed kernel's workspace: power-of-two chunks for about 8192
+    # items, records of d + 32 floats
     keys = max_hint + 1
-    chunk = -(-(-(-keys * B * Hkv // 8192)) // 128) * 128
-    assert chunk >= 1536
+    want = -(-keys * B * Hkv // 8192)
+    assert want >= 1536
+    chunk = 1024
+    while chunk * 3 // 2 < want:
+        chunk *= 2
     n_split = -(-keys // chunk)
     len_bytes = -(-B * 4 // 256) * 256         # the per-sequence lengths, 256-byte aligned
     assert binding.decode_workspace_size(desc_for(cfg), max_hint) == len_bytes + B * Hq * 2 * n_split * (d + 32) * 4
