@@ -84,18 +84,22 @@ def test_decode_lengths_at_stage_and_chunk_edges(d):
     assert torch.equal(bits(dec.v_cache.cpu()), bits(vc))
 
 
-@pytest.mark.parametrize("B,len_lo,len_hi,steps,w", [(32, 66000, 70000, 2, 128), (80, 20000, 24000, 1, 128),
-                                                   (32, 66000, 70000, 1, 5000)],
-                         ids=["B32-70K", "B80-24K-two-launches", "B32-70K-window-over-chunks"])
-def test_decode_lds_kernel_long_histories(B, len_lo, len_hi, steps, w):
-    """bf16, 32/8 heads, d128: 32 sequences with histories up to 70K keys,
+@pytest.mark.parametrize("B,Hq,len_lo,len_hi,steps,w", [(32, 32, 66000, 70000, 2, 128),
+                                                      (80, 32, 20000, 24000, 1, 128),
+                                                      (32, 32, 66000, 70000, 1, 5000),
+                                                      (16, 64, 66000, 70000, 1, 128)],
+                         ids=["B32-70K", "B80-24K-two-launches", "B32-70K-window-over-chunks",
+                              "B16-70K-G8-two-head-blocks"])
+def test_decode_lds_kernel_long_histories(B, Hq, len_lo, len_hi, steps, w):
+    """bf16, 8 KV heads, d128: 32 sequences (32 query heads) with histories
+    up to 70K keys, 16 with 64 query heads (two 4-head blocks per KV head),
     or 80 (two launches of 64 and 16 sequences) up to 24K -- large enough
     that the step runs on the LDS-streamed kernel (2048-key chunks).  Lengths include 0 and the edges of a 128-key stage and of a
     chunk; the base token's window straddles a chunk boundary (w = 128) or
     spans several chunks (w = 5000).  Unused cache slots hold the NaN
     sentinel, and one sequence's length is past the hint.  Every step
     against the oracle, caches and lengths in full."""
-    Hq, Hkv, d = 32, 8, 128
+    Hkv, d = 8, 128
     cfg = dict(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=w, dtype=torch.bfloat16,
                len_lo=len_lo, len_hi=len_hi, steps=steps)
     say("decode lds long histories: generate")
@@ -120,7 +124,7 @@ def test_decode_lds_kernel_long_histories(B, len_lo, len_hi, steps, w):
     # the LDS-streamed kernel's workspace: power-of-two chunks for about 8192
     # items, records of d + 32 floats
     keys = max_hint + 1
-    want = -(-keys * B * Hkv // 8192)
+    want = -(-keys * B * Hkv * (Hq // Hkv // 4) // 8192)
     assert want >= 1536
     chunk = 1024
     while chunk * 3 // 2 < want:
