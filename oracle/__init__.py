@@ -57,6 +57,8 @@ def lib():
         L.oracle_prefill.restype = ctypes.c_int
         L.oracle_swa_rows.argtypes = [sp, i64] + [vp] * 5 + [i64, vp, vp]
         L.oracle_swa_rows.restype = ctypes.c_int
+        L.oracle_swa_rows_given_q.argtypes = [sp, i64] + [vp] * 5 + [i64, vp, vp]
+        L.oracle_swa_rows_given_q.restype = ctypes.c_int
         L.oracle_decode_step.argtypes = [sp] + [vp] * 10 + [i64, vp, vp, vp]
         L.oracle_copies.argtypes = [sp, i64, i64] + [vp] * 6 + [i64, vp]
         L.oracle_copies.restype = ctypes.c_int
@@ -136,6 +138,24 @@ def swa_rows(q, k, v, alpha, beta, window, rows, softmax_scale=None, nthreads=No
                                rows.shape[0], _p(rows), _p(out))
     if rc != 0:
         raise ValueError("oracle_swa_rows rejected its arguments")
+    return out
+
+
+def swa_rows_given_q(qrows, k, v, alpha, beta, window, rows, n_q_heads, softmax_scale=None, nthreads=None):
+    """Eq. (4) at selected rows whose raw queries are given row by row.
+
+    qrows [n, d] (row u is the base-stream query of rows[u] = (b, t, h));
+    k, v [B,T,Hkv,d].  Same result as swa_rows on a full q holding those
+    rows."""
+    B, T, Hkv, d = k.shape
+    rows = torch.as_tensor(rows, dtype=torch.int64).contiguous()
+    assert qrows.shape == (rows.shape[0], d) and qrows.is_contiguous()
+    out = torch.zeros(rows.shape[0], d, dtype=torch.float64)
+    s = make_shape(B, n_q_heads, Hkv, d, window, k.dtype, softmax_scale, nthreads)
+    rc = lib().oracle_swa_rows_given_q(ctypes.byref(s), T, _p(qrows), _p(k), _p(v), _p(alpha), _p(beta),
+                                       rows.shape[0], _p(rows), _p(out))
+    if rc != 0:
+        raise ValueError("oracle_swa_rows_given_q rejected its arguments")
     return out
 
 

@@ -334,6 +334,45 @@ int oracle_swa_rows(const oracle_shape* s, int64_t T, const void* q,
     return 0;
 }
 
+/* Unit = listed row u whose raw query is qrows[u] (not read from a full q). */
+static void rows_given_q_unit(void* p, int64_t u)
+{
+    rows_ctx* c = (rows_ctx*)p;
+    const oracle_shape* s = c->s;
+    int Hq = s->n_q_heads, Hkv = s->n_kv_heads, d = s->head_dim;
+    int64_t b = c->rows[3 * u], t = c->rows[3 * u + 1];
+    int h = (int)c->rows[3 * u + 2], g = h / (Hq / Hkv);
+    double qh[512];
+    scale_offset(c->q, u * d, c->alpha, c->beta, h, d, s->dtype, qh);
+    int64_t lo = t - s->window + 1;
+    if (lo < 0) lo = 0;
+    attend(qh, d, s->softmax_scale, c->k, c->v, s->dtype,
+           (b * c->T * Hkv + g) * d, (int64_t)Hkv * d, lo, t, c->out + u * d);
+}
+
+/*
+ * Eq. (4) for a list of (b, t, h) rows whose raw queries are passed row by
+ * row (qrows [n_rows][d], in the storage type) instead of as a full
+ * [B][T][Hq][d] tensor; k, v and the result as in oracle_swa_rows.  The
+ * arithmetic is that of oracle_swa_rows, row for row.
+ */
+int oracle_swa_rows_given_q(const oracle_shape* s, int64_t T, const void* qrows,
+                            const void* k, const void* v, const void* alpha,
+                            const void* beta, int64_t n_rows, const int64_t* rows,
+                            double* out)
+{
+    if (!s || s->head_dim > 512 || s->n_kv_heads < 1 ||
+        s->n_q_heads % s->n_kv_heads || s->window < 1)
+        return -1;
+    for (int64_t u = 0; u < n_rows; ++u)
+        if (rows[3 * u] < 0 || rows[3 * u] >= s->batch || rows[3 * u + 1] < 0 ||
+            rows[3 * u + 1] >= T || rows[3 * u + 2] < 0 || rows[3 * u + 2] >= s->n_q_heads)
+            return -1;
+    rows_ctx c = {s, T, qrows, k, v, alpha, beta, rows, out};
+    parallel_for(s->nthreads, n_rows, rows_given_q_unit, &c);
+    return 0;
+}
+
 /* -------------------------------------------------------------- decode */
 
 typedef struct {

@@ -6,6 +6,8 @@ Parity bar (element by element against the fp64 oracle):
   fp32 storage: max-abs <= 1e-4 and relative L2 <= 1e-4
 Cache bytes, untouched slots, lengths and mask placement: bit-exact.
 """
+import json
+import os
 import sys
 
 import torch
@@ -22,18 +24,42 @@ def say(*a):
     sys.stdout.flush()
 
 
-def errors(gpu, ref):
-    g = gpu.detach().to("cpu", torch.float64)
-    r = ref.to(torch.float64)
-    assert torch.isfinite(g).all(), "non-finite values in the GPU output"
-    d = g - r
-    max_abs = d.abs().max().item() if d.numel() else 0.0
-    rel = (d.norm() / r.norm()).item() if r.norm() > 0 else d.norm().item()
+def errors(gpu, ref, chunk=1 << 24):
+    """(max-abs, relative L2) of gpu against ref, accumulated in fp64 over
+    slices of the first dimension so that full-size outputs need no fp64
+    copy of their own."""
+    g_all = gpu.detach()
+    n = g_all.shape[0] if g_all.dim() else 1
+    per = max(1, g_all[0].numel() if g_all.dim() else 1)
+    step = max(1, chunk // per)
+    max_abs, dsq, rsq = 0.0, 0.0, 0.0
+    for i in range(0, n, step):
+        g = (g_all[i:i + step] if g_all.dim() else g_all).to("cpu", torch.float64)
+        r = (ref[i:i + step] if ref.dim() else ref).to(torch.float64)
+        assert torch.isfinite(g).all(), "non-finite values in the GPU output"
+        d = g - r
+        if d.numel():
+            max_abs = max(max_abs, d.abs().max().item())
+        dsq += float((d * d).sum())
+        rsq += float((r * r).sum())
+    rel = (dsq ** 0.5) / (rsq ** 0.5) if rsq > 0 else dsq ** 0.5
     return max_abs, rel
 
 
-def assert_parity(gpu, ref, dtype, what=""):
+def record(case, what, max_abs, rel, n):
+    """Appends one parity result to the JSON-lines file named by
+    ORTHROS_PARITY_LOG (nothing when it is unset)."""
+    path = os.environ.get("ORTHROS_PARITY_LOG")
+    if not path:
+        return
+    with open(path, "a") as f:
+        f.write(json.dumps(dict(case=case, output=what, max_abs=max_abs, rel_l2=rel, elements=n)) + "\n")
+
+
+def assert_parity(gpu, ref, dtype, what="", case=None):
     max_abs, rel = errors(gpu, ref)
+    if case:
+        record(case, what, max_abs, rel, int(ref.numel()))
     tol_abs, tol_rel = TOL[dtype]
     assert max_abs <= tol_abs and rel <= tol_rel, (
         f"{what}: max-abs {max_abs:.3e} (<= {tol_abs}) rel-L2 {rel:.3e} (<= {tol_rel})")

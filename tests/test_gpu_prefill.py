@@ -14,7 +14,7 @@ def make_cfg(B, Hq, Hkv, d, w, dtype):
     return dict(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=w, dtype=dtype)
 
 
-def run_case(cfg, T, seed, out_pos=None, cap_extra=0, check_cache=True):
+def run_case(cfg, T, seed, out_pos=None, cap_extra=0, check_cache=True, case=None):
     cfg = {k: v for k, v in cfg.items() if k not in ("T", "kind")}
     say(f"prefill case {cfg} T={T} seed={seed} out_pos={out_pos} cap_extra={cap_extra}")
     xc = inputs.prefill_inputs(T=T, seed=seed, **cfg)
@@ -25,8 +25,8 @@ def run_case(cfg, T, seed, out_pos=None, cap_extra=0, check_cache=True):
     run.run()
     torch.cuda.synchronize()
     ref = oracle_prefill(xc, cfg["window"], cap=T + cap_extra)
-    assert_parity(run.o, ref["o"], cfg["dtype"], "o")
-    assert_parity(run.o_out, ref["o_out"], cfg["dtype"], "o_out")
+    assert_parity(run.o, ref["o"], cfg["dtype"], "o", case=case)
+    assert_parity(run.o_out, ref["o_out"], cfg["dtype"], "o_out", case=case)
     if check_cache:
         assert torch.equal(bits(run.k_cache.cpu()), bits(ref["k_cache"]))
         assert torch.equal(bits(run.v_cache.cpu()), bits(ref["v_cache"]))
@@ -77,13 +77,13 @@ def test_copy_masked_by_original_position(dtype):
 def test_tiny_fp32_workload():
     """Full parity at the tiny fp32 workload (B1, 4/4 heads, d64, T2048, w128)."""
     cfg = dict(inputs.WORKLOADS["tiny_fp32_prefill"])
-    run_case(cfg, cfg["T"], seed=0, cap_extra=64)
+    run_case(cfg, cfg["T"], seed=0, cap_extra=64, case="tiny_fp32_prefill")
 
 
 def test_mha_1p3b_8k_workload():
     """Full parity at the 1.3B-class MHA workload (B1, 16/16, d128, T8192, w128, bf16)."""
     cfg = dict(inputs.WORKLOADS["mha_1p3b_prefill_8k"])
-    run_case(cfg, cfg["T"], seed=1, cap_extra=64)
+    run_case(cfg, cfg["T"], seed=1, cap_extra=64, case="mha_1p3b_prefill_8k")
 
 
 def test_run_to_run_identical():

@@ -415,3 +415,42 @@ def test_swa_rows_match_full_prefill():
     out = oracle.swa_rows(x["q"], x["k"], x["v"], x["alpha"], x["beta"], 9, rows)
     for i, (b, tt, h) in enumerate(rows.tolist()):
         assert torch.equal(out[i], r["o"][b, tt, h])
+
+
+def test_swa_rows_given_q_match_full_prefill():
+    """Rows whose queries are passed one by one give the full call's rows bit
+    for bit (a row paired with the wrong query or head would not)."""
+    x = rand_case(2, 70, 4, 2, 16, seed=19, dtype=torch.bfloat16)
+    r = run_oracle(x, window=9)
+    rows = torch.tensor([[0, 0, 0], [1, 69, 3], [0, 8, 1], [1, 9, 2], [0, 40, 3], [1, 40, 0]])
+    qrows = torch.stack([x["q"][b, t, h] for b, t, h in rows.tolist()]).contiguous()
+    out = oracle.swa_rows_given_q(qrows, x["k"], x["v"], x["alpha"], x["beta"], 9, rows, n_q_heads=4)
+    for i, (b, tt, h) in enumerate(rows.tolist()):
+        assert torch.equal(out[i], r["o"][b, tt, h])
+
+
+def test_probe_closed_form_counts():
+    """The mask probes' closed form (tests/probe_util.py) against brute
+    force: residue counts of key intervals, and exact bf16 ratios."""
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    from probe_util import assert_probe, residue_counts
+    for m, d in ((127, 128), (127, 64)):
+        for lo in range(0, 260, 37):
+            for hi in range(lo - 1, lo + 300, 41):
+                for sh in (0, 5, 126):
+                    c = residue_counts(torch.tensor(lo), torch.tensor(hi), torch.tensor(sh), m, d)
+                    ref = torch.zeros(d, dtype=torch.int64)
+                    for j in range(lo, hi + 1):
+                        if (j + sh) % m < d:
+                            ref[(j + sh) % m] += 1
+                    assert torch.equal(c, ref), (m, d, lo, hi, sh)
+    # a window of 128 keys over V = one-hot (j mod 127): 2/128 and 1/128 exactly
+    cnt = residue_counts(torch.tensor([500]), torch.tensor([627]), torch.tensor([0]), 127, 128)
+    vals = (cnt.double() / 128).bfloat16()
+    assert assert_probe(vals, cnt, torch.tensor([128]), "closed form") == 0
+    assert sorted(set(vals.float()[0].tolist())) == [0.0, 1 / 128, 2 / 128]
+    bad = vals.clone()
+    bad[0, 3] = (cnt[0, 3].double() / 129).bfloat16()
+    with pytest.raises(AssertionError):
+        assert_probe(bad, cnt, torch.tensor([128]), "a key too many")
