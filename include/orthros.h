@@ -37,13 +37,16 @@
  *   - Ownership: the caller owns every buffer, including the KV cache, the
  *     lengths and the workspace.  The library allocates nothing, frees
  *     nothing and never synchronises: work is queued on `stream` (a
- *     hipStream_t; NULL is the null stream) and the call returns.
+ *     hipStream_t; NULL is the null stream) and the call returns.  (The one
+ *     exception to "the caller owns": orthros_decode_step_noalloc keeps its
+ *     partials in a scratch array the library holds on each device.)
  *   - Outputs must not alias inputs; k_cache/v_cache must not alias k/v.
  *   - Errors: arguments are validated on the host before anything is
  *     queued; a negative status means nothing was launched.  ORTHROS_E_HIP
  *     reports a failed launch; orthros_last_error() then holds the text.
  *   - Thread safety: calls may be made from several host threads; the only
- *     global state is the per-thread error text.
+ *     global state is the per-thread error text and, for
+ *     orthros_decode_step_noalloc, one scratch array per device (below).
  */
 #ifndef ORTHROS_H
 #define ORTHROS_H
@@ -260,6 +263,37 @@ orthros_status orthros_decode_step(const orthros_desc* desc,
                                    int32_t* cache_len, int64_t max_len_hint,
                                    void* o, void* o_out,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * orthros_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments (minus workspace
+ * and workspace_bytes), same kernels, same results bit for bit.
+ *
+ * The split-K partials live instead in a scratch array of 64 MiB that the
+ * library holds on every GPU it runs on (a device global, loaded with the
+ * library's code and kept until the process ends).  Nothing is allocated or
+ * freed per call.  The first call on a device looks the array's address up
+ * (hipGetSymbolAddress) with that device current; a caller about to
+ * capture can make one call before the capture so that no lookup happens
+ * inside it.
+ *
+ * Limits and errors: a step whose workspace (orthros_decode_workspace_size
+ * of desc and max_len_hint) exceeds 64 MiB is rejected with
+ * ORTHROS_E_WORKSPACE before anything is queued (the batch-16 step with
+ * 128K-key histories needs about 43 MB).  Every call on one GPU shares that
+ * GPU's array, which keeps the last call's contents; each step writes what
+ * it reads, so no clearing is needed, but calls that can overlap on one GPU
+ * (other streams, other host threads) race on it: serialise them.
+ */
+orthros_status orthros_decode_step_noalloc(const orthros_desc* desc,
+                                           const void* q, const void* q_out,
+                                           const void* k_new, const void* v_new,
+                                           const void* alpha, const void* beta,
+                                           const void* alpha_out, const void* beta_out,
+                                           void* k_cache, void* v_cache, int64_t cap,
+                                           int32_t* cache_len, int64_t max_len_hint,
+                                           void* o, void* o_out, void* stream);
 
 /* ------------------------------------------------------------ utilities */
 

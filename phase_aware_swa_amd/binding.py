@@ -63,6 +63,9 @@ def lib():
         L.orthros_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, vp, vp, vp,
                                           sz, vp]
         L.orthros_decode_step.restype = ctypes.c_int
+        L.orthros_decode_step_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, vp,
+                                                  vp, vp]
+        L.orthros_decode_step_noalloc.restype = ctypes.c_int
         L.orthros_copies.argtypes = [dp, i64, i64, vp, vp, vp, vp, vp, vp, i64, vp, vp]
         L.orthros_copies.restype = ctypes.c_int
         L.orthros_project.argtypes = [dp, i64, i64, i64] + [vp] * 13 + [i64, vp]
@@ -146,6 +149,16 @@ def decode_step(desc, q, q_out, k_new, v_new, alpha, beta, alpha_out, beta_out, 
         _ptr(alpha_out), _ptr(beta_out), _ptr(k_cache), _ptr(v_cache),
         k_cache.shape[2] if k_cache is not None else 0, _ptr(cache_len), max_len_hint, _ptr(o), _ptr(o_out),
         _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def decode_step_noalloc(desc, q, q_out, k_new, v_new, alpha, beta, alpha_out, beta_out, k_cache, v_cache,
+                        cache_len, max_len_hint, o, o_out, stream=None):
+    """orthros_decode_step_noalloc: the decode step on the library's own scratch (no workspace)."""
+    _check(lib().orthros_decode_step_noalloc(
+        ctypes.byref(desc), _ptr(q), _ptr(q_out), _ptr(k_new), _ptr(v_new), _ptr(alpha), _ptr(beta),
+        _ptr(alpha_out), _ptr(beta_out), _ptr(k_cache), _ptr(v_cache),
+        k_cache.shape[2] if k_cache is not None else 0, _ptr(cache_len), max_len_hint, _ptr(o), _ptr(o_out),
+        _stream(stream)))
 
 
 def copies(desc, T, q_out, out_pos, alpha_out, beta_out, k_cache, v_cache, o_out, stream=None):

@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
@@ -260,6 +261,77 @@ orthros_status run_xattn(const orthros_desc* d, int64_t T, const void* q_out, co
     return hip_status(orthros::launch_xattn(p, s), "cross-attention kernel launch");
 }
 
+orthros_status validate_decode(const orthros_desc* desc, const void* q, const void* q_out, const void* k_new,
+                               const void* v_new, const void* alpha, const void* beta, const void* alpha_out,
+                               const void* beta_out, const void* k_cache, const void* v_cache, int64_t cap,
+                               const int32_t* cache_len, int64_t max_len_hint, const void* o, const void* o_out)
+{
+    orthros_status st = check_desc(desc);
+    if (st) return st;
+    if (max_len_hint < 0 || max_len_hint >= INT32_MAX)
+        return fail(ORTHROS_E_SHAPE, "max_len_hint %lld outside [0, 2^31 - 1)", (long long)max_len_hint);
+    if (cap < max_len_hint + 1)
+        return fail(ORTHROS_E_CAPACITY, "cap %lld < max_len_hint + 1 = %lld", (long long)cap,
+                    (long long)max_len_hint + 1);
+    const int64_t rowq = (int64_t)desc->n_q_heads * desc->head_dim;
+    if ((int64_t)desc->batch * cap > kMaxElems / rowq)
+        return fail(ORTHROS_E_SHAPE, "cache size overflows the library's 2^50-element bound");
+    return check_ptrs({q, q_out, k_new, v_new, alpha, beta, alpha_out, beta_out, k_cache, v_cache, cache_len, o,
+                       o_out});
+}
+
+orthros_status run_decode(const orthros_desc* desc, const Split& sp, const void* q, const void* q_out,
+                          const void* k_new, const void* v_new, const void* alpha, const void* beta,
+                          const void* alpha_out, const void* beta_out, void* k_cache, void* v_cache, int64_t cap,
+                          int32_t* cache_len, int64_t max_len_hint, void* o, void* o_out, void* workspace,
+                          hipStream_t stream)
+{
+    orthros::DecodeParams p;
+    p.q = q; p.q_out = q_out; p.k_new = k_new; p.v_new = v_new;
+    p.alpha = alpha; p.beta = beta; p.alpha_out = alpha_out; p.beta_out = beta_out;
+    p.k_cache = k_cache; p.v_cache = v_cache; p.cache_len = cache_len; p.o = o; p.o_out = o_out;
+    p.ws_len = (int32_t*)workspace;
+    p.ws_part = (float*)((char*)workspace + len_bytes(desc));
+    p.cap = cap; p.max_len = max_len_hint;
+    p.B = desc->batch; p.Hq = desc->n_q_heads; p.Hkv = desc->n_kv_heads; p.D = desc->head_dim;
+    p.window = desc->window;
+    p.chunk = sp.chunk; p.n_split = sp.n_split; p.rec = sp.rec; p.lds = sp.lds ? 1 : 0;
+    p.qscale = qscale_of(desc);
+    p.dt = dt_of(desc);
+    return hip_status(orthros::launch_decode(p, stream), "decode kernel launch");
+}
+
+// Scratch of the allocation-free decode entry point: the per-step lengths
+// and split-K partials that orthros_decode_step keeps in the caller's
+// workspace.  Every step writes what it reads later in the same step, so
+// nothing needs clearing between calls.  In host code `scratch` only names
+// the variable; its device address (one copy per GPU) comes from
+// hipGetSymbolAddress, looked up once per device on that device's first call.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+orthros_status scratch_of_current_device(void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ORTHROS_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(ORTHROS_E_HIP, "device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(ORTHROS_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return ORTHROS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -398,37 +470,37 @@ orthros_status orthros_decode_step(const orthros_desc* desc, const void* q, cons
                                    void* workspace, size_t workspace_bytes, void* stream)
 {
     g_err.clear();
-    orthros_status st = check_desc(desc);
+    orthros_status st = validate_decode(desc, q, q_out, k_new, v_new, alpha, beta, alpha_out, beta_out, k_cache,
+                                        v_cache, cap, cache_len, max_len_hint, o, o_out);
     if (st) return st;
-    if (max_len_hint < 0 || max_len_hint >= INT32_MAX)
-        return fail(ORTHROS_E_SHAPE, "max_len_hint %lld outside [0, 2^31 - 1)", (long long)max_len_hint);
-    if (cap < max_len_hint + 1)
-        return fail(ORTHROS_E_CAPACITY, "cap %lld < max_len_hint + 1 = %lld", (long long)cap,
-                    (long long)max_len_hint + 1);
-    const int64_t rowq = (int64_t)desc->n_q_heads * desc->head_dim;
-    if ((int64_t)desc->batch * cap > kMaxElems / rowq)
-        return fail(ORTHROS_E_SHAPE, "cache size overflows the library's 2^50-element bound");
     if (!workspace) return fail(ORTHROS_E_WORKSPACE, "workspace is NULL");
-    if ((st = check_ptrs({q, q_out, k_new, v_new, alpha, beta, alpha_out, beta_out, k_cache, v_cache,
-                          cache_len, o, o_out, workspace})))
-        return st;
+    if ((st = check_ptrs({workspace}))) return st;
     const Split sp = decode_split(desc, max_len_hint);
     if (workspace_bytes < sp.bytes)
         return fail(ORTHROS_E_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, sp.bytes);
+    return run_decode(desc, sp, q, q_out, k_new, v_new, alpha, beta, alpha_out, beta_out, k_cache, v_cache, cap,
+                      cache_len, max_len_hint, o, o_out, workspace, (hipStream_t)stream);
+}
 
-    orthros::DecodeParams p;
-    p.q = q; p.q_out = q_out; p.k_new = k_new; p.v_new = v_new;
-    p.alpha = alpha; p.beta = beta; p.alpha_out = alpha_out; p.beta_out = beta_out;
-    p.k_cache = k_cache; p.v_cache = v_cache; p.cache_len = cache_len; p.o = o; p.o_out = o_out;
-    p.ws_len = (int32_t*)workspace;
-    p.ws_part = (float*)((char*)workspace + len_bytes(desc));
-    p.cap = cap; p.max_len = max_len_hint;
-    p.B = desc->batch; p.Hq = desc->n_q_heads; p.Hkv = desc->n_kv_heads; p.D = desc->head_dim;
-    p.window = desc->window;
-    p.chunk = sp.chunk; p.n_split = sp.n_split; p.rec = sp.rec; p.lds = sp.lds ? 1 : 0;
-    p.qscale = qscale_of(desc);
-    p.dt = desc->dtype == ORTHROS_F32 ? orthros::Dt::F32 : orthros::Dt::BF16;
-    return hip_status(orthros::launch_decode(p, (hipStream_t)stream), "decode kernel launch");
+orthros_status orthros_decode_step_noalloc(const orthros_desc* desc, const void* q, const void* q_out,
+                                           const void* k_new, const void* v_new, const void* alpha,
+                                           const void* beta, const void* alpha_out, const void* beta_out,
+                                           void* k_cache, void* v_cache, int64_t cap, int32_t* cache_len,
+                                           int64_t max_len_hint, void* o, void* o_out, void* stream)
+{
+    g_err.clear();
+    orthros_status st = validate_decode(desc, q, q_out, k_new, v_new, alpha, beta, alpha_out, beta_out, k_cache,
+                                        v_cache, cap, cache_len, max_len_hint, o, o_out);
+    if (st) return st;
+    const Split sp = decode_split(desc, max_len_hint);
+    if (sp.bytes > kScratchBytes)
+        return fail(ORTHROS_E_WORKSPACE, "this step needs %zu bytes of scratch, more than the %zu bytes the "
+                    "allocation-free entry point holds (use orthros_decode_step with a workspace)", sp.bytes,
+                    kScratchBytes);
+    void* ws = nullptr;
+    if ((st = scratch_of_current_device(&ws))) return st;
+    return run_decode(desc, sp, q, q_out, k_new, v_new, alpha, beta, alpha_out, beta_out, k_cache, v_cache, cap,
+                      cache_len, max_len_hint, o, o_out, ws, (hipStream_t)stream);
 }
 
 const char* orthros_status_str(int status)

@@ -203,3 +203,26 @@ def test_project_accepts_optional_pointers():
     ever launched on these fake pointers."""
     assert project_call(mk(), T_out=0, x_out=0, q_out=0, alpha=FAKE + 4, beta=FAKE + 4) == -8
     assert project_call(mk(), alpha=0, beta=0, alpha_out=FAKE + 4, beta_out=FAKE + 4) == -8
+
+
+def test_decode_noalloc_rejects_without_touching_the_gpu():
+    """The allocation-free decode step validates like orthros_decode_step and
+    refuses a step whose partials exceed its 64 MiB scratch array, before
+    any HIP call (so this runs without a GPU)."""
+    L = binding.lib()
+    p = ctypes.c_void_p(FAKE)
+    call = lambda d, cap, hint: L.orthros_decode_step_noalloc(ctypes.byref(d), p, p, p, p, p, p, p, p, p, p, cap, p,
+                                                              hint, p, p, None)
+    d = mk()
+    assert call(d, cap=100, hint=100) == -5
+    assert call(d, cap=100, hint=-1) == -2
+    assert call(mk(head_dim=96), cap=100, hint=50) == -2
+    big = mk(batch=2048, n_q_heads=32, n_kv_heads=8, head_dim=128)      # 2048 sequences of 1K keys
+    hint = 1000
+    assert binding.decode_workspace_size(big, hint) > 64 << 20
+    assert call(big, cap=hint + 1, hint=hint) == -6
+    assert b"scratch" in L.orthros_last_error()
+    # the 1024-step batch-16 workload (128K-key histories) fits, and so does batch 64
+    for B in (16, 64):
+        assert binding.decode_workspace_size(mk(batch=B, n_q_heads=32, n_kv_heads=8, head_dim=128),
+                                             131072 + 1023) <= 64 << 20
