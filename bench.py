@@ -9,26 +9,40 @@ tokens per second (B * T / time per step).  The decode step latency
 (batch 16, lengths U[8192, 131072], 1024 steps) is reported beside it.
 
 Timing: warm-up calls, then K calls bracketed by torch.cuda.synchronize()
-and HIP events on the stream the kernels run on.  The roofline figure is
-for the step's dominant kernel, the fused streaming kernel: the step's
-algorithmic bytes over the step time (the merge that follows it in the
-same call takes a few microseconds of that).  The separate entry points
-orthros_swa_prefill and orthros_global_xattn are timed too, as a
-breakdown.  The fp64 CPU oracle is timed on a bounded sample of the same
-workload on this machine's host cores (cpu_baseline).
+and HIP events on the stream the kernels run on (the library queues its
+work on torch's current stream).  The roofline figure is for the step's
+dominant kernel, the fused streaming kernel: the step's algorithmic bytes
+over the step time (the merge that follows it in the same call takes a few
+microseconds of that).  The separate entry points orthros_swa_prefill and
+orthros_global_xattn are timed too, as a breakdown.  The fp64 CPU oracle is
+timed on the same workload on this machine's host cores (cpu_baseline).
+
+Every other workload the library is checked on gets its own leg in
+`configs` (rate, algorithmic GB/s and MFMA TFLOP/s, fractions of the
+vendor peaks, and the oracle's time on this host, measured in full or
+extrapolated from a measured part and labelled so):
+
+  tiny_fp32_prefill     fp32, B1, 4/4 heads, d64, T2048 (a parity workload)
+  mha_1p3b_prefill_8k   bf16, B1, 16/16 heads (MHA), d128, T8192
+  gqa_8b_prefill_128k   the headline step above
+  gqa_8b_prefill_1m     bf16, B1, 32/8, d128, T2^20, 36 layers whose caches
+                        (144 GiB) stay resident: the 36-layer total and the
+                        per-layer rate
+  gqa_8b_decode_b16     the decode step
 
 The projections either side of the attention (orthros_project: the shared
 W_Q over the base and copy rows, K/V written into the cache; d_model 4096)
-are timed over the same 128K batch as an MFMA-bound breakdown leg.
+are timed over the same 128K batch as an MFMA-bound leg, the many-copy
+modes (orthros_copies) at an SFT span and a PT sequence, and the
+multi-layer decode step over 36 resident layers, eager and as one captured
+HIP graph.  hbm_practical measures what plain streaming kernels reach on
+this GPU (library copy / GEMV / fill, and the read and copy kernels of
+libhbmprobe.so swept over unroll and grid sizes).
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W]
-                  [--only prefill|swa|xattn|copies|project|decode|layers|copy]
-
-The multi-layer decode leg (layers) runs one decode step over a stack of 36
-resident layers (batch 4, lengths U[8192, 32768]; and batch 1, lengths
-U[1024, 4096], where launches matter), eager and as one captured HIP graph.
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--only LEG] [--skip LEG ...]
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -42,6 +56,8 @@ METRIC = "prefill attn tokens/s at 128K (SWA w=128 + 1 global query); decode us/
 PROFILES = os.path.join(ROOT, "profiles")
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
+LEGS = ["prefill", "swa", "xattn", "tiny", "mha8k", "prefill1m", "copies", "project", "layers", "decode"]
 
 
 def swa_bytes(B, T, Hq, Hkv, d, es=2):
@@ -63,16 +79,21 @@ def prefill_bytes(B, T, Hq, Hkv, d, es=2):
     return swa_bytes(B, T, Hq, Hkv, d, es) + 2 * B * Hq * d * es
 
 
+def xattn_bytes(B, pos_plus_1, Hkv, d, es=2):
+    """Algorithmic bytes of the copy's global read: K and V of keys [0, P]."""
+    return B * pos_plus_1 * Hkv * d * 2 * es
+
+
+def prefill_flops(B, T, Hq, d, w):
+    """SWA flops plus the copy's 4 d flops per key per query head."""
+    return swa_flops(B, T, Hq, d, w) + 4 * d * B * Hq * T
+
+
 def project_flops(c):
     """Algorithmic flops of orthros_project: 2 d_model per output element;
     base rows against W_Q, W_K and W_V, copy rows against W_Q."""
     nq, nk = c["n_q_heads"] * c["head_dim"], c["n_kv_heads"] * c["head_dim"]
     return 2 * c["d_model"] * c["batch"] * (c["T"] * (nq + 2 * nk) + c["T_out"] * nq)
-
-
-def xattn_bytes(B, pos_plus_1, Hkv, d, es=2):
-    """Algorithmic bytes of the copy's global read: K and V of keys [0, P]."""
-    return B * pos_plus_1 * Hkv * d * 2 * es
 
 
 def measured_traffic(summary):
@@ -123,11 +144,24 @@ def cpu_model():
     return "unknown"
 
 
+def hbm_fracs(nbytes, flops, sec, peak_tflops=BF16_PEAK_TFLOPS):
+    """Algorithmic GB/s and TFLOP/s of `sec` seconds, with the fractions of
+    the vendor peaks and of the attainable roofline min(P, I x BW)."""
+    gbs = nbytes / sec / 1e9
+    tfl = flops / sec / 1e12
+    attain = min(peak_tflops, flops / nbytes * HBM_PEAK_GBS / 1e3)
+    return {"GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "TFLOPs": tfl, "mfma_frac": tfl / peak_tflops,
+            "intensity_flop_per_byte": flops / nbytes, "attainable_TFLOPs": attain,
+            "attainable_frac": tfl / attain}
+
+
+# ---------------------------------------------------------------- oracle legs
+
 def cpu_baseline(cfg, x_dev, one_thread_rows=128):
     """The fp64 oracle on the whole workload (Eq. (4) for every token and
-    head, the cache, and each sequence's global query over all its keys),
-    about 10 s on 16 host threads; plus the Eq. (4) rate of a single thread
-    on a short run of rows."""
+    head, the cache, and each sequence's global query over all its keys) on
+    this host's cores; plus the Eq. (4) rate of a single thread on a short
+    run of rows."""
     import torch
 
     import oracle
@@ -143,23 +177,62 @@ def cpu_baseline(cfg, x_dev, one_thread_rows=128):
                    x_dev["beta_out"].cpu(), w, nthreads=nthreads)
     t_all = time.perf_counter() - s
     t0 = T // 2
-    rows = torch.tensor([(0, t, h) for t in range(t0, t0 + one_thread_rows) for h in range(Hq)])
+    n1 = min(one_thread_rows, T - t0)
+    rows = torch.tensor([(0, t, h) for t in range(t0, t0 + n1) for h in range(Hq)])
     s = time.perf_counter()
     oracle.swa_rows(q[:1], k[:1], v[:1], a, b, w, rows, nthreads=1)
-    t_row1 = (time.perf_counter() - s) / one_thread_rows            # seconds per token, 1 thread
+    t_row1 = (time.perf_counter() - s) / n1            # seconds per token, 1 thread
     return {"value": B * T / t_all, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "cpu_model": cpu_model(),
+            "seconds": t_all, "extrapolated": False, "cpu_model": cpu_model(),
             "one_thread_swa_tokens_per_s": 1.0 / t_row1,
             "sample": f"fp64 oracle, {nthreads} threads, the whole workload (B={B} x T={T}: Eq. (4) for every "
-                      f"token x {Hq} heads, the cache, and the global query over all {T} keys) in {t_all:.1f} s; "
-                      f"one thread: Eq. (4) for {one_thread_rows} tokens x {Hq} heads"}
+                      f"token x {Hq} heads, the cache, and the global query over all {T} keys) in {t_all:.2f} s; "
+                      f"one thread: Eq. (4) for {n1} tokens x {Hq} heads"}
 
 
-def cpu_baseline_decode(cfg, xd, len0, steps=2):
-    """The fp64 oracle on the decode workload: `steps` consecutive steps
-    from the starting lengths (every sequence's base token over its window
-    and its copy over the whole history), on this machine's host cores."""
+def cpu_baseline_1m(cfg, x_dev, n_rows=2048):
+    """The fp64 oracle on one layer of the 1M workload, measured in part and
+    extrapolated: the global query over all 2^20 keys (in full), and Eq. (4)
+    on n_rows consecutive mid-sequence tokens x every head, scaled to all T
+    tokens; the 36-layer figure is 36 such layers."""
+    import torch
+
     import oracle
+    B, T, Hq, d, w, L = (cfg[k] for k in ("batch", "T", "n_q_heads", "head_dim", "window", "layers"))
+    nthreads = oracle.default_threads()
+    k = x_dev["k"].cpu()
+    v = x_dev["v"].cpu()
+    ab = [x_dev[n].cpu() for n in ("alpha", "beta", "alpha_out", "beta_out")]
+    kc = torch.empty(B, k.shape[2], T, d, dtype=k.dtype)
+    vc = torch.empty_like(kc)
+    s = time.perf_counter()
+    oracle.prefill(None, x_dev["q_out"].cpu(), [T - 1] * B, k, v, *ab, w, swa=False, k_cache=kc, v_cache=vc,
+                   nthreads=nthreads)
+    t_glob = time.perf_counter() - s
+    t0 = T // 2
+    ts = torch.arange(t0, t0 + n_rows)
+    qrows = x_dev["q"][0, ts.cuda()].reshape(-1, d).cpu()
+    rows = torch.stack([torch.zeros_like(ts).repeat_interleave(Hq), ts.repeat_interleave(Hq),
+                        torch.arange(Hq).repeat(n_rows)], dim=1)
+    s = time.perf_counter()
+    oracle.swa_rows_given_q(qrows, k, v, ab[0], ab[1], w, rows, n_q_heads=Hq, nthreads=nthreads)
+    t_rows = time.perf_counter() - s
+    per_layer = t_glob + t_rows / n_rows * T * B
+    return {"value": B * T * L / (per_layer * L), "unit": "tokens/s (per layer)", "cores": nthreads,
+            "kind": "oracle", "extrapolated": True, "seconds_per_layer": per_layer,
+            "seconds_36_layers": per_layer * L, "cpu_model": cpu_model(),
+            "sample": f"fp64 oracle, {nthreads} threads, one layer: the global query over all {T} keys x {Hq} heads "
+                      f"measured in full ({t_glob:.2f} s, the cache copy included) and Eq. (4) measured on "
+                      f"{n_rows} tokens x {Hq} heads ({t_rows:.2f} s), extrapolated to {T} tokens and to {L} layers"}
+
+
+def cpu_baseline_decode(cfg, xd, len0, steps=8):
+    """The fp64 oracle on the decode workload: a contiguous block of `steps`
+    steps from the starting lengths (every sequence's base token over its
+    window and its copy over the whole history), on this machine's host
+    cores, extrapolated to the workload's step count."""
+    import oracle
+    steps = min(steps, xd["q"].shape[0])
     kc, vc = xd["k_cache"].cpu(), xd["v_cache"].cpu()
     lc = len0.cpu().to(dtype=len0.dtype).clone()
     a = {k: xd[k].cpu() for k in ("alpha", "beta", "alpha_out", "beta_out")}
@@ -170,22 +243,78 @@ def cpu_baseline_decode(cfg, xd, len0, steps=2):
                            a["alpha"], a["beta"], a["alpha_out"], a["beta_out"], cfg["window"], kc, vc, lc,
                            nthreads=nthreads)
     t = (time.perf_counter() - s) / steps
-    return {"value": t * 1e6, "unit": "us/step", "cores": nthreads, "kind": "oracle",
-            "sample": f"fp64 oracle, {nthreads} threads, the first {steps} steps of the workload (batch "
-                      f"{cfg['batch']}, every sequence's window and whole-history copy), "
-                      f"{t:.2f} s per step"}
+    total = cfg["steps"]
+    return {"value": t * 1e6, "unit": "us/step", "cores": nthreads, "kind": "oracle", "extrapolated": True,
+            "measured_steps": steps, "seconds_all_steps_extrapolated": t * total, "cpu_model": cpu_model(),
+            "sample": f"fp64 oracle, {nthreads} threads, the first {steps} consecutive steps of the workload "
+                      f"(batch {cfg['batch']}, every sequence's window and whole-history copy) measured, "
+                      f"{t:.2f} s per step; the {total}-step total ({t * total:.0f} s) is extrapolated from them"}
 
+
+# ------------------------------------------------------------ practical HBM
+
+def practical_ceilings():
+    """HBM rates plain streaming kernels reach on this GPU over 4 GiB:
+    PyTorch's copy (read + write), a bf16 matrix-vector product (read) and
+    fill (write); and the hand-written read and copy kernels of
+    libhbmprobe.so, swept over unroll (16-byte loads in flight per lane) and
+    grid size, best of the sweep.  Context for the rooflines, which price
+    against the 8 TB/s vendor figure."""
+    import torch
+    n = 4 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    mat = a.view(torch.bfloat16).view(-1, 4096)
+    vec = torch.ones(4096, 1, device="cuda", dtype=torch.bfloat16)
+    out = {}
+    sec, _ = timed(lambda: b.copy_(a), 5, 2)
+    out["torch_copy_read_plus_write_GBps"] = 2 * n * 5 / sec / 1e9
+    sec, _ = timed(lambda: mat @ vec, 5, 2)
+    out["torch_gemv_read_GBps"] = n * 5 / sec / 1e9
+    sec, _ = timed(lambda: b.fill_(1), 5, 2)
+    out["torch_fill_write_GBps"] = n * 5 / sec / 1e9
+    lib = ctypes.CDLL(os.path.join(ROOT, "phase_aware_swa_amd", "libhbmprobe.so"))
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.hbm_probe_read.argtypes = [vp, i64, vp, ci, ci, vp]
+    lib.hbm_probe_copy.argtypes = [vp, vp, i64, ci, ci, vp]
+    grids = (1024, 2048, 4096, 8192)
+    sink = torch.empty(max(grids) * 256, dtype=torch.int32, device="cuda")
+    stream = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = {"read": (0.0, None), "copy": (0.0, None)}
+    half = n // 2
+    for unroll in (4, 8, 16):
+        for grid in grids:
+            def rd():
+                assert lib.hbm_probe_read(a.data_ptr(), n, sink.data_ptr(), unroll, grid, stream()) == 0
+
+            def cp():
+                assert lib.hbm_probe_copy(b.data_ptr(), a.data_ptr(), half, unroll, grid, stream()) == 0
+            sec, _ = timed(rd, 5, 1)
+            r = n * 5 / sec / 1e9
+            if r > best["read"][0]:
+                best["read"] = (r, f"unroll {unroll}, grid {grid}")
+            sec, _ = timed(cp, 5, 1)
+            r = 2 * half * 5 / sec / 1e9
+            if r > best["copy"][0]:
+                best["copy"] = (r, f"unroll {unroll}, grid {grid}")
+    out["probe_read_GBps"], out["probe_read_best_launch"] = best["read"]
+    out["probe_copy_read_plus_write_GBps"], out["probe_copy_best_launch"] = best["copy"]
+    del a, b, mat, vec, sink
+    torch.cuda.empty_cache()
+    return out
+
+
+# ------------------------------------------------------------------- main
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", default="all",
-                    choices=["all", "prefill", "swa", "xattn", "copies", "project", "decode", "layers", "copy",
-                             "ceilings"])
+    ap.add_argument("--only", default="all", choices=["all", "copy", "ceilings"] + LEGS)
     ap.add_argument("--decode-steps", type=int, default=1024)
-    ap.add_argument("--skip", nargs="*", default=[], choices=["copies", "project", "layers"],
+    ap.add_argument("--skip", nargs="*", default=[], choices=LEGS + ["ceilings"],
                     help="legs to leave out of a full run (e.g. to keep a profiled run's trace small)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -200,7 +329,10 @@ def main():
     from phase_aware_swa_amd.runner import Copies, Decode, LayerStack, Prefill, Project
 
     torch.cuda.set_device(0)
-    out = {}
+    out, configs = {}, {}
+    cpu_ok = not args.no_cpu_baseline
+    run_leg = lambda leg: (args.only in ("all", leg)) and leg not in args.skip
+    progress = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)
 
     if args.only == "copy":
         # plain copy kernel of known size: calibrates the FETCH_SIZE / WRITE_SIZE counters
@@ -210,30 +342,6 @@ def main():
         sec, _ = timed(lambda: dst.copy_(src), args.steps, args.warmup)
         print(json.dumps({"copy_bytes_each_way": n, "copy_GBps": 2 * n * args.steps / sec / 1e9}), flush=True)
         return
-
-    def practical_ceilings():
-        """HBM rates that plain library kernels reach on this machine over 4 GiB:
-        PyTorch's copy (read + write), a bf16 matrix-vector product (the
-        fastest read-only library stream found: reductions such as sum reach
-        only about 4 TB/s) and fill (write only).  Context for the rooflines,
-        which price against the 8 TB/s vendor figure."""
-        n = 4 << 30
-        a = torch.empty(n, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        a.fill_(0)
-        mat = a.view(torch.bfloat16).view(-1, 4096)
-        vec = torch.ones(4096, 1, device="cuda", dtype=torch.bfloat16)
-        out = {}
-        sec, _ = timed(lambda: b.copy_(a), 5, 2)
-        out["copy_read_plus_write_GBps"] = 2 * n * 5 / sec / 1e9
-        sec, _ = timed(lambda: mat @ vec, 5, 2)
-        out["read_only_gemv_GBps"] = n * 5 / sec / 1e9
-        sec, _ = timed(lambda: b.fill_(1), 5, 2)
-        out["write_only_fill_GBps"] = n * 5 / sec / 1e9
-        del a, b, mat, vec
-        torch.cuda.empty_cache()
-        return out
-
     if args.only == "ceilings":
         print(json.dumps({"hbm_practical": practical_ceilings()}), flush=True)
         return
@@ -241,16 +349,17 @@ def main():
     cfg = dict(inputs.WORKLOADS["gqa_8b_prefill_128k"])
     B, T, Hq, Hkv, d, w = (cfg[k] for k in ("batch", "T", "n_q_heads", "n_kv_heads", "head_dim", "window"))
     result = None
-    if args.only in ("all", "prefill", "swa", "xattn"):
+    if run_leg("prefill") or run_leg("swa") or run_leg("xattn"):
+        progress("gqa_8b_prefill_128k")
         x = inputs.prefill_inputs(seed=2, device="cuda", **cfg)
         run = Prefill(cfg, x)
         run.run()
         torch.cuda.synchronize()
-        if args.only in ("all", "prefill"):
+        if run_leg("prefill"):
             sec, wall = timed(run.run, args.steps, args.warmup)
             ms = sec / args.steps * 1e3
             nbytes = prefill_bytes(B, T, Hq, Hkv, d)
-            fl = swa_flops(B, T, Hq, d, w) + 4 * d * B * Hq * T
+            fl = prefill_flops(B, T, Hq, d, w)
             out["prefill"] = {"kernel": "orthros_prefill", "us": ms * 1e3, "bytes": nbytes, "flops": fl,
                               "GBps": nbytes / (ms * 1e-3) / 1e9, "TFLOPs": fl / (ms * 1e-3) / 1e12}
             result = {"metric": METRIC, "value": B * T * args.steps / sec, "unit": "tokens/s", "n_gpus": 1,
@@ -260,27 +369,96 @@ def main():
                                  "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d, "window": w,
                                  "parallelism": "single-gpu"},
                       "wall_s_timed": wall}
-        if args.only in ("all", "prefill", "swa"):
+            configs["gqa_8b_prefill_128k"] = {"us_per_call": ms * 1e3, "tokens_per_s": B * T / (ms * 1e-3),
+                                              **hbm_fracs(nbytes, fl, ms * 1e-3)}
+        if run_leg("swa"):
             sec, _ = timed(run.run_swa, args.steps, args.warmup)
             t_swa = sec / args.steps
             nbytes = swa_bytes(B, T, Hq, Hkv, d)
             fl = swa_flops(B, T, Hq, d, w)
             out["swa"] = {"kernel": "orthros_swa_prefill", "us": t_swa * 1e6, "bytes": nbytes, "flops": fl,
                           "GBps": nbytes / t_swa / 1e9, "TFLOPs": fl / t_swa / 1e12}
-        if args.only in ("all", "prefill", "xattn"):
+        if run_leg("xattn"):
             sec, _ = timed(run.run_xattn, args.steps, args.warmup)
             t_x = sec / args.steps
             nbytes = xattn_bytes(B, T, Hkv, d)
             out["xattn"] = {"kernel": "orthros_global_xattn", "us": t_x * 1e6, "bytes": nbytes,
                             "GBps": nbytes / t_x / 1e9}
-        if result is not None and not args.no_cpu_baseline:
+        if result is not None and cpu_ok:
+            progress("gqa_8b_prefill_128k: oracle")
             result["cpu_baseline"] = cpu_baseline(cfg, x)
+            configs["gqa_8b_prefill_128k"]["cpu_baseline"] = result["cpu_baseline"]
         del run, x
         torch.cuda.empty_cache()
 
-    if args.only in ("all", "copies") and "copies" not in args.skip:
+    for leg, name in (("tiny", "tiny_fp32_prefill"), ("mha8k", "mha_1p3b_prefill_8k")):
+        if not run_leg(leg):
+            continue
+        progress(name)
+        c = dict(inputs.WORKLOADS[name])
+        cB, cT, cHq, cHkv, cd, cw = (c[k] for k in ("batch", "T", "n_q_heads", "n_kv_heads", "head_dim", "window"))
+        es = 4 if c["dtype"] == torch.float32 else 2
+        x = inputs.prefill_inputs(seed=1, device="cuda", **c)
+        run = Prefill(c, x)
+        n = max(50, args.steps * 10)
+        sec, _ = timed(run.run, n, args.warmup)
+        t = sec / n
+        nbytes = prefill_bytes(cB, cT, cHq, cHkv, cd, es)
+        fl = prefill_flops(cB, cT, cHq, cd, cw)
+        peak = FP32_PEAK_TFLOPS if es == 4 else BF16_PEAK_TFLOPS
+        configs[name] = {"us_per_call": t * 1e6, "tokens_per_s": cB * cT / t, "dtype": "f32" if es == 4 else "bf16",
+                         "kernels": "swa_f32_kernel + xattn_split_kernel + merge_kernel" if es == 4 else
+                                    "swa_bf16_kernel + xattn_split_kernel + merge_kernel",
+                         "bytes": nbytes, "flops": fl, **hbm_fracs(nbytes, fl, t, peak),
+                         "note": f"{nbytes / 2**20:.0f} MiB per call: much of it can be served from the 256 MB "
+                                 "last-level cache between back-to-back calls, so GB/s is an effective rate"}
+        if cpu_ok:
+            configs[name]["cpu_baseline"] = cpu_baseline(c, x)
+        del run, x
+        torch.cuda.empty_cache()
+
+    if run_leg("prefill1m"):
+        # 36 layers whose caches all stay resident; each layer's inputs are
+        # drawn (untimed) before its timed call
+        c = dict(inputs.WORKLOADS["gqa_8b_prefill_1m"])
+        cT, nl = c["T"], c["layers"]
+        progress(f"gqa_8b_prefill_1m: {nl} resident caches")
+        kc_all = torch.empty(nl, 1, c["n_kv_heads"], cT, c["head_dim"], dtype=torch.bfloat16, device="cuda")
+        vc_all = torch.empty_like(kc_all)
+        times = []
+        for layer in range(nl):
+            x = inputs.prefill_inputs(seed=1000 + layer, device="cuda", **c)
+            run = Prefill(c, x, k_cache=kc_all[layer], v_cache=vc_all[layer])
+            if layer == 0:
+                run.run()                          # warm-up call
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run.run()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / 1e3)
+            if layer < nl - 1:
+                del run, x
+        total = sum(times)
+        per = total / nl
+        nbytes = prefill_bytes(1, cT, c["n_q_heads"], c["n_kv_heads"], c["head_dim"])
+        fl = prefill_flops(1, cT, c["n_q_heads"], c["head_dim"], c["window"])
+        configs["gqa_8b_prefill_1m"] = {"layers": nl, "ms_36_layers": total * 1e3, "ms_per_layer": per * 1e3,
+                                        "ms_per_layer_min": min(times) * 1e3, "ms_per_layer_max": max(times) * 1e3,
+                                        "tokens_per_s_per_layer": cT / per, "tokens_per_s_36_layers": cT / total,
+                                        "bytes_per_layer": nbytes, "flops_per_layer": fl,
+                                        **hbm_fracs(nbytes, fl, per)}
+        if cpu_ok:
+            progress("gqa_8b_prefill_1m: oracle (one layer, extrapolated)")
+            configs["gqa_8b_prefill_1m"]["cpu_baseline"] = cpu_baseline_1m(c, x)
+        del run, x, kc_all, vc_all
+        torch.cuda.empty_cache()
+
+    if run_leg("copies"):
         # output copies at many positions (SFT answer span, PT every position): MFMA-bound
         for name in ("gqa_8b_sft_32k", "gqa_8b_pt_16k"):
+            progress(name)
             ccfg = dict(inputs.WORKLOADS[name])
             cB, cT, cTo = ccfg["batch"], ccfg["T"], ccfg["T_out"]
             xc = inputs.prefill_inputs(seed=7, device="cuda", **ccfg)
@@ -288,23 +466,24 @@ def main():
             pre.run_swa()                       # fills the caches, not timed
             q_out, pos = inputs.copies_inputs(cB, Hq, d, cT, cTo, torch.bfloat16, seed=8, device="cuda")
             cp = Copies(ccfg, cT, q_out, pos, xc["alpha_out"], xc["beta_out"], pre.k_cache, pre.v_cache)
-            sec, _ = timed(cp.run, max(3, args.steps // 4), args.warmup)
-            t = sec / max(3, args.steps // 4)
+            n = max(3, args.steps // 4)
+            sec, _ = timed(cp.run, n, args.warmup)
+            t = sec / n
             keys = float((pos.double() + 1).sum().item())           # admissible (copy, key) pairs per head
             fl = 4 * d * Hq * keys
             nbytes = cB * cT * Hkv * d * 2 * 2 + 2 * cB * cTo * Hq * d * 2
             out[name] = {"kernel": "orthros_copies (copies_flash_kernel<128>)", "us": t * 1e6, "T": cT,
                          "T_out": cTo, "copies_per_s": cB * cTo / t, "flops": fl, "TFLOPs": fl / t / 1e12,
-                         "bytes": nbytes, "GBps": nbytes / t / 1e9}
-            result_copies = {"bound": "mfma", "achieved": fl / t / 1e12, "peak": BF16_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": fl / t / 1e12 / BF16_PEAK_TFLOPS, "traffic": None,
-                             "kernel": f"orthros_copies at {name}"}
-            out[name]["roofline"] = result_copies
+                         "bytes": nbytes, "GBps": nbytes / t / 1e9,
+                         "roofline": {"bound": "mfma", "achieved": fl / t / 1e12, "peak": BF16_PEAK_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": fl / t / 1e12 / BF16_PEAK_TFLOPS, "traffic": None,
+                                      "kernel": f"orthros_copies at {name}"}}
             del pre, cp, xc, q_out, pos
             torch.cuda.empty_cache()
 
-    if args.only in ("all", "project") and "project" not in args.skip:
+    if run_leg("project"):
         # the projections either side of the attention over the 128K batch: MFMA-bound
+        progress("gqa_8b_project_128k")
         pcfg = dict(inputs.WORKLOADS["gqa_8b_project_128k"])
         xp = inputs.project_inputs(seed=9, device="cuda", **pcfg)
         pr = Project(pcfg, xp, cap=pcfg["T"])
@@ -321,9 +500,10 @@ def main():
         torch.cuda.empty_cache()
 
     for lname in ("gqa_8b_decode_36l_b4", "gqa_8b_decode_36l_b1_short"):
-        if args.only not in ("all", "layers") or "layers" in args.skip:
+        if not run_leg("layers"):
             break
         # one decode step over 36 resident layers: eager launches vs one HIP graph
+        progress(lname)
         lcfg = dict(inputs.WORKLOADS[lname])
         nl, ns = lcfg["layers"], lcfg["steps"]
         layers = [inputs.decode_inputs(seed=100 + l, device="cuda", **lcfg) for l in range(nl)]
@@ -350,19 +530,23 @@ def main():
             fn()                                   # warm-up pass
             reset()
             torch.cuda.synchronize()
-            t0 = time.perf_counter()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
             fn()
+            e1.record()
             torch.cuda.synchronize()
-            res[name] = (time.perf_counter() - t0) / ns * 1e6
+            res[name] = e0.elapsed_time(e1) * 1e3 / ns
         lens = torch.stack([l0.double() for l0 in len0])
         step_bytes = float(((lens + ns / 2).sum() * lcfg["n_kv_heads"] * lcfg["head_dim"] * 2 * 2).item())
         out["decode_layers_" + lname] = {"workload": lname, "layers": nl, "steps": ns,
-                                "eager_us_per_step": res["eager"], "graph_us_per_step": res["graph"],
-                                "bytes_per_step": step_bytes, "GBps_graph": step_bytes / (res["graph"] * 1e-6) / 1e9}
+                                         "eager_us_per_step": res["eager"], "graph_us_per_step": res["graph"],
+                                         "bytes_per_step": step_bytes,
+                                         "GBps_graph": step_bytes / (res["graph"] * 1e-6) / 1e9}
         del stack, graph, layers
         torch.cuda.empty_cache()
 
-    if args.only in ("all", "decode"):
+    if run_leg("decode"):
+        progress("gqa_8b_decode_b16")
         dcfg = dict(inputs.WORKLOADS["gqa_8b_decode_b16"])
         nsteps = args.decode_steps
         dcfg["steps"] = nsteps
@@ -393,25 +577,40 @@ def main():
         out["decode"] = {"workload": "gqa_8b_decode_b16", "us_per_step": us, "steps": nsteps,
                          "bytes_per_step": step_bytes, "GBps": step_bytes / (us * 1e-6) / 1e9,
                          "p50_us": per[len(per) // 2], "p99_us": per[min(len(per) - 1, (99 * len(per)) // 100)]}
-        if args.only == "all" and not args.no_cpu_baseline:
-            out["decode"]["cpu_baseline"] = cpu_baseline_decode(dcfg, xd, len0)
+        configs["gqa_8b_decode_b16"] = {"us_per_step": us, "steps": nsteps, "bytes_per_step": step_bytes,
+                                        "GBps": step_bytes / (us * 1e-6) / 1e9,
+                                        "hbm_frac": step_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        if cpu_ok:
+            progress("gqa_8b_decode_b16: oracle")
+            dcfg["steps"] = 1024
+            cb = cpu_baseline_decode(dcfg, xd, len0)
+            out["decode"]["cpu_baseline"] = cb
+            configs["gqa_8b_decode_b16"]["cpu_baseline"] = cb
         if result is None:
             result = {"metric": METRIC, "value": us, "unit": "us/step", "n_gpus": 1, "steps": nsteps,
                       "warmup": 1, "ms_per_step": us / 1e3, "higher_is_better": False, "scaling": "weak",
                       "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
                       "config": {"workload": "gqa_8b_decode_b16", "global_batch": 16,
                                  "parallelism": "single-gpu"}}
+        del dec, xd
+        torch.cuda.empty_cache()
 
     if result is None:
         result = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "data": "synthetic",
                   "dtype": "bf16", "config": {"workload": "gqa_8b_prefill_128k"}}
     if "prefill" in out:
         s = out["prefill"]
+        # the same step priced as two passes (SWA + writer, then the copy's
+        # read of the whole cache): 1 GiB more than the one fused pass moves
+        two_pass = s["bytes"] + xattn_bytes(B, T, Hkv, d)
         result["roofline"] = {"bound": "hbm", "achieved": s["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": s["GBps"] / HBM_PEAK_GBS,
                               "traffic": measured_traffic("traffic_prefill_fused_gqa_8b_128k.md"),
                               "kernel": "orthros_prefill: swa_ring_kernel<128, true> (+ merge_kernel)",
                               "algorithmic_bytes": s["bytes"],
+                              "two_pass_bytes": two_pass,
+                              "achieved_two_pass_bytes": two_pass / (s["us"] * 1e-6) / 1e9,
+                              "frac_two_pass_bytes": two_pass / (s["us"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
                               "mfma_algorithmic_TFLOPs": s["TFLOPs"],
                               "mfma_algorithmic_frac": s["TFLOPs"] / BF16_PEAK_TFLOPS,
                               # the attainable roofline min(MFMA peak, intensity x HBM peak) at this
@@ -440,8 +639,10 @@ def main():
                                      "traffic": measured_traffic("traffic_decode_gqa_8b_b16.md"),
                                      "kernel": "orthros_decode_step: decode_append_kernel + "
                                                "xattn_lds_kernel<128, DecodeParams> + merge_kernel (per step)"}
-    if args.only == "all":
+    if args.only == "all" and "ceilings" not in args.skip:
+        progress("practical HBM ceilings")
         result["hbm_practical"] = practical_ceilings()
+    result["configs"] = configs
     result["kernels"] = out
     print(json.dumps(result), flush=True)
 

@@ -1,4 +1,6 @@
-"""Build step of the HIP library: hipcc for gfx950 -> phase_aware_swa_amd/liborthros.so.
+"""Build step of the HIP libraries: hipcc for gfx950 -> phase_aware_swa_amd/liborthros.so
+(the attention library) and phase_aware_swa_amd/libhbmprobe.so (streaming
+kernels the benchmark uses to measure this GPU's practical HBM rates).
 
 Each kernel translation unit compiles on its own (no relocatable device
 code: every kernel is launched from the file that defines it), then the
@@ -15,6 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liborthros.so")
+PROBE_LIB = os.path.join(HERE, "libhbmprobe.so")
+PROBE_SOURCES = ["hbm_probe.hip"]
 SOURCES = ["api.hip", "swa_prefill.hip", "swa_ring.hip", "global_xattn.hip", "copies_flash.hip", "project.hip", "xattn_lds.hip"]
 # The attention kernels never produce or test NaNs in float arithmetic (masked
 # scores are -inf, running maxima start finite; an invalid copy position writes its
@@ -46,19 +50,24 @@ def _compile(src):
     return obj
 
 
-def build(verbose=False):
-    """Compiles every source and links liborthros.so (always rebuilds)."""
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    """Compiles every source and links both libraries (always rebuilds)."""
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
