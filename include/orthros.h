@@ -226,7 +226,11 @@ orthros_status orthros_project(const orthros_desc* desc, int64_t T, int64_t T_ou
 /* -------------------------------------------------------------- decode */
 
 /* Workspace bytes orthros_decode_step needs when every cache length is at
- * most max_len.  0 on an invalid desc or max_len. */
+ * most max_len.  0 on an invalid desc or max_len.  The workspace begins
+ * with the step's arrival counters: it must be zero-filled once before its
+ * first step (e.g. hipMemset after allocating it); every step leaves the
+ * counters at zero again, so one zero-fill serves any number of steps,
+ * replayed graphs included.  Do not share it with other calls. */
 size_t orthros_decode_workspace_size(const orthros_desc* desc, int64_t max_len);
 
 /*
@@ -246,7 +250,8 @@ size_t orthros_decode_workspace_size(const orthros_desc* desc, int64_t max_len);
  *   max_len_hint      host: an upper bound of every cache_len[b]; sizes the
  *                     grid; needs max_len_hint + 1 <= cap
  *   o, o_out          device [B][Hq][d]
- *   workspace         device, >= orthros_decode_workspace_size(desc, max_len_hint) bytes
+ *   workspace         device, >= orthros_decode_workspace_size(desc, max_len_hint) bytes,
+ *                     zero-filled before its first step (see above)
  *
  * A sequence whose cache_len[b] is negative or above max_len_hint is not
  * touched (no cache write, no length update) and gets NaN in o[b] and

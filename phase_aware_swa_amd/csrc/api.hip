@@ -87,7 +87,7 @@ size_t len_bytes(const orthros_desc* d)
     return ((size_t)d->batch * 4 + kLenBytesAlign - 1) / kLenBytesAlign * kLenBytesAlign;
 }
 
-struct Split { int chunk, n_split, rec; bool lds; size_t bytes; };
+struct Split { int chunk, n_split, rec; bool lds, fused = false; size_t bytes; };
 
 orthros::Dt dt_of(const orthros_desc* d) { return d->dtype == ORTHROS_F32 ? orthros::Dt::F32 : orthros::Dt::BF16; }
 
@@ -132,6 +132,15 @@ size_t prefill_ws_bytes(const orthros_desc* d, int64_t T)
     return a > b ? a : b;
 }
 
+// Bytes of the decode step's arrival counters at the start of its
+// workspace: one per (sequence, KV head, head block of the chunked kernel)
+// and one per sequence, 256-byte aligned.
+size_t cnt_bytes(const orthros_desc* d)
+{
+    const size_t n = (size_t)d->batch * (size_t)(streams_of(d) / d->batch + 1);
+    return (n * 4 + kLenBytesAlign - 1) / kLenBytesAlign * kLenBytesAlign;
+}
+
 Split decode_split(const orthros_desc* d, int64_t max_len)
 {
     Split s;
@@ -145,10 +154,15 @@ Split decode_split(const orthros_desc* d, int64_t max_len)
     int64_t lds_chunk = 1024;
     while (lds_chunk * 3 / 2 < want) lds_chunk <<= 1;
     s.lds = lds;
-    s.chunk = lds ? (int)lds_chunk : pick_chunk(keys, streams_of(d), kDecodeTargetWgs);
+    // short bf16 steps: one launch over 128-key chunks (latency-bound, so
+    // each workgroup reads its whole chunk in one round trip)
+    s.fused = !lds && d->dtype == ORTHROS_BF16 &&
+              keys <= (int64_t)orthros::kDecodeShortChunk * orthros::kDecodeShortMaxSplits;
+    s.chunk = lds ? (int)lds_chunk
+                  : s.fused ? orthros::kDecodeShortChunk : pick_chunk(keys, streams_of(d), kDecodeTargetWgs);
     s.n_split = (int)((keys + s.chunk - 1) / s.chunk);
-    s.rec = d->head_dim + (lds ? orthros::kXattnLdsRecPad : 2);
-    s.bytes = len_bytes(d) + (size_t)d->batch * d->n_q_heads * 2 * s.n_split * s.rec * 4;
+    s.rec = d->head_dim + (lds ? orthros::kXattnLdsRecPad : s.fused ? 4 : 2);
+    s.bytes = cnt_bytes(d) + len_bytes(d) + (size_t)d->batch * d->n_q_heads * 2 * s.n_split * s.rec * 4;
     return s;
 }
 
@@ -290,21 +304,24 @@ orthros_status run_decode(const orthros_desc* desc, const Split& sp, const void*
     p.q = q; p.q_out = q_out; p.k_new = k_new; p.v_new = v_new;
     p.alpha = alpha; p.beta = beta; p.alpha_out = alpha_out; p.beta_out = beta_out;
     p.k_cache = k_cache; p.v_cache = v_cache; p.cache_len = cache_len; p.o = o; p.o_out = o_out;
-    p.ws_len = (int32_t*)workspace;
-    p.ws_part = (float*)((char*)workspace + len_bytes(desc));
+    p.ws_cnt = (int32_t*)workspace;
+    p.ws_len = (int32_t*)((char*)workspace + cnt_bytes(desc));
+    p.ws_part = (float*)((char*)workspace + cnt_bytes(desc) + len_bytes(desc));
     p.cap = cap; p.max_len = max_len_hint;
     p.B = desc->batch; p.Hq = desc->n_q_heads; p.Hkv = desc->n_kv_heads; p.D = desc->head_dim;
     p.window = desc->window;
-    p.chunk = sp.chunk; p.n_split = sp.n_split; p.rec = sp.rec; p.lds = sp.lds ? 1 : 0;
+    p.chunk = sp.chunk; p.n_split = sp.n_split; p.rec = sp.rec; p.lds = sp.lds ? 1 : 0; p.fused = sp.fused ? 1 : 0;
     p.qscale = qscale_of(desc);
     p.dt = dt_of(desc);
     return hip_status(orthros::launch_decode(p, stream), "decode kernel launch");
 }
 
-// Scratch of the allocation-free decode entry point: the per-step lengths
-// and split-K partials that orthros_decode_step keeps in the caller's
-// workspace.  Every step writes what it reads later in the same step, so
-// nothing needs clearing between calls.  In host code `scratch` only names
+// Scratch of the allocation-free decode entry point: the arrival counters,
+// per-step lengths and split-K partials that orthros_decode_step keeps in
+// the caller's workspace.  The counters start at zero (a device global is
+// zero-filled when the library's code is loaded) and every step leaves them
+// at zero; every other word a step reads it has written itself, so nothing
+// needs clearing between calls.  In host code `scratch` only names
 // the variable; its device address (one copy per GPU) comes from
 // hipGetSymbolAddress, looked up once per device on that device's first call.
 constexpr size_t kScratchBytes = size_t(64) << 20;

@@ -65,6 +65,10 @@ __device__ __forceinline__ void buf_store8(u32x2 v, rsrc_t r, uint32_t off)
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)off, 0, 0);
 }
 
+// Cache-policy operand of the buffer load / store builtins selecting device
+// scope (sc1): the access is coherent across the XCDs' L2 caches.
+constexpr int kCachePolicySc1 = 16;
+
 typedef __attribute__((address_space(3))) void lds_void;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 

@@ -21,9 +21,10 @@
 //   - each lane keeps an fp32 online-softmax state per head for the keys
 //     it saw; the states of a workgroup are merged by lane shuffles, then
 //     through LDS, into one (max, sum, unnormalised output) partial per head;
-//   - a second kernel merges the partials of a (sequence, head) by
-//     log-sum-exp in a fixed split order, so results are run-to-run
-//     identical.
+//   - the partials of a (sequence, head) are merged by log-sum-exp in a
+//     fixed split order, so results are run-to-run identical: by a second
+//     kernel in prefill, and in decode by the last workgroup of the head
+//     block to finish (one launch per step).
 // The decode step uses the same chunk worker for the copy (range [0, L])
 // and the base token (range [L-w+1, L]); the new token's key L is read from
 // k_new/v_new, never from the cache slot the same launch is writing.
@@ -260,6 +261,79 @@ __device__ __forceinline__ void attend_chunk(const float (*qs)[D], const E* kc, 
     __syncthreads();
 }
 
+// --------------------------------------------------------------- LSE merge
+
+// Log-sum-exp merge of the partial records s0..s1 of one (sequence, head,
+// kind) at pk (record stride rec floats: max, sum, ..., weighted values at
+// rec - D) into out[row .. row + D):
+//   o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
+// 256 threads.  Thread t owns head-dim values 4 (t % (D/4)) .. +3 of split
+// group t / (D/4); the split groups are then added in a fixed order, so the
+// result is run-to-run identical.  Ends with a barrier (LDS reusable).
+template <typename E, int D>
+__device__ void merge_splits(const float* pk, int rec, int s0, int s1, E* out, int64_t row)
+{
+    constexpr int TPR = D / 4;            // threads per head-dim row
+    constexpr int NG = 256 / TPR;         // split groups
+    __shared__ float red[NG][D + 1];
+    __shared__ float wmax[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int gp = tid / TPR, d4 = tid % TPR;
+    const int aoff = rec - D;             // the weighted values' offset in a record
+    // M = max over splits
+    float mx = kNegBig;
+    for (int s = s0 + tid; s <= s1; s += 256) mx = fmaxf(mx, pk[(int64_t)s * rec]);
+#pragma unroll
+    for (int x = 32; x > 0; x >>= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
+    if (lane == 0) wmax[wv] = mx;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    // this thread's split group: weighted sums of 4 head-dim values and of
+    // l, eight splits per round with every load of the round issued first
+    // (one L2 round trip per round, not per split); a round's splits past
+    // s1 read split s1 again with weight 0
+    float n0 = 0.f, n1 = 0.f, n2 = 0.f, n3 = 0.f, den = 0.f;
+    constexpr int RB = 8;
+    for (int s = s0 + gp; s <= s1; s += NG * RB) {
+        float ml[RB][2];
+        float2 a[RB], c[RB];
+#pragma unroll
+        for (int k = 0; k < RB; ++k) {
+            const int sk = s + NG * k <= s1 ? s + NG * k : s1;
+            const float* ps = pk + (int64_t)sk * rec;
+            ml[k][0] = ps[0];
+            ml[k][1] = ps[1];
+            a[k] = *(const float2*)(ps + aoff + 4 * d4);
+            c[k] = *(const float2*)(ps + aoff + 2 + 4 * d4);
+        }
+#pragma unroll
+        for (int k = 0; k < RB; ++k) {
+            const float f = s + NG * k <= s1 ? fast_exp2(ml[k][0] - M) : 0.f;
+            den += f * ml[k][1];
+            n0 += f * a[k].x;
+            n1 += f * a[k].y;
+            n2 += f * c[k].x;
+            n3 += f * c[k].y;
+        }
+    }
+    red[gp][4 * d4] = n0;
+    red[gp][4 * d4 + 1] = n1;
+    red[gp][4 * d4 + 2] = n2;
+    red[gp][4 * d4 + 3] = n3;
+    if (d4 == 0) red[gp][D] = den;
+    __syncthreads();
+    for (int d = tid; d < D; d += 256) {
+        float num = 0.f, dsum = 0.f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            num += red[g][d];
+            dsum += red[g][D];
+        }
+        st_elem(out, row + d, num / dsum);
+    }
+    __syncthreads();
+}
+
 // ------------------------------------------------------ prefill: split-K
 
 template <typename E, int D, int HG>
@@ -289,6 +363,12 @@ __global__ __launch_bounds__(256) void xattn_split_kernel(XattnParams p, int b0,
 
 // ----------------------------------------------------------- decode: split
 
+// The decode step's split kernel (the two-launch form): a workgroup takes
+// split s (keys [s chunk, (s+1) chunk)) of one KV head's HG-head block of
+// sequence b, for the copy over [0, L] and the base token over its window;
+// the partials and each sequence's length go to the workspace and the merge
+// kernel combines them (many splits per row merge fastest there, spread over
+// B x Hq workgroups).
 template <typename E, int D, int HG>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p)
 {
@@ -335,6 +415,276 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p)
                                vnew, wlo, hi, red, out + kind_stride, head_stride);
 }
 
+// --------------------------------------------- decode: short steps, fused
+
+// Device-scope 16-byte load / store of a partial record quad (sc1: written
+// through to, and read from, the level every XCD shares).
+__device__ __forceinline__ f32x4 rec_ld(rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCachePolicySc1));
+}
+__device__ __forceinline__ void rec_st(f32x4 v, rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kCachePolicySc1);
+}
+
+// The merge of a whole head block by one workgroup, from records of D + 4
+// floats (max, sum, 0, 0, weighted values) read at device scope: D / 4
+// threads per (head, kind) row, one 4-value quad each, one pass over the
+// splits in order with a running maximum (RB splits' header and quad
+// loaded per round); the result is run-to-run identical.  Threads past the
+// 2 HG rows do nothing; no barrier.
+template <int D, int HG>
+__device__ __forceinline__ void merge_block(rsrc_t part, int64_t head_stride, int64_t kind_stride, int sw0, int s1,
+                                            uint16_t* o_out, uint16_t* o, int64_t row0)
+{
+    constexpr int TPR = D / 4;
+    constexpr int RB = 16;
+    constexpr int REC = D + 4;
+    const int u = threadIdx.x / TPR, qd = threadIdx.x % TPR;
+    if (u >= 2 * HG) return;
+    const int hh = u >> 1, kind = u & 1;
+    const uint32_t base = (uint32_t)((hh * head_stride + kind * kind_stride) * 4);
+    const int s0 = kind ? sw0 : 0;
+    float M = kNegBig, den = 0.f;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    for (int s = s0; s <= s1; s += RB) {
+        f32x4 hd[RB], v[RB];
+#pragma unroll
+        for (int k = 0; k < RB; ++k) {
+            const uint32_t off = base + (uint32_t)((s + k <= s1 ? s + k : s1) * REC * 4);
+            hd[k] = rec_ld(part, off);
+            v[k] = rec_ld(part, off + 16 + 16 * qd);
+        }
+#pragma unroll
+        for (int k = 0; k < RB; ++k) {
+            // (no early exit: the arrays stay in registers)
+            if (s + k <= s1) {
+                const float mn = fmaxf(M, hd[k][0]);
+                const float sc = fast_exp2(M - mn), f = fast_exp2(hd[k][0] - mn);
+                den = den * sc + f * hd[k][1];
+                num = num * sc + f * v[k];
+                M = mn;
+            }
+        }
+    }
+    uint16_t* out = kind ? o : o_out;
+    const int64_t row = row0 + (int64_t)hh * D + 4 * qd;
+    const float inv = 1.f / den;
+    *(u32x2*)(out + row) = u32x2{pack_bf16x2(num[0] * inv, num[1] * inv), pack_bf16x2(num[2] * inv, num[3] * inv)};
+}
+
+// One launch per decode step when the histories are short (bf16, at most
+// kDecodeShortMaxSplits chunks of kDecodeShortChunk keys): the step is then
+// a few serial memory round trips long, so each workgroup (chunk s of one
+// KV head's HG-head block of sequence b) issues its query slices and every
+// K/V row of its chunk at once (no LDS staging, one round trip), scores the
+// copy's and the base token's HG heads together on the same rows (the base
+// token's keys below its window masked), reduces, and writes one partial
+// record per (head, kind) at device scope (D + 4 floats: max, sum, 0, 0,
+// weighted values).  It then counts itself in on the block's
+// counter; the last of the block's n_split workgroups to arrive merges the
+// block into o_out and o, and the last block of the sequence to finish
+// merging advances cache_len[b].  Every workgroup of the grid arrives, those
+// past the history too, so cache_len[b] changes only once every workgroup
+// of sequence b has read it.  The counters live at the start of the
+// workspace, start at zero and are left at zero.
+template <int D, int HG>
+__global__ __launch_bounds__(256) void decode_short_kernel(DecodeParams p)
+{
+    constexpr int LPK = D / 8;                    // lanes per key row (16 bytes each)
+    constexpr int KPW = 64 / LPK;                 // key rows per wave per load
+    constexpr int KPS = 4 * KPW;                  // key rows per workgroup per load
+    constexpr int NU = kDecodeShortChunk / KPS;   // loads per lane (K and V each)
+    constexpr int NR = 2 * HG;                    // query rows: the copy's heads, then the base token's
+    __shared__ float red[4][NR][D + 2];
+    __shared__ int last;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int c = lane % LPK, kg = lane / LPK;
+    const int s = blockIdx.x;
+    const int G = p.Hq / p.Hkv, hblocks = G / HG;
+    const int nblk = p.Hkv * hblocks;
+    const int g = blockIdx.y / hblocks, hb = blockIdx.y % hblocks;
+    const int b = blockIdx.z;
+    const int64_t L = p.cache_len[b];
+    const int h0 = g * G + hb * HG;
+    if (L < 0 || L > p.max_len) {
+        // a length outside [0, max_len]: NaN outputs, nothing else touched
+        if (s == 0)
+            for (int idx = tid; idx < HG * D; idx += 256) {
+                const int64_t o = ((int64_t)b * p.Hq + h0) * D + idx;
+                st_elem((uint16_t*)p.o_out, o, __builtin_nanf(""));
+                st_elem((uint16_t*)p.o, o, __builtin_nanf(""));
+            }
+        return;
+    }
+    const int64_t crow = ((int64_t)b * p.Hkv + g) * p.cap * D;
+    const uint16_t* kc = (const uint16_t*)p.k_cache + crow;
+    const uint16_t* vc = (const uint16_t*)p.v_cache + crow;
+    const uint16_t* knew = (const uint16_t*)p.k_new + ((int64_t)b * p.Hkv + g) * D;
+    const uint16_t* vnew = (const uint16_t*)p.v_new + ((int64_t)b * p.Hkv + g) * D;
+    if (s == 0 && hb == 0) {
+        // append the new base token's K/V at slot L (nobody reads slot L from
+        // the cache in this launch: readers take key L from k_new / v_new)
+        for (int d = tid; d < D; d += 256) {
+            ((uint16_t*)p.k_cache)[crow + L * D + d] = knew[d];
+            ((uint16_t*)p.v_cache)[crow + L * D + d] = vnew[d];
+        }
+    }
+    const int64_t lo = (int64_t)s * kDecodeShortChunk;
+    const int64_t wlo = L - p.window + 1 > 0 ? L - p.window + 1 : 0;
+    const int64_t kind_stride = (int64_t)p.n_split * (D + 4);
+    const int64_t head_stride = 2 * kind_stride;
+    // this head block's records, through a buffer resource (device-scope 16-byte accesses)
+    const rsrc_t prs = make_rsrc(p.ws_part + ((int64_t)b * p.Hq + h0) * head_stride, HG * head_stride * 4);
+    const bool any = lo <= L;                            // this chunk holds keys of the history
+    const bool win = any && lo + kDecodeShortChunk - 1 >= wlo;   // ... and of the base token's window
+    if (any) {
+        // every K/V row of the chunk this lane reads, then the query slices
+        Row8<uint16_t> kx[NU], vx[NU];
+        int64_t key[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            key[u] = lo + (int64_t)u * KPS + wv * KPW + kg;
+            kx[u].zero();
+            vx[u].zero();
+            if (key[u] <= L) {
+                const uint16_t* kr = key[u] == L ? knew : kc + key[u] * D;
+                const uint16_t* vr = key[u] == L ? vnew : vc + key[u] * D;
+                kx[u].load(kr + 8 * c);
+                vx[u].load(vr + 8 * c);
+            }
+        }
+        QSlice<uint16_t> qr[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const bool base = r >= HG;
+            const int h = h0 + (base ? r - HG : r);
+            const uint16_t* q = (const uint16_t*)(base ? p.q : p.q_out) + ((int64_t)b * p.Hq + h) * D + 8 * c;
+            const uint16_t* al = (const uint16_t*)(base ? p.alpha : p.alpha_out) + (int64_t)h * D + 8 * c;
+            const uint16_t* be = (const uint16_t*)(base ? p.beta : p.beta_out) + (int64_t)h * D + 8 * c;
+            Row8<uint16_t> qv, av, bv;
+            qv.load(q);
+            av.load(al);
+            bv.load(be);
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (qv[e] * av[e] + bv[e]) * p.qscale;
+            qr[r].set(x);
+        }
+        // bf16 V values of keys (u, u+1) paired per head-dim value, shared by the rows
+        uint32_t vp[NU / 2][8];
+#pragma unroll
+        for (int u = 0; u < NU; u += 2)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t a0 = vx[u].w[w], a1 = vx[u + 1].w[w];
+                vp[u / 2][2 * w] = (a0 & 0xffffu) | (a1 << 16);
+                vp[u / 2][2 * w + 1] = (a0 >> 16) | (a1 & 0xffff0000u);
+            }
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            if (r >= HG && !win) continue;               // uniform: no window key in this chunk
+            const int64_t klo = r >= HG ? wlo : 0;
+            float sc[NU];
+            float mx = kNegBig;
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const float dot = group_sum<LPK>(qr[r].dot(kx[u]));
+                sc[u] = (key[u] <= L && key[u] >= klo) ? dot : -INFINITY;
+                mx = fmaxf(mx, sc[u]);
+            }
+            float l = 0.f, acc[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+            for (int u = 0; u < NU; u += 2) {
+                // P as a bf16 pair; the row sum takes the same rounded weights
+                const uint32_t pp = pack_bf16x2(fast_exp2(sc[u] - mx), fast_exp2(sc[u + 1] - mx));
+                l += bf16_lo(pp) + bf16_hi(pp);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, vp[u / 2][e]),
+                                                             __builtin_bit_cast(bf16x2, pp), acc[e], false);
+            }
+            // merge the KPW key slots of the wave (lanes differing in kg)
+#pragma unroll
+            for (int x = LPK; x < 64; x <<= 1) {
+                const float mo = __shfl_xor(mx, x);
+                const float lo_ = __shfl_xor(l, x);
+                const float mm = fmaxf(mx, mo);
+                const float f = fast_exp2(mx - mm), fo = fast_exp2(mo - mm);
+                l = l * f + lo_ * fo;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = acc[e] * f + __shfl_xor(acc[e], x) * fo;
+                mx = mm;
+            }
+            if (kg == 0) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) red[wv][r][2 + 8 * c + e] = acc[e];
+                if (c == 0) {
+                    red[wv][r][0] = mx;
+                    red[wv][r][1] = l;
+                }
+            }
+        }
+        __syncthreads();
+        // merge the 4 waves in a fixed order; one record per (head, kind) of
+        // D + 4 floats (max, sum, 0, 0, weighted values), stored at device
+        // scope one 16-byte quad at a time
+        const int nr = win ? NR : HG;
+        constexpr int NQ = D / 4 + 1;
+        for (int idx = tid; idx < nr * NQ; idx += 256) {
+            const int r = idx / NQ, qd = idx % NQ;         // qd == 0: the (max, sum) header
+            float M = red[0][r][0];
+#pragma unroll
+            for (int w = 1; w < 4; ++w) M = fmaxf(M, red[w][r][0]);
+            float f[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) f[w] = fast_exp2(red[w][r][0] - M);
+            f32x4 q4 = {0.f, 0.f, 0.f, 0.f};
+            if (qd == 0) {
+                float l = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) l += f[w] * red[w][r][1];
+                q4[0] = M;
+                q4[1] = l;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float x = 0.f;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) x += f[w] * red[w][r][2 + 4 * (qd - 1) + e];
+                    q4[e] = x;
+                }
+            }
+            const int64_t off = (r % HG) * head_stride + (r >= HG ? kind_stride : 0) + (int64_t)s * (D + 4) + 4 * qd;
+            rec_st(q4, prs, (uint32_t)(off * 4));
+        }
+    }
+    // count in once this workgroup's records are written at device scope:
+    // the device-scope stores have completed (vmcnt) before the barrier, and
+    // the counter moves after it.  No cache-wide fence: the records bypass
+    // the non-coherent caches on both sides (device-scope stores here,
+    // device-scope loads in the merge).
+    wait_vmcnt<0>();
+    __syncthreads();
+    int* blk_cnt = p.ws_cnt + (int64_t)b * nblk + blockIdx.y;
+    if (tid == 0) last = atomicAdd(blk_cnt, 1) == p.n_split - 1;
+    __syncthreads();
+    if (!last) return;
+    merge_block<D, HG>(prs, head_stride, kind_stride, (int)(wlo / kDecodeShortChunk), (int)(L / kDecodeShortChunk),
+                       (uint16_t*)p.o_out, (uint16_t*)p.o, ((int64_t)b * p.Hq + h0) * D);
+    if (tid == 0) {
+        __hip_atomic_store(blk_cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int* seq_cnt = p.ws_cnt + (int64_t)p.B * nblk + b;
+        if (atomicAdd(seq_cnt, 1) == nblk - 1) {
+            __hip_atomic_store(seq_cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            p.cache_len[b] = (int32_t)(L + 1);
+        }
+    }
+}
+
 // ------------------------------------------------ many copies: general form
 
 // One workgroup per (copy, KV group block, sequence): the copy's HG heads
@@ -370,31 +720,20 @@ __global__ __launch_bounds__(256) void copies_simple_kernel(CopiesParams p)
     }
 }
 
-// --------------------------------------------------------------- LSE merge
-
-// One workgroup (256 threads) per (sequence, query head):
-//   o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s,
-// over the splits s that hold keys of the query's range.  Thread t owns
-// head-dim values 4 (t % (D/4)) .. +3 of split group t / (D/4); the split
-// groups are then added in a fixed order, so the result is run-to-run
-// identical.  kinds = 1: the copy only (prefill); kinds = 2: the copy, then
-// the base token (decode), which also advances cache_len.
+// One workgroup (256 threads) per (sequence, query head): the merge of its
+// splits that hold keys of the query's range.  kinds = 1: the copy only
+// (prefill); kinds = 2: the copy, then the base token (decode), which also
+// advances cache_len.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const float* ws_part, const int32_t* ws_len,
                                                     int32_t* cache_len, int64_t max_len, int window,
                                                     int Hq, int chunk, int n_split, int rec,
                                                     int kinds, E* o_out, E* o)
 {
-    constexpr int TPR = D / 4;            // threads per head-dim row
-    constexpr int NG = 256 / TPR;         // split groups
-    __shared__ float red[NG][D + 1];
-    __shared__ float wmax[4];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x;
     const int b = blockIdx.x / Hq, h = blockIdx.x % Hq;
-    const int gp = tid / TPR, d4 = tid % TPR;
     const int64_t L = ws_len[b];
     const int64_t kind_stride = (int64_t)n_split * rec;
-    const int aoff = rec - D;             // the weighted values' offset in a record
     const float* part = ws_part + ((int64_t)b * Hq + h) * kinds * kind_stride;
     const int64_t row = ((int64_t)b * Hq + h) * D;
     if (L < 0 || L > max_len) {
@@ -406,60 +745,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* ws_part, const 
     }
     for (int kind = 0; kind < kinds; ++kind) {
         const int64_t lo = kind == 0 ? 0 : (L - window + 1 > 0 ? L - window + 1 : 0);
-        const int s0 = (int)(lo / chunk), s1 = (int)(L / chunk);
-        const float* pk = part + kind * kind_stride;
-        // M = max over splits
-        float mx = kNegBig;
-        for (int s = s0 + tid; s <= s1; s += 256) mx = fmaxf(mx, pk[(int64_t)s * rec]);
-#pragma unroll
-        for (int x = 32; x > 0; x >>= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
-        if (lane == 0) wmax[wv] = mx;
-        __syncthreads();
-        const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-        // this thread's split group: weighted sums of 4 head-dim values and of
-        // l, eight splits per round with every load of the round issued first
-        // (one L2 round trip per round, not per split); a round's splits past
-        // s1 read split s1 again with weight 0
-        float n0 = 0.f, n1 = 0.f, n2 = 0.f, n3 = 0.f, den = 0.f;
-        constexpr int RB = 8;
-        for (int s = s0 + gp; s <= s1; s += NG * RB) {
-            float ml[RB][2];
-            float2 a[RB], c[RB];
-#pragma unroll
-            for (int k = 0; k < RB; ++k) {
-                const int sk = s + NG * k <= s1 ? s + NG * k : s1;
-                const float* ps = pk + (int64_t)sk * rec;
-                ml[k][0] = ps[0];
-                ml[k][1] = ps[1];
-                a[k] = *(const float2*)(ps + aoff + 4 * d4);
-                c[k] = *(const float2*)(ps + aoff + 2 + 4 * d4);
-            }
-#pragma unroll
-            for (int k = 0; k < RB; ++k) {
-                const float f = s + NG * k <= s1 ? fast_exp2(ml[k][0] - M) : 0.f;
-                den += f * ml[k][1];
-                n0 += f * a[k].x;
-                n1 += f * a[k].y;
-                n2 += f * c[k].x;
-                n3 += f * c[k].y;
-            }
-        }
-        red[gp][4 * d4] = n0;
-        red[gp][4 * d4 + 1] = n1;
-        red[gp][4 * d4 + 2] = n2;
-        red[gp][4 * d4 + 3] = n3;
-        if (d4 == 0) red[gp][D] = den;
-        __syncthreads();
-        for (int d = tid; d < D; d += 256) {
-            float num = 0.f, dsum = 0.f;
-#pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                num += red[g][d];
-                dsum += red[g][D];
-            }
-            st_elem(kind == 0 ? o_out : o, row + d, num / dsum);
-        }
-        __syncthreads();
+        merge_splits<E, D>(part + kind * kind_stride, rec, (int)(lo / chunk), (int)(L / chunk),
+                           kind == 0 ? o_out : o, row);
     }
     if (cache_len && h == 0 && tid == 0) cache_len[b] = (int32_t)(L + 1);
 }
@@ -489,8 +776,15 @@ template <typename E, int D, int HG>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t st)
 {
     const int hblocks = (p.Hq / p.Hkv) / HG;
-    hipLaunchKernelGGL((decode_split_kernel<E, D, HG>), dim3(p.n_split, p.Hkv * hblocks, p.B), dim3(256), 0,
-                       st, p);
+    const dim3 grid(p.n_split, p.Hkv * hblocks, p.B);
+    if constexpr (sizeof(E) == 2) {
+        if (p.fused) {
+            hipLaunchKernelGGL((decode_short_kernel<D, HG>), grid, dim3(256), 0, st, p);
+            return hipGetLastError();
+        }
+    }
+    if (p.fused) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_split_kernel<E, D, HG>), grid, dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_decode_merge(p, st);

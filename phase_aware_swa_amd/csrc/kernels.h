@@ -66,6 +66,8 @@ struct DecodeParams {
     int32_t* cache_len;   // device [B]
     void* o;              // [B][Hq][D]
     void* o_out;
+    int32_t* ws_cnt;      // workspace: arrival counters, [B][Hkv * G / HG] per head block then [B] per
+                          // sequence (short-history kernel); zero before a step and after it
     int32_t* ws_len;      // workspace: per-sequence length seen by this step
     float* ws_part;       // workspace: partials [B][Hq][2][n_split][rec]
     int64_t cap, max_len;
@@ -73,6 +75,7 @@ struct DecodeParams {
     int32_t chunk, n_split;
     int32_t rec;          // as in XattnParams
     int32_t lds;          // nonzero: the LDS-streamed kernel (chosen with the split)
+    int32_t fused;        // nonzero: the one-launch short-history kernel (chunk = kDecodeShortChunk)
     float qscale;
     Dt dt;
 };
@@ -108,6 +111,12 @@ inline bool xattn_lds_applies(Dt dt, int Hq, int Hkv) { return dt == Dt::BF16 &&
 constexpr int64_t kXattnLdsTargetWgs = 512;
 constexpr int kXattnLdsRecPad = 32;   // floats before the values in a partial record
 hipError_t launch_xattn_lds(const XattnParams& p, hipStream_t s);
+// The decode step: on the LDS-streamed kernel (append, stream, merge); for
+// bf16 steps of at most kDecodeShortMaxSplits chunks of kDecodeShortChunk
+// keys, on the one-launch short-history kernel (fused = 1); otherwise on the
+// lane-parallel split kernel and a merge kernel.
+constexpr int kDecodeShortChunk = 128;
+constexpr int kDecodeShortMaxSplits = 32;
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 // The decode step on the LDS-streamed kernel (bf16, groups of 4 query heads,
 // d = 128): append, the copy and the base token in one streaming pass, then

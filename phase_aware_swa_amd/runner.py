@@ -77,7 +77,8 @@ class Decode:
         self.o = torch.empty(B, Hq, d, dtype=dt, device=dev)
         self.o_out = torch.empty(B, Hq, d, dtype=dt, device=dev)
         ws = binding.decode_workspace_size(self.desc, max_len_hint)
-        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+        # zero-filled once: the step's arrival counters start at zero (each step leaves them so)
+        self.workspace = torch.zeros(max(ws, 16), dtype=torch.uint8, device=dev)
 
     def step(self, q, q_out, k_new, v_new, o=None, o_out=None, stream=None):
         binding.decode_step(self.desc, q, q_out, k_new, v_new, self.alpha, self.beta, self.alpha_out,

@@ -95,15 +95,17 @@ def test_decode_bad_arguments():
     assert call(cap=100, hint=50, wsb=8) == -6
 
 
-@pytest.mark.parametrize("B,hint,lds", [(16, 132095, True), (4, 32767, False), (1, 4095, False)],
-                         ids=["B16-128K-lds", "B4-32K-lane", "B1-4K-lane"])
+@pytest.mark.parametrize("B,hint,lds", [(16, 132095, True), (4, 32767, False), (1, 4095, False), (1, 4096, False)],
+                         ids=["B16-128K-lds", "B4-32K-lane", "B1-4K-short", "B1-4K-plus-one-lane"])
 def test_decode_workspace_layout(B, hint, lds):
-    """The decode workspace: 256-byte-aligned lengths, then two kinds of split
-    partials per (sequence, query head).  Long steps (bf16, 4-head groups,
+    """The decode workspace: 256-byte-aligned arrival counters and lengths,
+    then two kinds of split partials per (sequence, query head).  Long steps (bf16, 4-head groups,
     d128, at least 1536-key chunks at about 8192 items) take the LDS-streamed
     kernel's chunks -- the power of two nearest that -- and records of
     d + 32 floats; shorter ones the lane kernel's power-of-two chunks (>= 256
-    keys, about 16384 workgroups) and records of d + 2 floats.  A workspace one
+    keys, about 16384 workgroups) and records of d + 2 floats, or, up to 32
+    chunks of 128 keys, the one-launch short kernel's 128-key chunks and
+    records of d + 4 floats.  A workspace one
     byte short is rejected before anything runs."""
     Hq, Hkv, d = 32, 8, 128
     desc = mk(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=128, dtype=binding.BF16)
@@ -114,12 +116,15 @@ def test_decode_workspace_layout(B, hint, lds):
         chunk, rec = 1024, d + 32
         while chunk * 3 // 2 < want:
             chunk *= 2
+    elif keys <= 32 * 128:
+        chunk, rec = 128, d + 4                  # short bf16 steps: one launch over 128-key chunks
     else:
         chunk, rec = 256, d + 2
         while chunk < -(-keys * streams // 16384):
             chunk *= 2
     n_split = -(-keys // chunk)
-    need = -(-B * 4 // 256) * 256 + B * Hq * 2 * n_split * rec * 4
+    counters = -(-B * (Hkv * (Hq // Hkv // 4) + 1) * 4 // 256) * 256      # one per head block, one per sequence
+    need = counters + -(-B * 4 // 256) * 256 + B * Hq * 2 * n_split * rec * 4
     assert binding.decode_workspace_size(desc, hint) == need
     p = ctypes.c_void_p(FAKE)
     st = binding.lib().orthros_decode_step(ctypes.byref(desc), p, p, p, p, p, p, p, p, p, p, hint + 1, p, hint, p, p,

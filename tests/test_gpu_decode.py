@@ -84,6 +84,38 @@ def test_decode_lengths_at_stage_and_chunk_edges(d):
     assert torch.equal(bits(dec.v_cache.cpu()), bits(vc))
 
 
+@pytest.mark.parametrize("keys", [4096, 4097], ids=["one-launch-32-chunks", "two-launches"])
+def test_decode_short_kernel_edge(keys):
+    """bf16 steps of at most 32 chunks of 128 keys run as one launch of the
+    short-history kernel; a key more and they run on the lane-parallel split
+    kernel and a merge kernel: the step whose longest history makes
+    max_len_hint + 1 = 4096 keys and the one a key longer, three steps each,
+    against the oracle."""
+    steps = 3
+    lens = [keys - steps, 1, 4000]
+    Hq, Hkv, d, w = 8, 2, 128, 128
+    dtype = torch.bfloat16
+    say(f"decode split-count edge keys={keys}")
+    xc, cap = small_decode_inputs(len(lens), Hq, Hkv, d, dtype, lens, steps, seed=27 + keys)
+    cfg = dict(batch=len(lens), n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=w, dtype=dtype)
+    x = to_dev(xc)
+    hint = max(lens) + steps - 1
+    assert hint + 1 == keys
+    dec = Decode(cfg, x["k_cache"], x["v_cache"], x["cache_len"], hint, x["alpha"], x["beta"],
+                 x["alpha_out"], x["beta_out"])
+    kc, vc, lc = xc["k_cache"].clone(), xc["v_cache"].clone(), xc["cache_len"].clone()
+    for s in range(steps):
+        dec.step(x["q"][s], x["q_out"][s], x["k_new"][s], x["v_new"][s])
+        torch.cuda.synchronize()
+        o, o_out = oracle.decode_step(xc["q"][s], xc["q_out"][s], xc["k_new"][s], xc["v_new"][s], xc["alpha"],
+                                      xc["beta"], xc["alpha_out"], xc["beta_out"], w, kc, vc, lc)
+        assert_parity(dec.o, o, dtype, f"o step {s}")
+        assert_parity(dec.o_out, o_out, dtype, f"o_out step {s}")
+    assert torch.equal(dec.cache_len.cpu(), lc)
+    assert torch.equal(bits(dec.k_cache.cpu()), bits(kc))
+    assert torch.equal(bits(dec.v_cache.cpu()), bits(vc))
+
+
 @pytest.mark.parametrize("B,Hq,len_lo,len_hi,steps,w", [(32, 32, 66000, 70000, 2, 128),
                                                       (80, 32, 20000, 24000, 1, 128),
                                                       (32, 32, 66000, 70000, 1, 5000),
@@ -131,7 +163,9 @@ def test_decode_lds_kernel_long_histories(B, Hq, len_lo, len_hi, steps, w):
         chunk *= 2
     n_split = -(-keys // chunk)
     len_bytes = -(-B * 4 // 256) * 256         # the per-sequence lengths, 256-byte aligned
-    assert binding.decode_workspace_size(desc_for(cfg), max_hint) == len_bytes + B * Hq * 2 * n_split * (d + 32) * 4
+    cnt_bytes = -(-B * (Hkv * (Hq // Hkv // 4) + 1) * 4 // 256) * 256     # arrival counters
+    assert binding.decode_workspace_size(desc_for(cfg), max_hint) == (cnt_bytes + len_bytes +
+                                                                      B * Hq * 2 * n_split * (d + 32) * 4)
     kc, vc, lc = xc["k_cache"], xc["v_cache"], xc["cache_len"].clone()
     for s in range(steps):
         say(f"decode lds long histories: step {s}")

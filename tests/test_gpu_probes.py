@@ -57,8 +57,10 @@ def decode_split_of(B, Hq, Hkv, d, hint):
     """(uses the LDS-streamed kernel, workspace bytes) of a bf16 decode step,
     from the split rule of orthros_decode_step: about 8192 items of
     power-of-two chunks (at least 1536 keys asked for) on the LDS-streamed
-    kernel, else power-of-two chunks of at least 256 keys for about 16384
-    workgroups; records of d + 32 or d + 2 floats."""
+    kernel, else 128-key chunks when that makes at most 32 (the one-launch
+    kernel), else power-of-two chunks of at least 256 keys for about 16384
+    workgroups; records of d + 32, d + 4 or d + 2 floats; arrival counters
+    and lengths first."""
     G = Hq // Hkv
     hpw = 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
     streams = B * Hkv * (G // hpw)
@@ -69,13 +71,16 @@ def decode_split_of(B, Hq, Hkv, d, hint):
         chunk = 1024
         while chunk * 3 // 2 < want:
             chunk *= 2
+    elif keys <= 32 * 128:                       # short steps: one launch over 128-key chunks
+        chunk = 128
     else:
         chunk, need = 256, -(-keys * streams // 16384)
         while chunk < need:
             chunk *= 2
-    rec = d + (32 if lds else 2)
+    rec = d + (32 if lds else 4 if chunk == 128 else 2)
     n_split = -(-keys // chunk)
-    return lds, -(-B * 4 // 256) * 256 + B * Hq * 2 * n_split * rec * 4
+    counters = -(-B * (Hkv * (G // hpw) + 1) * 4 // 256) * 256
+    return lds, counters + -(-B * 4 // 256) * 256 + B * Hq * 2 * n_split * rec * 4
 
 
 # ------------------------------------------------------------------ prefill
@@ -296,10 +301,17 @@ def test_probe_decode_lds_copy_marked_chunk_edges():
     decode_probe(32, 32, 8, 128, 128, lens, 2, seed=332, marked=True, expect_lds=True)
 
 
-@pytest.mark.parametrize("Hq,Hkv,d,w", [(8, 2, 128, 128), (8, 2, 128, 1), (8, 2, 64, 300), (4, 2, 128, 128),
-                                       (16, 2, 128, 128)], ids=["G4", "G4-w1", "G4-d64-w300", "G2", "G8"])
-def test_probe_decode_lane_kernel(Hq, Hkv, d, w):
-    """Short histories (the lane-parallel kernel): lengths 0, 1, around the
-    window, and on the edges of 256-key chunks; three steps."""
-    lens = [0, 1, 126, 127, 128, 255, 256, 1000, 4095]
+@pytest.mark.parametrize("Hq,Hkv,d,w,longest", [(8, 2, 128, 128, 4095), (8, 2, 128, 1, 4095),
+                                               (8, 2, 64, 300, 4095), (4, 2, 128, 128, 4095),
+                                               (16, 2, 128, 128, 4095), (8, 2, 128, 128, 9000)],
+                         ids=["G4", "G4-w1", "G4-d64-w300", "G2", "G8", "G4-two-launches"])
+def test_probe_decode_lane_kernel(Hq, Hkv, d, w, longest):
+    """Short histories: lengths 0, 1, around the window, and on the edges of
+    128- and 256-key chunks; three steps.  Up to 4096 keys the step is one
+    launch of the short-history kernel (128-key chunks, merged in the
+    launch); with a 9000-key history it is the lane-parallel split kernel
+    and a merge kernel (256-key chunks)."""
+    lens = [0, 1, 126, 127, 128, 255, 256, 1000, longest]
+    if longest == 4095:
+        lens[-1] = 4093                          # keys = max_len_hint + 1 = 4096: the one-launch kernel
     decode_probe(len(lens), Hq, Hkv, d, w, lens, 3, seed=340 + w + d + Hq, expect_lds=False)
