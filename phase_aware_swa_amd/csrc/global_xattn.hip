@@ -31,6 +31,7 @@
 
 #include "device.h"
 #include "kernels.h"
+#include "pair_tile.h"
 
 namespace orthros {
 namespace {
@@ -475,32 +476,48 @@ __device__ __forceinline__ void merge_block(rsrc_t part, int64_t head_stride, in
 }
 
 // One launch per decode step when the histories are short (bf16, at most
-// kDecodeShortMaxSplits chunks of kDecodeShortChunk keys): the step is then
-// a few serial memory round trips long, so each workgroup (chunk s of one
-// KV head's HG-head block of sequence b) issues its query slices and every
-// K/V row of its chunk at once (no LDS staging, one round trip), scores the
-// copy's and the base token's HG heads together on the same rows (the base
-// token's keys below its window masked), reduces, and writes one partial
-// record per (head, kind) at device scope (D + 4 floats: max, sum, 0, 0,
-// weighted values).  It then counts itself in on the block's
-// counter; the last of the block's n_split workgroups to arrive merges the
-// block into o_out and o, and the last block of the sequence to finish
-// merging advances cache_len[b].  Every workgroup of the grid arrives, those
-// past the history too, so cache_len[b] changes only once every workgroup
-// of sequence b has read it.  The counters live at the start of the
-// workspace, start at zero and are left at zero.
+// kDecodeShortMaxSplits chunks of kDecodeShortChunk = 128 keys): the step is
+// then a few serial memory round trips long, so the work of a chunk is laid
+// out for latency.  A workgroup takes chunk s of one KV head's HG-head block
+// of sequence b; wave w takes the chunk's w-th run of kDecodeShortChunk / 128
+// 32-key pairs:
+//   - its pairs' K and V rows go straight into the wave's own LDS region by
+//     direct buffer-to-LDS loads in the pair layout of the streaming kernels
+//     (keys past L land as zeros), issued together with the query rows, and
+//     the new token's key L is then written over its slot there from
+//     k_new / v_new (the cache slot is being written by this launch);
+//   - S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16 with
+//     the copy's HG heads as query columns 0..HG-1 and the base token's as
+//     columns HG..2HG-1 (live when the chunk holds keys of its window;
+//     keys below the window are masked in those columns); V^T comes from the
+//     transposing LDS read; the row sums from an all-ones MFMA;
+//   - the 4 waves' states merge through LDS (in a fixed order) into one
+//     partial record per (head, kind), D + 4 floats (max, sum, 0, 0,
+//     weighted values), stored at device scope in 16-byte quads.
+// The workgroup then counts itself in on the block's counter; the last of
+// the block's n_split workgroups to arrive merges the block into o_out and
+// o, and the last block of the sequence to finish merging advances
+// cache_len[b].  Every workgroup of the grid arrives, those past the history
+// too, so cache_len[b] changes only once every workgroup of sequence b has
+// read it.  The counters live at the start of the workspace, start at zero
+// and are left at zero.
 template <int D, int HG>
 __global__ __launch_bounds__(256) void decode_short_kernel(DecodeParams p)
 {
-    constexpr int LPK = D / 8;                    // lanes per key row (16 bytes each)
-    constexpr int KPW = 64 / LPK;                 // key rows per wave per load
-    constexpr int KPS = 4 * KPW;                  // key rows per workgroup per load
-    constexpr int NU = kDecodeShortChunk / KPS;   // loads per lane (K and V each)
-    constexpr int NR = 2 * HG;                    // query rows: the copy's heads, then the base token's
-    __shared__ float red[4][NR][D + 2];
+    using R = PairTile<D>;
+    constexpr int NQ = D / 32, ND = D / 16;
+    constexpr int NH = 2 * HG;                 // live query columns
+    constexpr int PPW = kDecodeShortChunk / 128;   // 32-key pairs per wave
+    constexpr int KJ = R::KPART * 2 / 16 / 64; // direct loads per lane for a pair's K (and for its V)
+    constexpr int CPR = D / 8;                 // 16-byte chunks of a row
+    static_assert(PPW >= 1 && kDecodeShortChunk == 128 * PPW, "chunk of whole pairs per wave");
+    static_assert(4 * NH * (D + 2) * 4 <= 4 * PPW * R::SLOT * 2, "the wave combine fits in the pair regions");
+    __shared__ __align__(16) uint16_t lds[4 * PPW * R::SLOT];   // the waves' pairs, then the wave combine
     __shared__ int last;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int c = lane % LPK, kg = lane / LPK;
+    float (*red)[NH][D + 2] = reinterpret_cast<float (*)[NH][D + 2]>(lds);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, gq = lane >> 4;
     const int s = blockIdx.x;
     const int G = p.Hq / p.Hkv, hblocks = G / HG;
     const int nblk = p.Hkv * hblocks;
@@ -519,13 +536,11 @@ __global__ __launch_bounds__(256) void decode_short_kernel(DecodeParams p)
         return;
     }
     const int64_t crow = ((int64_t)b * p.Hkv + g) * p.cap * D;
-    const uint16_t* kc = (const uint16_t*)p.k_cache + crow;
-    const uint16_t* vc = (const uint16_t*)p.v_cache + crow;
     const uint16_t* knew = (const uint16_t*)p.k_new + ((int64_t)b * p.Hkv + g) * D;
     const uint16_t* vnew = (const uint16_t*)p.v_new + ((int64_t)b * p.Hkv + g) * D;
     if (s == 0 && hb == 0) {
-        // append the new base token's K/V at slot L (nobody reads slot L from
-        // the cache in this launch: readers take key L from k_new / v_new)
+        // append the new base token's K/V at slot L (this launch takes key L
+        // from k_new / v_new, never from that slot)
         for (int d = tid; d < D; d += 256) {
             ((uint16_t*)p.k_cache)[crow + L * D + d] = knew[d];
             ((uint16_t*)p.v_cache)[crow + L * D + d] = vnew[d];
@@ -537,112 +552,165 @@ __global__ __launch_bounds__(256) void decode_short_kernel(DecodeParams p)
     const int64_t head_stride = 2 * kind_stride;
     // this head block's records, through a buffer resource (device-scope 16-byte accesses)
     const rsrc_t prs = make_rsrc(p.ws_part + ((int64_t)b * p.Hq + h0) * head_stride, HG * head_stride * 4);
-    const bool any = lo <= L;                            // this chunk holds keys of the history
-    const bool win = any && lo + kDecodeShortChunk - 1 >= wlo;   // ... and of the base token's window
+    const bool any = lo <= L;                                    // the chunk holds keys of the history
+    const bool win = any && lo + kDecodeShortChunk - 1 >= wlo;    // ... and of the base token's window
     if (any) {
-        // every K/V row of the chunk this lane reads, then the query slices
-        Row8<uint16_t> kx[NU], vx[NU];
-        int64_t key[NU];
+        // wave wv takes pairs PPW wv .. PPW wv + PPW - 1 of the chunk
+        const int64_t kw0 = lo + 32 * PPW * wv;
+        const bool mine = kw0 <= L;                              // wave-uniform
+        const bool hasL = mine && L - kw0 < 32 * PPW;
+        uint16_t* slots = lds + wv * PPW * R::SLOT;
+        if (mine) {
+            // the pairs' rows through key L (the buffer range ends there, so
+            // later keys land as zeros), unit u = 64 j + lane of each part
+            const int64_t avail = (L - kw0 + 1) * D * 2;
+            const i32x4 rk = buffer_words((const uint16_t*)p.k_cache + crow + kw0 * D, avail);
+            const i32x4 rv = buffer_words((const uint16_t*)p.v_cache + crow + kw0 * D, avail);
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            key[u] = lo + (int64_t)u * KPS + wv * KPW + kg;
-            kx[u].zero();
-            vx[u].zero();
-            if (key[u] <= L) {
-                const uint16_t* kr = key[u] == L ? knew : kc + key[u] * D;
-                const uint16_t* vr = key[u] == L ? vnew : vc + key[u] * D;
-                kx[u].load(kr + 8 * c);
-                vx[u].load(vr + 8 * c);
-            }
-        }
-        QSlice<uint16_t> qr[NR];
+            for (int pp = 0; pp < PPW; ++pp) {
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const bool base = r >= HG;
-            const int h = h0 + (base ? r - HG : r);
-            const uint16_t* q = (const uint16_t*)(base ? p.q : p.q_out) + ((int64_t)b * p.Hq + h) * D + 8 * c;
-            const uint16_t* al = (const uint16_t*)(base ? p.alpha : p.alpha_out) + (int64_t)h * D + 8 * c;
-            const uint16_t* be = (const uint16_t*)(base ? p.beta : p.beta_out) + (int64_t)h * D + 8 * c;
-            Row8<uint16_t> qv, av, bv;
-            qv.load(q);
-            av.load(al);
-            bv.load(be);
-            float x[8];
+                for (int j = 0; j < KJ; ++j) {
+                    int r, c;
+                    R::k_unit(64 * j + lane, r, c);
+                    load_lds16(rk, (uint32_t)(((32 * pp + r) * D + 8 * c) * 2), 0, slots + pp * R::SLOT + 64 * j * 8);
+                }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (qv[e] * av[e] + bv[e]) * p.qscale;
-            qr[r].set(x);
-        }
-        // bf16 V values of keys (u, u+1) paired per head-dim value, shared by the rows
-        uint32_t vp[NU / 2][8];
-#pragma unroll
-        for (int u = 0; u < NU; u += 2)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t a0 = vx[u].w[w], a1 = vx[u + 1].w[w];
-                vp[u / 2][2 * w] = (a0 & 0xffffu) | (a1 << 16);
-                vp[u / 2][2 * w + 1] = (a0 >> 16) | (a1 & 0xffff0000u);
-            }
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            if (r >= HG && !win) continue;               // uniform: no window key in this chunk
-            const int64_t klo = r >= HG ? wlo : 0;
-            float sc[NU];
-            float mx = kNegBig;
-#pragma unroll
-            for (int u = 0; u < NU; ++u) {
-                const float dot = group_sum<LPK>(qr[r].dot(kx[u]));
-                sc[u] = (key[u] <= L && key[u] >= klo) ? dot : -INFINITY;
-                mx = fmaxf(mx, sc[u]);
-            }
-            float l = 0.f, acc[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-#pragma unroll
-            for (int u = 0; u < NU; u += 2) {
-                // P as a bf16 pair; the row sum takes the same rounded weights
-                const uint32_t pp = pack_bf16x2(fast_exp2(sc[u] - mx), fast_exp2(sc[u + 1] - mx));
-                l += bf16_lo(pp) + bf16_hi(pp);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    acc[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, vp[u / 2][e]),
-                                                             __builtin_bit_cast(bf16x2, pp), acc[e], false);
-            }
-            // merge the KPW key slots of the wave (lanes differing in kg)
-#pragma unroll
-            for (int x = LPK; x < 64; x <<= 1) {
-                const float mo = __shfl_xor(mx, x);
-                const float lo_ = __shfl_xor(l, x);
-                const float mm = fmaxf(mx, mo);
-                const float f = fast_exp2(mx - mm), fo = fast_exp2(mo - mm);
-                l = l * f + lo_ * fo;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] = acc[e] * f + __shfl_xor(acc[e], x) * fo;
-                mx = mm;
-            }
-            if (kg == 0) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) red[wv][r][2 + 8 * c + e] = acc[e];
-                if (c == 0) {
-                    red[wv][r][0] = mx;
-                    red[wv][r][1] = l;
+                for (int j = 0; j < KJ; ++j) {
+                    int r, c;
+                    R::v_unit(64 * j + lane, r, c);
+                    load_lds16(rv, (uint32_t)(((32 * pp + r) * D + 8 * c) * 2), 0,
+                               slots + pp * R::SLOT + R::KPART + 64 * j * 8);
                 }
             }
         }
+        // the new token's row chunks (lanes 0 .. 2 CPR - 1: K, then V)
+        u32x4 nrow = {0u, 0u, 0u, 0u};
+        if (hasL && lane < 2 * CPR) nrow = *(const u32x4*)(lane < CPR ? knew + 8 * lane : vnew + 8 * (lane - CPR));
+        // the query rows: lane (n, gq) holds column n, dims 32 i + 8 gq .. + 7
+        const bool base = n >= HG;
+        const bool live = n < HG || (n < NH && win);
+        const int h = h0 + (base ? n - HG : n);
+        u32x4 qw[NQ], aw[NQ], bw[NQ];
+        if (live) {
+            const uint16_t* q = (const uint16_t*)(base ? p.q : p.q_out) + ((int64_t)b * p.Hq + h) * D + 8 * gq;
+            const uint16_t* al = (const uint16_t*)(base ? p.alpha : p.alpha_out) + (int64_t)h * D + 8 * gq;
+            const uint16_t* be = (const uint16_t*)(base ? p.beta : p.beta_out) + (int64_t)h * D + 8 * gq;
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                qw[i] = *(const u32x4*)(q + 32 * i);
+                aw[i] = *(const u32x4*)(al + 32 * i);
+                bw[i] = *(const u32x4*)(be + 32 * i);
+            }
+        }
+        wait_vmcnt<0>();
+        if (hasL && lane < 2 * CPR) {
+            const int r = (int)(L - kw0);
+            uint16_t* sl = slots + (r >> 5) * R::SLOT;
+            uint16_t* dst = lane < CPR ? sl + R::kofs(r & 31, lane) : sl + R::KPART + R::vofs16(r & 31, lane - CPR);
+            *(u32x4*)dst = nrow;
+        }
+        // scale-offset queries in exp2 units as the B operand (zero columns past the live ones)
+        bf16x8 qf[NQ];
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            u32x4 r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t w = qw[i][e], a = aw[i][e], bb = bw[i][e];
+                r[e] = live ? pack_bf16x2(__builtin_fmaf(bf16_lo(w), bf16_lo(a), bf16_lo(bb)) * p.qscale,
+                                          __builtin_fmaf(bf16_hi(w), bf16_hi(a), bf16_hi(bb)) * p.qscale)
+                            : 0u;
+            }
+            qf[i] = __builtin_bit_cast(bf16x8, r);
+        }
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4 oacc[ND];
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) oacc[dt] = zero;
+        f32x4 lacc = zero;
+        float m = kNegBig;
+        if (mine) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0): key L's slot rewritten
+            // S^T per pair: sc[pp][0][r]: key 32 pp + 4 gq + r, sc[pp][1][r]:
+            // key 32 pp + 16 + 4 gq + r (from kw0, column n); admissible:
+            // <= L, and for the base token's columns >= wlo
+            f32x4 sc[PPW][2];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int pp = 0; pp < PPW; ++pp) {
+                const uint16_t* kb = slots + pp * R::SLOT + R::kofs(n, gq);
+                sc[pp][0] = zero;
+                sc[pp][1] = zero;
+#pragma unroll
+                for (int i = 0; i < NQ; ++i) {
+                    const bf16x8 k0 = *(const bf16x8*)(kb + i * R::K_STEP);
+                    const bf16x8 k1 = *(const bf16x8*)(kb + i * R::K_STEP + R::K_KEY16);
+                    sc[pp][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[i], sc[pp][0], 0, 0, 0);
+                    sc[pp][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[i], sc[pp][1], 0, 0, 0);
+                }
+                const int64_t key0 = kw0 + 32 * pp;
+                const int hi_off = (int)(L - key0 < 64 ? (L - key0 > -64 ? L - key0 : -64) : 64) - 4 * gq;
+                const int lo_off =
+                    (base ? (int)(wlo - key0 > -64 ? (wlo - key0 < 64 ? wlo - key0 : 64) : -64) : -64) - 4 * gq;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (r > hi_off || r < lo_off) sc[pp][0][r] = -INFINITY;
+                    if (16 + r > hi_off || 16 + r < lo_off) sc[pp][1][r] = -INFINITY;
+                    mx = fmaxf(mx, fmaxf(sc[pp][0][r], sc[pp][1][r]));
+                }
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            m = fmaxf(mx, kNegBig);
+            const bf16x8 kOnes = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+#pragma unroll
+            for (int pp = 0; pp < PPW; ++pp) {
+                const f32x4 s0 = sc[pp][0], s1 = sc[pp][1];
+                const u32x4 pw4 = {pack_bf16x2(fast_exp2(s0[0] - m), fast_exp2(s0[1] - m)),
+                                   pack_bf16x2(fast_exp2(s0[2] - m), fast_exp2(s0[3] - m)),
+                                   pack_bf16x2(fast_exp2(s1[0] - m), fast_exp2(s1[1] - m)),
+                                   pack_bf16x2(fast_exp2(s1[2] - m), fast_exp2(s1[3] - m))};
+                const bf16x8 pb = __builtin_bit_cast(bf16x8, pw4);
+                lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pb, lacc, 0, 0, 0);
+                // V^T operands: this lane addresses key rows 4 gq + (n >> 2) and
+                // 16 + 4 gq + (n >> 2), dims 16 dt + 4 (n & 3)
+                const uint16_t* vb = slots + pp * R::SLOT + R::KPART + R::vofs_tr(4 * gq + (n >> 2), 0, n & 3);
+#pragma unroll
+                for (int dt = 0; dt < ND; ++dt) {
+                    const s16x4 v0 = lds_read_tr(vb + dt * R::V_DT);
+                    const s16x4 v1 = lds_read_tr(vb + R::V_KEY16 + dt * R::V_DT);
+                    const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+                    const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, oacc[dt], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();                                         // every wave is done with its pair region
+        if (n < NH) {
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) red[wv][n][2 + 16 * dt + 4 * gq + r] = oacc[dt][r];
+            if (gq == 0) {
+                red[wv][n][0] = m;
+                red[wv][n][1] = lacc[0];
+            }
+        }
         __syncthreads();
-        // merge the 4 waves in a fixed order; one record per (head, kind) of
+        // the 4 waves in a fixed order; one record per (head, kind) of
         // D + 4 floats (max, sum, 0, 0, weighted values), stored at device
         // scope one 16-byte quad at a time
-        const int nr = win ? NR : HG;
-        constexpr int NQ = D / 4 + 1;
-        for (int idx = tid; idx < nr * NQ; idx += 256) {
-            const int r = idx / NQ, qd = idx % NQ;         // qd == 0: the (max, sum) header
+        const int nr = win ? NH : HG;
+        constexpr int NQD = D / 4 + 1;
+        for (int idx = tid; idx < nr * NQD; idx += 256) {
+            const int r = idx / NQD, qd = idx % NQD;          // column r; qd == 0: the (max, sum) header
             float M = red[0][r][0];
 #pragma unroll
             for (int w = 1; w < 4; ++w) M = fmaxf(M, red[w][r][0]);
             float f[4];
 #pragma unroll
             for (int w = 0; w < 4; ++w) f[w] = fast_exp2(red[w][r][0] - M);
-            f32x4 q4 = {0.f, 0.f, 0.f, 0.f};
+            f32x4 q4 = zero;
             if (qd == 0) {
                 float l = 0.f;
 #pragma unroll
