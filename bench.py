@@ -8,9 +8,11 @@ per segment), then the LSE merge of those partials.  value = prefill
 tokens per second (B * T / time per step).  The decode step latency
 (batch 16, lengths U[8192, 131072], 1024 steps) is reported beside it.
 
-Timing: warm-up calls, then K calls bracketed by torch.cuda.synchronize()
-and HIP events on the stream the kernels run on (the library queues its
-work on torch's current stream).  The roofline figure is for the step's
+Timing: W untimed warm-up calls (30 by default: from idle the GPU's clocks
+need about 20 back-to-back calls of this step to ramp up, and calls during
+the ramp run 15-20% slower), then K calls bracketed by
+torch.cuda.synchronize() and HIP events on the stream the kernels run on
+(the library queues its work on torch's current stream).  The roofline figure is for the step's
 dominant kernel, the fused streaming kernel: the step's algorithmic bytes
 over the step time (the merge that follows it in the same call takes a few
 microseconds of that).  The separate entry points orthros_swa_prefill and
@@ -311,7 +313,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # untimed calls before each timed leg: the GPU's clocks take about 20
+    # back-to-back calls of the 128K step (~30 ms of load) to ramp up from
+    # idle, and a few idle seconds undo it
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--only", default="all", choices=["all", "copy", "ceilings"] + LEGS)
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--skip", nargs="*", default=[], choices=LEGS + ["ceilings"],
@@ -430,7 +435,8 @@ def main():
             x = inputs.prefill_inputs(seed=1000 + layer, device="cuda", **c)
             run = Prefill(c, x, k_cache=kc_all[layer], v_cache=vc_all[layer])
             if layer == 0:
-                run.run()                          # warm-up call
+                for _ in range(5):                 # warm-up calls (clock ramp)
+                    run.run()
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
