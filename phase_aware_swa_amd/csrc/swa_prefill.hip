@@ -32,8 +32,8 @@
 // Workgroup ids are remapped so each XCD walks a contiguous run of tiles
 // and the 127-key halo of the next tile is still in its L2.
 //
-// fp32 kernel: a plain VALU variant (one wave per 64 rows of one head) for
-// fp32 storage, where the tolerance is 1e-4.
+// fp32 kernel: a VALU variant (8 lanes per row, 32 rows of one head per
+// workgroup) for fp32 storage, where the tolerance is 1e-4.
 
 #include "device.h"
 #include "kernels.h"
@@ -264,32 +264,43 @@ __global__ __launch_bounds__(256, 2) void swa_bf16_kernel(SwaParams a, int n_til
 
 // ------------------------------------------------------------------- fp32
 
+// fp32 storage (tolerance 1e-4): fp32 FMAs on the VALU.  A workgroup takes
+// 32 rows of one query head; each row is served by 8 lanes, lane e of the
+// row holding head dims [D/8 e, D/8 (e+1)) of the query and of the output
+// accumulator.  The key band [q0 - w + 1, q0 + 31] streams through LDS in
+// 32-key blocks (the next block's rows are loaded into registers while the
+// current one is used); per key the 8 lanes' partial dot products meet in a
+// DPP reduction, so every lane of the row has the score and updates its
+// slice of the online softmax state.  The workgroup of the KV group's first
+// query head writes the K/V rows it owns ([q0, q0 + 32)) to the cache.
 template <int D>
-__global__ __launch_bounds__(64) void swa_f32_kernel(SwaParams a, int n_tiles)
+__global__ __launch_bounds__(256) void swa_f32_kernel(SwaParams a, int n_tiles)
 {
     constexpr int KB = 32;                  // keys per LDS block
+    constexpr int DL = D / 8;               // head dims per lane
+    constexpr int F4 = KB * D / 4 / 256;    // float4 of a K (or V) block per thread
     __shared__ __align__(16) float Ks[KB][D];
     __shared__ __align__(16) float Vs[KB][D];
 
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int row = tid >> 3, e = tid & 7;
     const int tile = blockIdx.x % n_tiles;
     const int h = (blockIdx.x / n_tiles) % a.Hq;
     const int b = blockIdx.x / n_tiles / a.Hq;
     const int G = a.Hq / a.Hkv, g = h / G;
     const int64_t T = a.T;
     const int W = a.window;
-    const int64_t q0 = (int64_t)tile * 64, t = q0 + lane;
-    const float* qg = (const float*)a.q;
+    const int64_t q0 = (int64_t)tile * 32, t = q0 + row;
     const float* kg = (const float*)a.k;
     const float* vg = (const float*)a.v;
 
-    float qh[D], acc[D];
+    float qh[DL], acc[DL];
     {
-        const float* al = (const float*)a.alpha + (int64_t)h * D;
-        const float* be = (const float*)a.beta + (int64_t)h * D;
-        const float* qrow = qg + (((int64_t)b * T + (t < T ? t : T - 1)) * a.Hq + h) * D;
+        const float* al = (const float*)a.alpha + (int64_t)h * D + DL * e;
+        const float* be = (const float*)a.beta + (int64_t)h * D + DL * e;
+        const float* qrow = (const float*)a.q + (((int64_t)b * T + (t < T ? t : T - 1)) * a.Hq + h) * D + DL * e;
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
+        for (int d = 0; d < DL; ++d) {
             qh[d] = (qrow[d] * al[d] + be[d]) * a.qscale;
             acc[d] = 0.f;
         }
@@ -297,51 +308,64 @@ __global__ __launch_bounds__(64) void swa_f32_kernel(SwaParams a, int n_tiles)
     float m_run = kNegBig, l_run = 0.f;
 
     const int64_t klo = q0 - W + 1 > 0 ? q0 - W + 1 : 0;
-    const int64_t khi = (q0 + 64 < T ? q0 + 64 : T) - 1;
+    const int64_t khi = (q0 + 32 < T ? q0 + 32 : T) - 1;
     const bool writer = (h % G) == 0;
-    for (int64_t kbase = klo & ~(int64_t)(KB - 1); kbase <= khi; kbase += KB) {
-        // stage K/V rows [kbase, kbase + KB) of KV head g; write owned rows to the cache
-        for (int idx = lane; idx < KB * D / 4; idx += 64) {
-            const int kk = idx / (D / 4), d4 = idx % (D / 4);
+    const int64_t kb0 = klo & ~(int64_t)(KB - 1);
+    // rows of one block: thread tid holds float4 i of K and V, i = tid + 256 f
+    float4 kr[F4], vr[F4];
+    auto load_block = [&](int64_t kbase) {
+#pragma unroll
+        for (int f = 0; f < F4; ++f) {
+            const int idx = tid + 256 * f, kk = idx / (D / 4), d4 = idx % (D / 4);
             const int64_t j = kbase + kk;
-            float4 kv4 = make_float4(0.f, 0.f, 0.f, 0.f), vv4 = kv4;
+            kr[f] = vr[f] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (j < T) {
                 const int64_t off = (((int64_t)b * T + j) * a.Hkv + g) * D + 4 * d4;
-                kv4 = *(const float4*)(kg + off);
-                vv4 = *(const float4*)(vg + off);
-                if (writer && j >= q0) {
-                    const int64_t coff = (((int64_t)b * a.Hkv + g) * a.cap + j) * D + 4 * d4;
-                    *(float4*)((float*)a.k_cache + coff) = kv4;
-                    *(float4*)((float*)a.v_cache + coff) = vv4;
-                }
+                kr[f] = *(const float4*)(kg + off);
+                vr[f] = *(const float4*)(vg + off);
             }
-            *(float4*)&Ks[kk][4 * d4] = kv4;
-            *(float4*)&Vs[kk][4 * d4] = vv4;
         }
-        __syncthreads();
-        if (t < T) {
-            for (int kk = 0; kk < KB; ++kk) {
-                const int64_t j = kbase + kk;
-                if (j > t || j < t - W + 1) continue;
-                float s = 0.f;
+    };
+    load_block(kb0);
+    for (int64_t kbase = kb0; kbase <= khi; kbase += KB) {
+        __syncthreads();                    // the previous block is no longer read
 #pragma unroll
-                for (int d = 0; d < D; ++d) s += qh[d] * Ks[kk][d];
-                const float m_new = fmaxf(m_run, s);
-                const float corr = fast_exp2(m_run - m_new);
-                const float p = fast_exp2(s - m_new);
-                m_run = m_new;
-                l_run = l_run * corr + p;
-#pragma unroll
-                for (int d = 0; d < D; ++d) acc[d] = acc[d] * corr + p * Vs[kk][d];
+        for (int f = 0; f < F4; ++f) {
+            const int idx = tid + 256 * f, kk = idx / (D / 4), d4 = idx % (D / 4);
+            *(float4*)&Ks[kk][4 * d4] = kr[f];
+            *(float4*)&Vs[kk][4 * d4] = vr[f];
+            const int64_t j = kbase + kk;
+            if (writer && j >= q0 && j < T) {
+                const int64_t coff = (((int64_t)b * a.Hkv + g) * a.cap + j) * D + 4 * d4;
+                *(float4*)((float*)a.k_cache + coff) = kr[f];
+                *(float4*)((float*)a.v_cache + coff) = vr[f];
             }
         }
         __syncthreads();
+        if (kbase + KB <= khi) load_block(kbase + KB);
+        // keys of this block in the row's window [t - w + 1, t]
+        const int64_t lo = t - W + 1 > kbase ? t - W + 1 : kbase;
+        const int64_t hi = t < kbase + KB - 1 ? t : kbase + KB - 1;
+        for (int64_t j = kbase; j < kbase + KB; ++j) {
+            float sp = 0.f;
+#pragma unroll
+            for (int d = 0; d < DL; ++d) sp += qh[d] * Ks[j - kbase][DL * e + d];
+            const float s = group_sum<8>(sp);
+            if (j < lo || j > hi || t >= T) continue;   // uniform over the row's 8 lanes
+            const float m_new = fmaxf(m_run, s);
+            const float corr = fast_exp2(m_run - m_new);
+            const float p = fast_exp2(s - m_new);
+            m_run = m_new;
+            l_run = l_run * corr + p;
+#pragma unroll
+            for (int d = 0; d < DL; ++d) acc[d] = acc[d] * corr + p * Vs[j - kbase][DL * e + d];
+        }
     }
     if (t < T) {
-        float* orow = (float*)a.o + (((int64_t)b * T + t) * a.Hq + h) * D;
+        float* orow = (float*)a.o + (((int64_t)b * T + t) * a.Hq + h) * D + DL * e;
         const float inv = 1.f / l_run;
 #pragma unroll
-        for (int d = 0; d < D; d += 4)
+        for (int d = 0; d < DL; d += 4)
             *(float4*)(orow + d) = make_float4(acc[d] * inv, acc[d + 1] * inv, acc[d + 2] * inv, acc[d + 3] * inv);
     }
 }
@@ -361,9 +385,9 @@ hipError_t launch_bf16(const SwaParams& p, hipStream_t s)
 template <int D>
 hipError_t launch_f32(const SwaParams& p, hipStream_t s)
 {
-    const int n_tiles = (int)((p.T + 63) / 64);
+    const int n_tiles = (int)((p.T + 31) / 32);
     const int64_t n_wg = (int64_t)p.B * p.Hq * n_tiles;
-    hipLaunchKernelGGL((swa_f32_kernel<D>), dim3((unsigned)n_wg), dim3(64), 0, s, p, n_tiles);
+    hipLaunchKernelGGL((swa_f32_kernel<D>), dim3((unsigned)n_wg), dim3(256), 0, s, p, n_tiles);
     return hipGetLastError();
 }
 
