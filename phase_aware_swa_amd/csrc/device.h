@@ -52,9 +52,15 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes)
     const int64_t n = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)(uint32_t)n, 0x00020000);
 }
+// Cache-policy operand of the buffer builtins marking an access
+// non-temporal (nt): a stream read once.  On this GPU it is what lets a
+// one-workgroup-per-CU read stream reach the HBM rate of a many-wave copy.
+constexpr int kCachePolicyNt = 2;
+
+template <int CP = 0>
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off)
 {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CP));
 }
 __device__ __forceinline__ void buf_store16(u32x4 v, rsrc_t r, uint32_t off)
 {
@@ -95,6 +101,15 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voffset, int sof
 {
     const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)lds;
     asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voffset), "s"(rsrc), "s"(soffset), "s"(m0)
+                 : "memory", "m0");
+}
+// The same, non-temporal (a stream read once; see kCachePolicyNt).
+__device__ __forceinline__ void load_lds16_nt(i32x4 rsrc, uint32_t voffset, int soffset, const uint16_t* lds)
+{
+    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)lds;
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen nt lds"
                  :
                  : "v"(voffset), "s"(rsrc), "s"(soffset), "s"(m0)
                  : "memory", "m0");

@@ -504,7 +504,7 @@ __device__ __forceinline__ void merge_block(rsrc_t part, int64_t head_stride, in
 template <int D, int HG>
 __global__ __launch_bounds__(256) void decode_short_kernel(DecodeParams p)
 {
-    using R = PairTile<D>;
+    using R = LinePairTile<D>;
     constexpr int NQ = D / 32, ND = D / 16;
     constexpr int NH = 2 * HG;                 // live query columns
     constexpr int PPW = kDecodeShortChunk / 128;   // 32-key pairs per wave
@@ -572,14 +572,14 @@ __global__ __launch_bounds__(256) void decode_short_kernel(DecodeParams p)
                 for (int j = 0; j < KJ; ++j) {
                     int r, c;
                     R::k_unit(64 * j + lane, r, c);
-                    load_lds16(rk, (uint32_t)(((32 * pp + r) * D + 8 * c) * 2), 0, slots + pp * R::SLOT + 64 * j * 8);
+                    load_lds16_nt(rk, (uint32_t)(((32 * pp + r) * D + 8 * c) * 2), 0, slots + pp * R::SLOT + 64 * j * 8);
                 }
 #pragma unroll
                 for (int j = 0; j < KJ; ++j) {
                     int r, c;
                     R::v_unit(64 * j + lane, r, c);
-                    load_lds16(rv, (uint32_t)(((32 * pp + r) * D + 8 * c) * 2), 0,
-                               slots + pp * R::SLOT + R::KPART + 64 * j * 8);
+                    load_lds16_nt(rv, (uint32_t)(((32 * pp + r) * D + 8 * c) * 2), 0,
+                                  slots + pp * R::SLOT + R::KPART + 64 * j * 8);
                 }
             }
         }
@@ -638,13 +638,15 @@ __global__ __launch_bounds__(256) void decode_short_kernel(DecodeParams p)
             float mx = -INFINITY;
 #pragma unroll
             for (int pp = 0; pp < PPW; ++pp) {
-                const uint16_t* kb = slots + pp * R::SLOT + R::kofs(n, gq);
+                const uint16_t* kb0 = slots + pp * R::SLOT + R::kofs(n, gq);
+                const uint16_t* kb1 = slots + pp * R::SLOT + R::kofs(n, 4 + gq);
                 sc[pp][0] = zero;
                 sc[pp][1] = zero;
 #pragma unroll
                 for (int i = 0; i < NQ; ++i) {
-                    const bf16x8 k0 = *(const bf16x8*)(kb + i * R::K_STEP);
-                    const bf16x8 k1 = *(const bf16x8*)(kb + i * R::K_STEP + R::K_KEY16);
+                    const uint16_t* kb = ((i & 1) ? kb1 : kb0) + (i >> 1) * R::K_STEP2;
+                    const bf16x8 k0 = *(const bf16x8*)kb;
+                    const bf16x8 k1 = *(const bf16x8*)(kb + R::K_KEY16);
                     sc[pp][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[i], sc[pp][0], 0, 0, 0);
                     sc[pp][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[i], sc[pp][1], 0, 0, 0);
                 }

@@ -85,6 +85,42 @@ struct PairTile {
     }
 };
 
+// The same pair with K in line-aligned form, for kernels whose direct loads
+// fill LDS in lane order (one 1 KB block per load instruction): block b of
+// 64 16-byte units holds 8 keys x 8 chunks, i.e. 128 contiguous bytes of each
+// of 8 key rows, so every load instruction reads whole 128-byte lines of the
+// cache (what lets non-temporal loads stream at the full HBM rate; a load
+// that reads part of a line leaves the rest to be fetched again).  Within a
+// 16-key block, keys r and r + 8 take adjacent 8-unit rows and chunk c of key
+// r sits at position (c & 7) ^ (r & 7) of its row, so the operand read of a
+// k-step (16 keys, one chunk) hits 16 distinct 16-byte bank groups, and any
+// 8 consecutive of those keys 8 distinct ones.  V is laid out as in PairTile.
+template <int D>
+struct LinePairTile {
+    using P = PairTile<D>;
+    static constexpr int KPART = P::KPART, VPART = P::VPART, SLOT = P::SLOT;
+    // K: element offset of 16-byte chunk c (dims 8c .. 8c + 7) of key r.
+    __device__ static int kofs(int r, int c)
+    {
+        const int row = ((r & 7) << 1) | ((r >> 3) & 1);
+        return ((r >> 4) * 2 * D + (c >> 3) * 128 + row * 8 + ((c & 7) ^ (r & 7))) * 8;
+    }
+    // The operand of k-step i (chunk 4 i + gq of key n of block 0) is at
+    // kofs(n, 4 (i & 1) + gq) + (i >> 1) * K_STEP2; block 1 adds K_KEY16.
+    static constexpr int K_STEP2 = 128 * 8, K_KEY16 = 2 * D * 8;
+    // Inverse map: key row r and chunk c held by 16-byte unit u of the K part.
+    __device__ static void k_unit(int u, int& r, int& c)
+    {
+        const int row = (u >> 3) & 15;
+        r = 16 * (u / (2 * D)) + ((row & 1) << 3) + (row >> 1);
+        c = 8 * ((u % (2 * D)) >> 7) + ((u & 7) ^ (r & 7));
+    }
+    __device__ static int vofs_tr(int r, int dt, int q) { return P::vofs_tr(r, dt, q); }
+    __device__ static int vofs16(int r, int c) { return P::vofs16(r, c); }
+    __device__ static void v_unit(int u, int& r, int& c) { P::v_unit(u, r, c); }
+    static constexpr int V_DT = P::V_DT, V_KEY16 = P::V_KEY16, V_KEY8 = P::V_KEY8, V_KEY4 = P::V_KEY4;
+};
+
 // Four bf16 of V^T through the transposing read (see above).
 __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p)
 {

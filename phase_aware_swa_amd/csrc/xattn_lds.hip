@@ -32,8 +32,10 @@
 //     stage's wait lets exactly those stay in flight;
 //   - each load instruction fills 1 KB of a slot in lane order, so each lane
 //     fetches the cache chunk that belongs at its 16-byte unit of the pair
-//     layout (PairTile's inverse maps); the stage's buffer range ends at the
-//     item's last key, so keys past it land as zeros;
+//     layout (LinePairTile's inverse maps: every instruction reads whole
+//     128-byte lines, 8 key rows x 128 bytes, which the loads mark
+//     non-temporal -- the cache is read once per call); the stage's buffer
+//     range ends at the item's last key, so keys past it land as zeros;
 //   - pair p of a stage is consumed by wave p % 4: S^T = K Q^T and
 //     O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 with the 4 heads' queries as
 //     columns 0..3 of the B operand (the other 12 are zero: the MFMAs are
@@ -66,20 +68,14 @@ __device__ __forceinline__ void block_barrier()
     asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ int64_t readlane64(int64_t x, int l)
-{
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), l);
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
 // One item: chunk s of stream j = (KV head g, 4-head block hb) of sequence b,
 // keys lo .. hi (hi <= P, the copy's position), nst stages.  In decode, P is
 // the cache length L and `win` marks the chunks that hold keys of the base
-// token's window [wlo, L].
+// token's window [wlo, L].  Key indices fit 32 bits (positions are below
+// 2^31); only cache offsets need 64.
 struct Item {
     int b, g, hb, s, nst;
-    int64_t lo, hi, wlo;
+    int lo, hi, wlo;
     bool win;
 };
 
@@ -89,11 +85,12 @@ struct Item {
 // along as query columns 4..7 of the same MFMAs (their keys are a subset of
 // the copy's), leaving a second partial per head for the chunks that hold
 // its window.
+// The chunk is a power of two, 2^cshift keys.
 template <int D, typename PT>
-__global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, PosBlock pos)
+__global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, int cshift, PosBlock pos)
 {
     constexpr bool DEC = std::is_same<PT, DecodeParams>::value;
-    using R = PairTile<D>;
+    using R = LinePairTile<D>;
     constexpr int NP = 128 / D * 4;       // pairs per stage: 64 KB
     constexpr int SK = 32 * NP;           // keys per stage
     constexpr int PAIRB = 32 * D * 2;     // bytes of one pair's K (or V) rows in the cache
@@ -123,23 +120,23 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, Po
     const uint16_t* v_cache = (const uint16_t*)a.v_cache;
 
     // lane i < nb: sequence b0 + i, its copy position and its item count
-    int64_t Lv = -1;
+    int Lv = -1;
     if constexpr (DEC) {
         // a length outside [0, max_len] gives the sequence no items (the
         // merge turns it into NaN outputs and leaves cache_len alone)
-        const int64_t Lraw = lane < nb ? (int64_t)a.cache_len[b0 + lane] : -1;
-        if (blockIdx.x == 0 && tid < nb) a.ws_len[b0 + tid] = (int32_t)Lraw;
+        const int Lraw = lane < nb ? a.cache_len[b0 + lane] : -1;
+        if (blockIdx.x == 0 && tid < nb) a.ws_len[b0 + tid] = Lraw;
         Lv = Lraw >= 0 && Lraw <= a.max_len ? Lraw : -1;
     } else {
-        Lv = lane < nb ? pos.v[lane] : -1;
-        if (blockIdx.x == 0 && tid < nb) a.ws_len[b0 + tid] = (int32_t)Lv;
+        Lv = lane < nb ? (int)pos.v[lane] : -1;
+        if (blockIdx.x == 0 && tid < nb) a.ws_len[b0 + tid] = Lv;
     }
     // Item order: every stream's full chunks first (chunks 0 .. nch - 2, by
     // sequence, stream, chunk), then every stream's last chunk, which may be
     // short.  Round-robin over that order gives each workgroup an equal
     // count of full items to within one, and the short last chunks go first
     // to the workgroups that drew one full item fewer.
-    const int nchv = Lv >= 0 ? (int)(Lv / a.chunk) + 1 : 0;   // chunks per stream of sequence b0 + lane
+    const int nchv = Lv >= 0 ? (Lv >> cshift) + 1 : 0;   // chunks per stream of sequence b0 + lane
     const int cntF = nchv > 0 ? (nchv - 1) * S : 0;
     const int cntT = nchv > 0 ? S : 0;
     int inclF = cntF, inclT = cntT;      // inclusive prefix sums over the lanes
@@ -163,8 +160,8 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, Po
         const uint64_t m = __ballot(lane < nb && (full ? exclF : exclT) <= kk);
         const int bl = __popcll(m) - 1;
         it.b = b0 + bl;
-        const int64_t L = readlane64(Lv, bl);
-        const int nch = (int)(L / a.chunk) + 1;
+        const int L = __builtin_amdgcn_readlane(Lv, bl);
+        const int nch = (L >> cshift) + 1;
         const int r = kk - __builtin_amdgcn_readlane(full ? exclF : exclT, bl);
         int j;
         if (full) {
@@ -176,14 +173,14 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, Po
         }
         it.g = j / hblocks;
         it.hb = j - it.g * hblocks;
-        it.lo = (int64_t)it.s * a.chunk;
-        it.hi = it.lo + a.chunk - 1 < L ? it.lo + a.chunk - 1 : L;
-        it.nst = (int)((it.hi - it.lo) / SK) + 1;
+        it.lo = it.s << cshift;
+        it.hi = L - it.lo < (1 << cshift) ? L : it.lo + (1 << cshift) - 1;
+        it.nst = (it.hi - it.lo) / SK + 1;
         it.wlo = 0;
         it.win = false;
         if constexpr (DEC) {
             it.wlo = L - a.window + 1 > 0 ? L - a.window + 1 : 0;
-            it.win = it.s >= (int)(it.wlo / a.chunk);
+            it.win = it.s >= (it.wlo >> cshift);
         }
     };
 
@@ -202,16 +199,16 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, Po
     // 256 j + 64 wv .. + 63 of the slot, i.e. part (j % JP) of pair j / JP
     auto issue = [&](const Item& it, int st, int sl) {
         const int64_t crow = ((int64_t)it.b * a.Hkv + it.g) * a.cap * D;
-        const int64_t k0 = it.lo + (int64_t)st * SK;
-        const int64_t avail = (it.hi - k0 + 1) * D * 2;
-        const i32x4 rk = buffer_words(k_cache + crow + k0 * D, avail);
-        const i32x4 rv = buffer_words(v_cache + crow + k0 * D, avail);
+        const int k0 = it.lo + st * SK;
+        const int64_t avail = (int64_t)(it.hi - k0 + 1) * D * 2;
+        const i32x4 rk = buffer_words(k_cache + crow + (int64_t)k0 * D, avail);
+        const i32x4 rv = buffer_words(v_cache + crow + (int64_t)k0 * D, avail);
         const uint16_t* dst = lds + sl * SLOTE + 64 * wv * 8;
 #pragma unroll
         for (int j = 0; j < LPS; ++j) {
             const int pp = j / JP, jj = j % JP;
-            if (jj < JH) load_lds16(rk, koff[jj] + pp * PAIRB, 0, dst + 256 * j * 8);
-            else load_lds16(rv, voff[jj - JH] + pp * PAIRB, 0, dst + 256 * j * 8);
+            if (jj < JH) load_lds16_nt(rk, koff[jj] + pp * PAIRB, 0, dst + 256 * j * 8);
+            else load_lds16_nt(rv, voff[jj - JH] + pp * PAIRB, 0, dst + 256 * j * 8);
         }
     };
     // the item's query rows and scale-offsets into qa[q]: region i by wave
@@ -228,8 +225,12 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, Po
                       : (r == 1 ? (const uint16_t*)a.alpha_out : (const uint16_t*)a.beta_out) + (int64_t)h0 * D;
     };
     auto issue_rows = [&](const Item& it, int q) {
+        // the wave index read afresh here: the region tests then cost a
+        // compare at each call instead of scalar masks held across the loop
+        int w0 = wv;
+        asm volatile("" : "+s"(w0));
 #pragma unroll
-        for (int r = wv; r < NREG; r += 4) {
+        for (int r = w0; r < NREG; r += 4) {
             const i32x4 rs = buffer_words(row_src(it, r), HRE * 2);
             if (lane < HRE / 8) load_lds16(rs, 16 * lane, 0, &qa[q][r * HRE]);
         }
@@ -239,6 +240,9 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, Po
     if (kc >= total) return;
     Item ci;
     item_of(kc, ci);
+    // the consumed item's sequence, head block and chunk only address its
+    // partial records: vector registers, like the issue cursor's item below
+    asm volatile("" : "+v"(ci.b), "+v"(ci.g), "+v"(ci.hb), "+v"(ci.s));
     int sc = 0, qc = 0;           // qc: parity of ci's row area
     Item ii = ci;                 // the item being issued, its next stage and row area
     int ki = kc, si = 0, qi = 0;
@@ -251,6 +255,11 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, Po
             return;
         }
         item_of(ki, ii);
+        // the issue cursor's item only feeds address arithmetic: it is kept
+        // in vector registers (the same value in every lane), which leaves
+        // the scalar file room for the rest without spilling (its stage
+        // count stays scalar: the cursor's branches must stay uniform)
+        asm volatile("" : "+v"(ii.b), "+v"(ii.g), "+v"(ii.hb), "+v"(ii.lo), "+v"(ii.hi));
         si = 0;
         qi ^= 1;
     };
@@ -283,21 +292,21 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, Po
     float m_run = kNegBig;        // lane (n, .): the running maximum of head n of the block
 
     // one pair of the stage in `slot`: keys key0 .. key0 + 31, the last admissible hi
-    auto attend = [&](const uint16_t* slot, int pp, int64_t key0, int64_t hi, int64_t wlo, bool win) {
-        int ko = pp * R::SLOT + R::kofs(n, gq);
-        asm volatile("" : "+v"(ko));
-        const uint16_t* kb = slot + ko;
+    auto attend = [&](const uint16_t* slot, int pp, int key0, int hi, int wlo, bool win) {
+        int ko0 = pp * R::SLOT + R::kofs(n, gq), ko1 = pp * R::SLOT + R::kofs(n, 4 + gq);
+        asm volatile("" : "+v"(ko0), "+v"(ko1));
         f32x4 s0 = zero, s1 = zero;
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
-            const bf16x8 k0 = *(const bf16x8*)(kb + i * R::K_STEP);
-            const bf16x8 k1 = *(const bf16x8*)(kb + i * R::K_STEP + R::K_KEY16);
+            const uint16_t* kb = slot + ((i & 1) ? ko1 : ko0) + (i >> 1) * R::K_STEP2;
+            const bf16x8 k0 = *(const bf16x8*)kb;
+            const bf16x8 k1 = *(const bf16x8*)(kb + R::K_KEY16);
             s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[i], s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[i], s1, 0, 0, 0);
         }
         // s0[r]: key key0 + 4 gq + r, s1[r]: key key0 + 16 + 4 gq + r (column n)
         if (key0 + 31 > hi) {
-            const int lim = (int)(hi - key0) - 4 * gq;
+            const int lim = hi - key0 - 4 * gq;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 if (r > lim) s0[r] = -INFINITY;
@@ -307,7 +316,7 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, Po
         if constexpr (DEC) {
             // the base token's columns 4..7: keys below its window
             if (win && key0 < wlo) {
-                const int lim = wlo - key0 < 64 ? (int)(wlo - key0) - 4 * gq : 64;
+                const int lim = wlo - key0 < 64 ? wlo - key0 - 4 * gq : 64;
                 if ((n >> 2) == 1) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
@@ -391,7 +400,7 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, Po
         // pair pp of the stage goes to wave pp % 4
 #pragma unroll
         for (int pp = 0; pp < NP; ++pp) {
-            const int64_t key0 = ci.lo + (int64_t)sc * SK + 32 * pp;
+            const int key0 = ci.lo + sc * SK + 32 * pp;
             if ((pp & 3) == wv && key0 <= ci.hi) attend(slot, pp, key0, ci.hi, ci.wlo, ci.win);
         }
         if (++sc < ci.nst) {
@@ -459,6 +468,7 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, Po
         kc += nwg;
         if (kc >= total) break;
         item_of(kc, ci);
+        asm volatile("" : "+v"(ci.b), "+v"(ci.g), "+v"(ci.hb), "+v"(ci.s));
         sc = 0;
         qc ^= 1;
     }
@@ -501,11 +511,25 @@ int cu_count()
     return v;
 }
 
+// log2 of a power-of-two chunk of at most 2^30 keys, else -1.
+int chunk_shift(int chunk)
+{
+    if (chunk < 1 || chunk > (1 << 30) || (chunk & (chunk - 1))) return -1;
+    int s = 0;
+    while ((1 << s) < chunk) ++s;
+    return s;
+}
+
+// Key indices travel as 32-bit integers in the kernel: every cached key,
+// plus a stage of overrun, must stay below 2^31.
+constexpr int64_t kLdsMaxCap = INT32_MAX - 4096;
+
 }  // namespace
 
 hipError_t launch_xattn_lds(const XattnParams& p, hipStream_t st)
 {
-    if (p.rec != p.D + kXattnLdsRecPad) return hipErrorInvalidValue;
+    const int cshift = chunk_shift(p.chunk);
+    if (p.rec != p.D + kXattnLdsRecPad || cshift < 0 || p.cap > kLdsMaxCap) return hipErrorInvalidValue;
     const int hblocks = (p.Hq / p.Hkv) / 4;
     const int ncu = cu_count();
     for (int b0 = 0; b0 < p.B; b0 += kPosPerLaunch) {
@@ -516,9 +540,10 @@ hipError_t launch_xattn_lds(const XattnParams& p, hipStream_t st)
         const int64_t max_items = (int64_t)nb * p.Hkv * hblocks * p.n_split;
         const unsigned grid = (unsigned)(max_items < ncu ? max_items : ncu);
         if (p.D == 64)
-            hipLaunchKernelGGL((xattn_lds_kernel<64, XattnParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, pos);
+            hipLaunchKernelGGL((xattn_lds_kernel<64, XattnParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, cshift, pos);
         else
-            hipLaunchKernelGGL((xattn_lds_kernel<128, XattnParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, pos);
+            hipLaunchKernelGGL((xattn_lds_kernel<128, XattnParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, cshift,
+                               pos);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -527,7 +552,9 @@ hipError_t launch_xattn_lds(const XattnParams& p, hipStream_t st)
 
 hipError_t launch_decode_lds(const DecodeParams& p, hipStream_t st)
 {
-    if (p.D != 128 || p.rec != p.D + kXattnLdsRecPad) return hipErrorInvalidValue;
+    const int cshift = chunk_shift(p.chunk);
+    if (p.D != 128 || p.rec != p.D + kXattnLdsRecPad || cshift < 0 || p.cap > kLdsMaxCap)
+        return hipErrorInvalidValue;
     // the new token's K/V into slot L first: the streaming kernel reads
     // every key of [0, L] from the cache
     hipLaunchKernelGGL((decode_append_kernel<128>), dim3(p.B), dim3(256), 0, st, p);
@@ -541,7 +568,8 @@ hipError_t launch_decode_lds(const DecodeParams& p, hipStream_t st)
         // items of this launch, at most (every length at max_len)
         const int64_t max_items = (int64_t)nb * p.Hkv * hblocks * p.n_split;
         const unsigned grid = (unsigned)(max_items < ncu ? max_items : ncu);
-        hipLaunchKernelGGL((xattn_lds_kernel<128, DecodeParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, unused);
+        hipLaunchKernelGGL((xattn_lds_kernel<128, DecodeParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, cshift,
+                           unused);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
