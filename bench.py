@@ -280,7 +280,7 @@ def practical_ceilings():
     vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.hbm_probe_read.argtypes = [vp, i64, vp, ci, ci, vp]
     lib.hbm_probe_copy.argtypes = [vp, vp, i64, ci, ci, vp]
-    grids = (1024, 2048, 4096, 8192)
+    grids = (256, 512, 1024, 2048, 4096, 8192)
     sink = torch.empty(max(grids) * 256, dtype=torch.int32, device="cuda")
     stream = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     best = {"read": (0.0, None), "copy": (0.0, None)}
@@ -644,7 +644,7 @@ def main():
                                      "frac": dd["GBps"] / HBM_PEAK_GBS,
                                      "traffic": measured_traffic("traffic_decode_gqa_8b_b16.md"),
                                      "kernel": "orthros_decode_step: decode_append_kernel + "
-                                               "xattn_lds_kernel<128, DecodeParams> + merge_kernel (per step)"}
+                                               "xattn_lds_kernel<128, DecodeParams> + lds_merge_kernel (per step)"}
     if args.only == "all" and "ceilings" not in args.skip:
         progress("practical HBM ceilings")
         result["hbm_practical"] = practical_ceilings()

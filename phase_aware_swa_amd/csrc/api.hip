@@ -89,6 +89,23 @@ size_t len_bytes(const orthros_desc* d)
 
 struct Split { int chunk, n_split, rec; bool lds, fused = false; size_t bytes; };
 
+// Bytes of the LDS-streamed kernel's per-stream record ranges ([B][streams][3]
+// int32, 256-byte aligned), which sit between the lengths and the records;
+// 0 for the other kernels.
+size_t rng_bytes(const orthros_desc* d, bool lds)
+{
+    if (!lds) return 0;
+    return ((size_t)streams_of(d) * 3 * 4 + kLenBytesAlign - 1) / kLenBytesAlign * kLenBytesAlign;
+}
+
+// The LDS-streamed kernel's records: ids over every launch, kinds x 4 heads
+// of rec floats each.
+size_t lds_record_bytes(const orthros_desc* d, int kinds, int rec)
+{
+    const int S = (int)(streams_of(d) / d->batch);
+    return (size_t)orthros::xattn_lds_records(d->batch, S) * kinds * 4 * rec * 4;
+}
+
 orthros::Dt dt_of(const orthros_desc* d) { return d->dtype == ORTHROS_F32 ? orthros::Dt::F32 : orthros::Dt::BF16; }
 
 bool fused_prefill(const orthros_desc* d)
@@ -96,18 +113,26 @@ bool fused_prefill(const orthros_desc* d)
     return orthros::ring_applies(dt_of(d), d->n_q_heads, d->n_kv_heads, d->window);
 }
 
-// Key splits of the output copy in prefill.  The separate cross-attention
-// kernel uses power-of-two chunks; the fused path (streaming SWA kernel with
-// the copy's query folded in) leaves one partial per segment of its launch.
-// The workspace covers whichever the call takes.
+// Key splits of the output copy in prefill.  The LDS-streamed kernel cuts
+// the keys into equal runs per workgroup (records by id, their ranges per
+// stream); the lane-parallel kernel uses power-of-two chunks; the fused path
+// (streaming SWA kernel with the copy's query folded in) leaves one partial
+// per segment of its launch.  The workspace covers whichever the call takes.
 Split prefill_split(const orthros_desc* d, int64_t T)
 {
     Split s;
     const bool lds = orthros::xattn_lds_applies(dt_of(d), d->n_q_heads, d->n_kv_heads);
-    s.chunk = pick_chunk(T, streams_of(d), lds ? orthros::kXattnLdsTargetWgs : kPrefillTargetWgs);
-    s.n_split = (int)((T + s.chunk - 1) / s.chunk);
-    s.rec = d->head_dim + (lds ? orthros::kXattnLdsRecPad : 2);
     s.lds = lds;
+    if (lds) {
+        s.chunk = 0;
+        s.n_split = 0;
+        s.rec = d->head_dim + orthros::kXattnLdsRecPad;
+        s.bytes = len_bytes(d) + rng_bytes(d, true) + lds_record_bytes(d, 1, s.rec);
+        return s;
+    }
+    s.chunk = pick_chunk(T, streams_of(d), kPrefillTargetWgs);
+    s.n_split = (int)((T + s.chunk - 1) / s.chunk);
+    s.rec = d->head_dim + 2;
     s.bytes = len_bytes(d) + (size_t)d->batch * d->n_q_heads * s.n_split * s.rec * 4;
     return s;
 }
@@ -145,23 +170,25 @@ Split decode_split(const orthros_desc* d, int64_t max_len)
 {
     Split s;
     const int64_t keys = max_len + 1;
-    // the LDS-streamed kernel: about kXattnLdsDecodeItems items, the chunk
-    // the power of two nearest (geometrically) to what that asks for
-    int64_t want = (keys * streams_of(d) + orthros::kXattnLdsDecodeItems - 1) / orthros::kXattnLdsDecodeItems;
-    want = want < (int64_t(1) << 24) ? want : (int64_t(1) << 24);
+    // the LDS-streamed kernel: enough keys over all streams to keep one
+    // pipeline per CU busy
     const bool lds = orthros::xattn_lds_applies(dt_of(d), d->n_q_heads, d->n_kv_heads) && d->head_dim == 128 &&
-                     want >= orthros::kXattnLdsDecodeMinChunk;
-    int64_t lds_chunk = 1024;
-    while (lds_chunk * 3 / 2 < want) lds_chunk <<= 1;
+                     keys * streams_of(d) >= orthros::kXattnLdsDecodeMinKeys;
     s.lds = lds;
+    if (lds) {
+        s.chunk = 0;
+        s.n_split = 0;
+        s.rec = d->head_dim + orthros::kXattnLdsRecPad;
+        s.bytes = cnt_bytes(d) + len_bytes(d) + rng_bytes(d, true) + lds_record_bytes(d, 2, s.rec);
+        return s;
+    }
     // short bf16 steps: one launch over 128-key chunks (latency-bound, so
     // each workgroup reads its whole chunk in one round trip)
     s.fused = !lds && d->dtype == ORTHROS_BF16 &&
               keys <= (int64_t)orthros::kDecodeShortChunk * orthros::kDecodeShortMaxSplits;
-    s.chunk = lds ? (int)lds_chunk
-                  : s.fused ? orthros::kDecodeShortChunk : pick_chunk(keys, streams_of(d), kDecodeTargetWgs);
+    s.chunk = s.fused ? orthros::kDecodeShortChunk : pick_chunk(keys, streams_of(d), kDecodeTargetWgs);
     s.n_split = (int)((keys + s.chunk - 1) / s.chunk);
-    s.rec = d->head_dim + (lds ? orthros::kXattnLdsRecPad : s.fused ? 4 : 2);
+    s.rec = d->head_dim + (s.fused ? 4 : 2);
     s.bytes = cnt_bytes(d) + len_bytes(d) + (size_t)d->batch * d->n_q_heads * 2 * s.n_split * s.rec * 4;
     return s;
 }
@@ -248,7 +275,8 @@ orthros::XattnParams xattn_params(const orthros_desc* d, const Split& sp, const 
     p.q_out = q_out; p.alpha_out = alpha_out; p.beta_out = beta_out;
     p.k_cache = k_cache; p.v_cache = v_cache; p.o_out = o_out;
     p.ws_len = (int32_t*)ws;
-    p.ws_part = (float*)((char*)ws + len_bytes(d));
+    p.ws_rng = sp.lds ? (int32_t*)((char*)ws + len_bytes(d)) : nullptr;
+    p.ws_part = (float*)((char*)ws + len_bytes(d) + rng_bytes(d, sp.lds));
     p.pos = out_pos;
     p.cap = cap;
     p.B = d->batch; p.Hq = d->n_q_heads; p.Hkv = d->n_kv_heads; p.D = d->head_dim;
@@ -306,7 +334,8 @@ orthros_status run_decode(const orthros_desc* desc, const Split& sp, const void*
     p.k_cache = k_cache; p.v_cache = v_cache; p.cache_len = cache_len; p.o = o; p.o_out = o_out;
     p.ws_cnt = (int32_t*)workspace;
     p.ws_len = (int32_t*)((char*)workspace + cnt_bytes(desc));
-    p.ws_part = (float*)((char*)workspace + cnt_bytes(desc) + len_bytes(desc));
+    p.ws_rng = sp.lds ? (int32_t*)((char*)workspace + cnt_bytes(desc) + len_bytes(desc)) : nullptr;
+    p.ws_part = (float*)((char*)workspace + cnt_bytes(desc) + len_bytes(desc) + rng_bytes(desc, sp.lds));
     p.cap = cap; p.max_len = max_len_hint;
     p.B = desc->batch; p.Hq = desc->n_q_heads; p.Hkv = desc->n_kv_heads; p.D = desc->head_dim;
     p.window = desc->window;

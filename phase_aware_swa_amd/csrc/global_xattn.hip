@@ -265,14 +265,14 @@ __device__ __forceinline__ void attend_chunk(const float (*qs)[D], const E* kc, 
 // --------------------------------------------------------------- LSE merge
 
 // Log-sum-exp merge of the partial records s0..s1 of one (sequence, head,
-// kind) at pk (record stride rec floats: max, sum, ..., weighted values at
-// rec - D) into out[row .. row + D):
+// kind) at pk (record s at pk + s * stride floats: max, sum, ..., weighted
+// values at aoff) into out[row .. row + D):
 //   o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
 // 256 threads.  Thread t owns head-dim values 4 (t % (D/4)) .. +3 of split
 // group t / (D/4); the split groups are then added in a fixed order, so the
 // result is run-to-run identical.  Ends with a barrier (LDS reusable).
 template <typename E, int D>
-__device__ void merge_splits(const float* pk, int rec, int s0, int s1, E* out, int64_t row)
+__device__ void merge_splits(const float* pk, int64_t stride, int aoff, int s0, int s1, E* out, int64_t row)
 {
     constexpr int TPR = D / 4;            // threads per head-dim row
     constexpr int NG = 256 / TPR;         // split groups
@@ -280,10 +280,9 @@ __device__ void merge_splits(const float* pk, int rec, int s0, int s1, E* out, i
     __shared__ float wmax[4];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int gp = tid / TPR, d4 = tid % TPR;
-    const int aoff = rec - D;             // the weighted values' offset in a record
     // M = max over splits
     float mx = kNegBig;
-    for (int s = s0 + tid; s <= s1; s += 256) mx = fmaxf(mx, pk[(int64_t)s * rec]);
+    for (int s = s0 + tid; s <= s1; s += 256) mx = fmaxf(mx, pk[(int64_t)s * stride]);
 #pragma unroll
     for (int x = 32; x > 0; x >>= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
     if (lane == 0) wmax[wv] = mx;
@@ -301,7 +300,7 @@ __device__ void merge_splits(const float* pk, int rec, int s0, int s1, E* out, i
 #pragma unroll
         for (int k = 0; k < RB; ++k) {
             const int sk = s + NG * k <= s1 ? s + NG * k : s1;
-            const float* ps = pk + (int64_t)sk * rec;
+            const float* ps = pk + (int64_t)sk * stride;
             ml[k][0] = ps[0];
             ml[k][1] = ps[1];
             a[k] = *(const float2*)(ps + aoff + 4 * d4);
@@ -815,9 +814,39 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* ws_part, const 
     }
     for (int kind = 0; kind < kinds; ++kind) {
         const int64_t lo = kind == 0 ? 0 : (L - window + 1 > 0 ? L - window + 1 : 0);
-        merge_splits<E, D>(part + kind * kind_stride, rec, (int)(lo / chunk), (int)(L / chunk),
+        merge_splits<E, D>(part + kind * kind_stride, rec, rec - D, (int)(lo / chunk), (int)(L / chunk),
                            kind == 0 ? o_out : o, row);
     }
+    if (cache_len && h == 0 && tid == 0) cache_len[b] = (int32_t)(L + 1);
+}
+
+// The LDS-streamed kernel's records: one workgroup per (sequence, query
+// head) merges the record ids its stream's range lists (ws_rng: first, first
+// holding keys of the base token's window, last) -- records [id][kinds][4
+// heads of the block][rec].  kinds = 2 (decode) also advances cache_len.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void lds_merge_kernel(const float* ws_part, const int32_t* ws_rng,
+                                                        const int32_t* ws_len, int32_t* cache_len, int64_t max_len,
+                                                        int Hq, int G, int rec, int kinds, E* o_out, E* o)
+{
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x / Hq, h = blockIdx.x % Hq;
+    const int64_t L = ws_len[b];
+    const int64_t row = ((int64_t)b * Hq + h) * D;
+    if (L < 0 || L > max_len) {
+        for (int d = tid; d < D; d += 256) {
+            st_elem(o_out, row + d, __builtin_nanf(""));
+            if (kinds == 2) st_elem(o, row + d, __builtin_nanf(""));
+        }
+        return;
+    }
+    const int hblocks = G / 4, S = (Hq / G) * hblocks;
+    const int j = (h / G) * hblocks + (h % G) / 4;          // the head's stream: KV head, 4-head block
+    const int32_t* rg = ws_rng + ((int64_t)b * S + j) * 3;
+    const int64_t stride = (int64_t)kinds * 4 * rec;
+    for (int kind = 0; kind < kinds; ++kind)
+        merge_splits<E, D>(ws_part + ((int64_t)kind * 4 + h % 4) * rec, stride, rec - D, kind == 0 ? rg[0] : rg[1],
+                           rg[2], kind == 0 ? o_out : o, row);
     if (cache_len && h == 0 && tid == 0) cache_len[b] = (int32_t)(L + 1);
 }
 
@@ -919,6 +948,29 @@ hipError_t launch_merge(const XattnParams& p, hipStream_t st)
     };
     if (p.D == 64) go(merge_kernel<uint16_t, 64>);
     else go(merge_kernel<uint16_t, 128>);
+    return hipGetLastError();
+}
+
+hipError_t launch_lds_merge(const XattnParams& p, hipStream_t st)
+{
+    int64_t max_len = 0;
+    for (int b = 0; b < p.B; ++b) max_len = p.pos[b] > max_len ? p.pos[b] : max_len;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part, p.ws_rng, p.ws_len,
+                           (int32_t*)nullptr, max_len, p.Hq, p.Hq / p.Hkv, p.rec, 1, (uint16_t*)p.o_out,
+                           (uint16_t*)nullptr);
+    };
+    if (p.D == 64) go(lds_merge_kernel<uint16_t, 64>);
+    else go(lds_merge_kernel<uint16_t, 128>);
+    return hipGetLastError();
+}
+
+hipError_t launch_lds_merge(const DecodeParams& p, hipStream_t st)
+{
+    if (p.dt != Dt::BF16 || p.D != 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((lds_merge_kernel<uint16_t, 128>), dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part, p.ws_rng,
+                       p.ws_len, p.cache_len, p.max_len, p.Hq, p.Hq / p.Hkv, p.rec, 2, (uint16_t*)p.o_out,
+                       (uint16_t*)p.o);
     return hipGetLastError();
 }
 

@@ -39,7 +39,9 @@ struct XattnParams {
     const void* v_cache;
     void* o_out;          // [B][Hq][D]
     int32_t* ws_len;      // workspace: per-sequence last key index
-    float* ws_part;       // workspace: partials [B][Hq][1][n_split][rec]
+    int32_t* ws_rng;      // workspace (LDS-streamed kernel): record range per stream, [B][streams][3]
+    float* ws_part;       // workspace: partials [B][Hq][1][n_split][rec], or the LDS-streamed
+                          // kernel's records [id][4][rec]
     const int64_t* pos;   // host [B]: copy positions
     int64_t cap;
     int32_t B, Hq, Hkv, D;
@@ -69,7 +71,9 @@ struct DecodeParams {
     int32_t* ws_cnt;      // workspace: arrival counters, [B][Hkv * G / HG] per head block then [B] per
                           // sequence (short-history kernel); zero before a step and after it
     int32_t* ws_len;      // workspace: per-sequence length seen by this step
-    float* ws_part;       // workspace: partials [B][Hq][2][n_split][rec]
+    int32_t* ws_rng;      // workspace (LDS-streamed kernel): as in XattnParams
+    float* ws_part;       // workspace: partials [B][Hq][2][n_split][rec], or the LDS-streamed
+                          // kernel's records [id][2][4][rec]
     int64_t cap, max_len;
     int32_t B, Hq, Hkv, D, window;
     int32_t chunk, n_split;
@@ -105,12 +109,29 @@ hipError_t launch_xattn(const XattnParams& p, hipStream_t s);
 // LSE merge of bf16 prefill partials [B][Hq][1][n_split][rec] into o_out.
 hipError_t launch_merge(const XattnParams& p, hipStream_t s);
 // The LDS-streamed MFMA form of the prefill cross-attention (bf16, groups of
-// 4 query heads): a persistent kernel, one workgroup per CU, then the LSE
-// merge.  Its key chunks aim at about kXattnLdsTargetWgs items in all.
+// 4 query heads): a persistent kernel, one workgroup per CU (at most
+// kXattnLdsMaxGrid), each taking an equal run of the launch's keys (at least
+// kXattnLdsSegMin), then the LSE merge.  A launch serves up to
+// kPosPerLaunch sequences; its records take ids rbase .. rbase + region - 1
+// (one per segment: a run's piece of one stream, at most streams + grid of
+// them), where launch i has rbase = i * region.
 inline bool xattn_lds_applies(Dt dt, int Hq, int Hkv) { return dt == Dt::BF16 && (Hq / Hkv) % 4 == 0; }
-constexpr int64_t kXattnLdsTargetWgs = 512;
 constexpr int kXattnLdsRecPad = 32;   // floats before the values in a partial record
+constexpr int kXattnLdsMaxGrid = 512;
+constexpr int64_t kXattnLdsSegMin = 256;
+inline int64_t xattn_lds_region(int B, int streams)
+{
+    return (int64_t)(B < kPosPerLaunch ? B : kPosPerLaunch) * streams + kXattnLdsMaxGrid;
+}
+inline int64_t xattn_lds_records(int B, int streams)
+{
+    return (int64_t)((B + kPosPerLaunch - 1) / kPosPerLaunch) * xattn_lds_region(B, streams);
+}
 hipError_t launch_xattn_lds(const XattnParams& p, hipStream_t s);
+// LSE merge of the LDS-streamed kernel's records (the ranges in ws_rng)
+// into o_out (and in decode o, then cache_len[b] += 1).
+hipError_t launch_lds_merge(const XattnParams& p, hipStream_t s);
+hipError_t launch_lds_merge(const DecodeParams& p, hipStream_t s);
 // The decode step: on the LDS-streamed kernel (append, stream, merge); for
 // bf16 steps of at most kDecodeShortMaxSplits chunks of kDecodeShortChunk
 // keys, on the one-launch short-history kernel (fused = 1); otherwise on the
@@ -120,13 +141,11 @@ constexpr int kDecodeShortMaxSplits = 32;
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 // The decode step on the LDS-streamed kernel (bf16, groups of 4 query heads,
 // d = 128): append, the copy and the base token in one streaming pass, then
-// the LSE merge of both kinds (which advances cache_len).  Its key chunks (a
-// power of two, at least 2048 keys) aim at about kXattnLdsDecodeItems items
-// per step, and it is taken only when that asks for chunks of at least
-// kXattnLdsDecodeMinChunk keys: smaller steps go to the lane-parallel kernel, whose many resident
-// workgroups hide latency better than a per-CU pipeline with short items.
-constexpr int64_t kXattnLdsDecodeItems = 8192;
-constexpr int kXattnLdsDecodeMinChunk = 1536;
+// the LSE merge of both kinds (which advances cache_len).  It is taken when
+// the step holds at least kXattnLdsDecodeMinKeys keys over all streams (at
+// max_len): smaller steps go to the lane-parallel kernel, whose many
+// resident workgroups hide latency better than one pipeline per CU.
+constexpr int64_t kXattnLdsDecodeMinKeys = int64_t(12) << 20;
 hipError_t launch_decode_lds(const DecodeParams& p, hipStream_t s);
 // LSE merge of decode partials [B][Hq][2][n_split][rec] into o_out and o,
 // then cache_len[b] += 1 for every valid sequence.

@@ -68,13 +68,29 @@ __device__ __forceinline__ void block_barrier()
     asm volatile("" ::: "memory");
 }
 
-// One item: chunk s of stream j = (KV head g, 4-head block hb) of sequence b,
-// keys lo .. hi (hi <= P, the copy's position), nst stages.  In decode, P is
-// the cache length L and `win` marks the chunks that hold keys of the base
-// token's window [wlo, L].  Key indices fit 32 bits (positions are below
-// 2^31); only cache offsets need 64.
+__device__ __forceinline__ int64_t readlane64(int64_t x, int l)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), l);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Keys per workgroup when `total` keys are cut into nwg equal runs (at least
+// kXattnLdsSegMin, so that a short call uses fewer workgroups).
+__device__ __forceinline__ int64_t run_keys(int64_t total, int nwg)
+{
+    const int64_t e = (total + nwg - 1) / nwg;
+    return e > kXattnLdsSegMin ? e : kXattnLdsSegMin;
+}
+
+// One segment: keys lo .. hi (len keys) of stream j = (KV head g, 4-head
+// block hb) of sequence b, hi <= P (the copy's position), nst stages, its
+// partial records under record id `id`.  In decode, P is the cache length L
+// and `win` marks a segment that holds keys of the base token's window
+// [wlo, L].  Key indices fit 32 bits (positions are below 2^31); cache
+// offsets and positions in the launch's key order take 64.
 struct Item {
-    int b, g, hb, s, nst;
+    int b, g, hb, id, nst, len;
     int lo, hi, wlo;
     bool win;
 };
@@ -84,10 +100,9 @@ struct Item {
 // new token's K/V are already in slot L), and the base token's 4 heads ride
 // along as query columns 4..7 of the same MFMAs (their keys are a subset of
 // the copy's), leaving a second partial per head for the chunks that hold
-// its window.
-// The chunk is a power of two, 2^cshift keys.
+// its window.  Record ids of this launch start at rbase.
 template <int D, typename PT>
-__global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, int cshift, PosBlock pos)
+__global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, int rbase, PosBlock pos)
 {
     constexpr bool DEC = std::is_same<PT, DecodeParams>::value;
     using R = LinePairTile<D>;
@@ -103,8 +118,9 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
     // beta_out (then q, alpha, beta of the base token in decode)
     constexpr int NREG = DEC ? 6 : 3;
     constexpr int HRE = 4 * D;            // elements per region
-    constexpr int NST = D / 64 + 1;       // partial store instructions per wave, item and kind
+    constexpr int NST = D / 64 + 1;       // partial store instructions per wave, segment and kind
     constexpr int REC = D + kXattnLdsRecPad, AOFF = kXattnLdsRecPad;   // partial record layout
+    constexpr int KINDS = DEC ? 2 : 1;    // records per head and id: the copy (then the base token)
     constexpr int NH = DEC ? 8 : 4;       // live query columns
     static_assert(SLOTE * 2 == kStageBytes && LPS == 16, "stage shape");
     __shared__ __align__(16) uint16_t lds[2 * SLOTE];
@@ -115,14 +131,14 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, gq = lane >> 4;
     const int hblocks = (a.Hq / a.Hkv) / 4;
-    const int S = a.Hkv * hblocks;        // streams (items per chunk index) of a sequence
+    const int S = a.Hkv * hblocks;        // streams of a sequence
     const uint16_t* k_cache = (const uint16_t*)a.k_cache;
     const uint16_t* v_cache = (const uint16_t*)a.v_cache;
 
-    // lane i < nb: sequence b0 + i, its copy position and its item count
+    // lane i < nb: sequence b0 + i, its copy position and its key count
     int Lv = -1;
     if constexpr (DEC) {
-        // a length outside [0, max_len] gives the sequence no items (the
+        // a length outside [0, max_len] gives the sequence no keys (the
         // merge turns it into NaN outputs and leaves cache_len alone)
         const int Lraw = lane < nb ? a.cache_len[b0 + lane] : -1;
         if (blockIdx.x == 0 && tid < nb) a.ws_len[b0 + tid] = Lraw;
@@ -131,56 +147,80 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
         Lv = lane < nb ? (int)pos.v[lane] : -1;
         if (blockIdx.x == 0 && tid < nb) a.ws_len[b0 + tid] = Lv;
     }
-    // Item order: every stream's full chunks first (chunks 0 .. nch - 2, by
-    // sequence, stream, chunk), then every stream's last chunk, which may be
-    // short.  Round-robin over that order gives each workgroup an equal
-    // count of full items to within one, and the short last chunks go first
-    // to the workgroups that drew one full item fewer.
-    const int nchv = Lv >= 0 ? (Lv >> cshift) + 1 : 0;   // chunks per stream of sequence b0 + lane
-    const int cntF = nchv > 0 ? (nchv - 1) * S : 0;
-    const int cntT = nchv > 0 ? S : 0;
-    int inclF = cntF, inclT = cntT;      // inclusive prefix sums over the lanes
+    // Work split: the keys of every stream of the launch, in (sequence,
+    // stream, key) order, cut into nwg runs of E consecutive keys; workgroup
+    // w takes run w, which may cross from one stream into the next (each
+    // piece is a segment with its own records).  Every workgroup gets the
+    // same number of keys to within one, whatever the mix of lengths, and
+    // writes records for only one or a few segments.  A segment of stream t
+    // (t = sequence * S + stream, counted in the launch) in run w has record
+    // id rbase + t + w: those of one stream are consecutive, and no two
+    // segments share one.
+    const int64_t cnt = Lv >= 0 ? (int64_t)(Lv + 1) * S : 0;   // keys of sequence b0 + lane
+    int64_t incl = cnt;                   // inclusive prefix sum over the lanes
 #pragma unroll
     for (int x = 1; x < 64; x <<= 1) {
-        const int tf = __shfl_up(inclF, x), tt = __shfl_up(inclT, x);
-        if (lane >= x) {
-            inclF += tf;
-            inclT += tt;
+        const int64_t t = __shfl_up(incl, x);
+        if (lane >= x) incl += t;
+    }
+    const int64_t excl = incl - cnt;
+    const int64_t total = readlane64(incl, 63);
+    const int64_t E = run_keys(total, gridDim.x);
+    if (blockIdx.x == 0) {
+        // each stream's records for the merge: first id, first id holding
+        // keys of the base token's window (decode), last id
+        for (int t0 = 0; t0 < nb * S; t0 += 256) {
+            const int t = t0 + tid;
+            const int bl = t / S < 63 ? t / S : 63;
+            const int L = __shfl(Lv, bl);
+            const int64_t ex = __shfl(excl, bl);
+            if (t < nb * S) {
+                int32_t* rg = a.ws_rng + ((int64_t)b0 * S + t) * 3;
+                if (L < 0) {
+                    rg[0] = 0;
+                    rg[1] = 0;
+                    rg[2] = -1;
+                } else {
+                    const int64_t P = ex + (int64_t)(t - bl * S) * (L + 1);
+                    int wlo = 0;
+                    if constexpr (DEC) wlo = L - a.window + 1 > 0 ? L - a.window + 1 : 0;
+                    rg[0] = rbase + t + (int)(P / E);
+                    rg[1] = rbase + t + (int)((P + wlo) / E);
+                    rg[2] = rbase + t + (int)((P + L) / E);
+                }
+            }
         }
     }
-    const int exclF = inclF - cntF, exclT = inclT - cntT;
-    const int nfull = __builtin_amdgcn_readlane(inclF, 63);
-    const int total = nfull + __builtin_amdgcn_readlane(inclT, 63);
-    const int nwg = gridDim.x;
+    // this workgroup's run: keys beg .. beg + run - 1 of the order (below
+    // 2^30 keys: the launchers check it)
+    const int64_t beg = (int64_t)blockIdx.x * E;
+    const int run = (int)(beg + E < total ? E : total - beg);
 
-    auto item_of = [&](int k, Item& it) {
-        // the item's sequence: the last lane whose exclusive prefix is <= k
-        const bool full = k < nfull;
-        const int kk = full ? k : k - nfull;
-        const uint64_t m = __ballot(lane < nb && (full ? exclF : exclT) <= kk);
+    // the segment that starts at key rel of the run
+    auto item_of = [&](int rel, Item& it) {
+        const int64_t at = beg + rel;
+        // its sequence: the last lane whose exclusive prefix is <= at (a
+        // lane with no keys is never the last: the next one shares its prefix)
+        const uint64_t m = __ballot(lane < nb && excl <= at);
         const int bl = __popcll(m) - 1;
         it.b = b0 + bl;
         const int L = __builtin_amdgcn_readlane(Lv, bl);
-        const int nch = (L >> cshift) + 1;
-        const int r = kk - __builtin_amdgcn_readlane(full ? exclF : exclT, bl);
-        int j;
-        if (full) {
-            j = r / (nch - 1);
-            it.s = r - j * (nch - 1);
-        } else {
-            j = r;
-            it.s = nch - 1;
-        }
+        // the key's place among the sequence's S * (L + 1) keys (below 2^32:
+        // the launchers check S * cap)
+        const uint32_t off = (uint32_t)(at - readlane64(excl, bl));
+        const int j = (int)(off / (uint32_t)(L + 1));
         it.g = j / hblocks;
         it.hb = j - it.g * hblocks;
-        it.lo = it.s << cshift;
-        it.hi = L - it.lo < (1 << cshift) ? L : it.lo + (1 << cshift) - 1;
+        it.lo = (int)(off - (uint32_t)j * (uint32_t)(L + 1));
+        it.hi = run - rel > L - it.lo ? L : it.lo + (run - rel) - 1;
+        it.len = it.hi - it.lo + 1;
         it.nst = (it.hi - it.lo) / SK + 1;
+        it.id = rbase + bl * S + j + (int)blockIdx.x;
         it.wlo = 0;
         it.win = false;
         if constexpr (DEC) {
             it.wlo = L - a.window + 1 > 0 ? L - a.window + 1 : 0;
-            it.win = it.s >= (it.wlo >> cshift);
+            it.win = it.hi >= it.wlo;
         }
     };
 
@@ -236,29 +276,30 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
         }
     };
 
-    int kc = blockIdx.x;          // the item being consumed, and its stage
-    if (kc >= total) return;
+    if (run <= 0) return;
+    int pc = 0;                   // the segment being consumed starts at key pc of the run
     Item ci;
-    item_of(kc, ci);
-    // the consumed item's sequence, head block and chunk only address its
-    // partial records: vector registers, like the issue cursor's item below
-    asm volatile("" : "+v"(ci.b), "+v"(ci.g), "+v"(ci.hb), "+v"(ci.s));
-    int sc = 0, qc = 0;           // qc: parity of ci's row area
-    Item ii = ci;                 // the item being issued, its next stage and row area
-    int ki = kc, si = 0, qi = 0;
+    item_of(pc, ci);
+    // its record id only addresses the records: a vector register, like the
+    // issue cursor's segment below
+    asm volatile("" : "+v"(ci.id));
+    int sc = 0, qc = 0;           // its stage; qc: parity of its row area
+    Item ii = ci;                 // the segment being issued, its next stage and row area
+    int pi = pc, si = 0, qi = 0;
     bool more = true;             // the issue cursor has stages left
     auto advance_issue = [&]() {
         if (++si < ii.nst) return;
-        ki += nwg;
-        if (ki >= total) {
+        pi += ii.len;
+        if (pi >= run) {
             more = false;
             return;
         }
-        item_of(ki, ii);
-        // the issue cursor's item only feeds address arithmetic: it is kept
-        // in vector registers (the same value in every lane), which leaves
-        // the scalar file room for the rest without spilling (its stage
-        // count stays scalar: the cursor's branches must stay uniform)
+        item_of(pi, ii);
+        // the issue cursor's segment only feeds address arithmetic: it is
+        // kept in vector registers (the same value in every lane), which
+        // leaves the scalar file room for the rest without spilling (its
+        // stage count and length stay scalar: the cursor's branches must
+        // stay uniform)
         asm volatile("" : "+v"(ii.b), "+v"(ii.g), "+v"(ii.hb), "+v"(ii.lo), "+v"(ii.hi));
         si = 0;
         qi ^= 1;
@@ -434,12 +475,10 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
         wait_lgkm0();
         block_barrier();
         {
-            const int h0 = ci.g * (a.Hq / a.Hkv) + ci.hb * 4;
             const int nkind = DEC && ci.win ? 2 : 1;
             for (int kind = 0; kind < nkind; ++kind) {
                 const int col = 4 * kind + wv;
-                const int64_t head = (int64_t)ci.b * a.Hq + h0 + wv;
-                float* o = a.ws_part + ((DEC ? 2 * head + kind : head) * a.n_split + ci.s) * REC;
+                float* o = a.ws_part + (((int64_t)ci.id * KINDS + kind) * 4 + wv) * REC;
                 float mw[4], M = kNegBig;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
@@ -465,10 +504,10 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
             after0 += NST * nkind;
             after1 += NST * nkind;
         }
-        kc += nwg;
-        if (kc >= total) break;
-        item_of(kc, ci);
-        asm volatile("" : "+v"(ci.b), "+v"(ci.g), "+v"(ci.hb), "+v"(ci.s));
+        pc += ci.len;
+        if (pc >= run) break;
+        item_of(pc, ci);
+        asm volatile("" : "+v"(ci.id));
         sc = 0;
         qc ^= 1;
     }
@@ -511,69 +550,79 @@ int cu_count()
     return v;
 }
 
-// log2 of a power-of-two chunk of at most 2^30 keys, else -1.
-int chunk_shift(int chunk)
-{
-    if (chunk < 1 || chunk > (1 << 30) || (chunk & (chunk - 1))) return -1;
-    int s = 0;
-    while ((1 << s) < chunk) ++s;
-    return s;
-}
-
 // Key indices travel as 32-bit integers in the kernel: every cached key,
 // plus a stage of overrun, must stay below 2^31.
 constexpr int64_t kLdsMaxCap = INT32_MAX - 4096;
+
+// Workgroups of one launch over at most `keys` keys in all: one per CU,
+// fewer when runs of kXattnLdsSegMin keys do not fill them; 0 when a run
+// would not fit the kernel's 32-bit key counts.
+unsigned lds_grid(int64_t keys)
+{
+    int64_t g = cu_count();
+    if (g > kXattnLdsMaxGrid) g = kXattnLdsMaxGrid;
+    const int64_t need = (keys + kXattnLdsSegMin - 1) / kXattnLdsSegMin;
+    if (need < g) g = need;
+    if (g < 1) g = 1;
+    return (keys + g - 1) / g < (int64_t(1) << 30) ? (unsigned)g : 0u;
+}
 
 }  // namespace
 
 hipError_t launch_xattn_lds(const XattnParams& p, hipStream_t st)
 {
-    const int cshift = chunk_shift(p.chunk);
-    if (p.rec != p.D + kXattnLdsRecPad || cshift < 0 || p.cap > kLdsMaxCap) return hipErrorInvalidValue;
-    const int hblocks = (p.Hq / p.Hkv) / 4;
-    const int ncu = cu_count();
+    const int S = p.Hkv * ((p.Hq / p.Hkv) / 4);
+    if (p.rec != p.D + kXattnLdsRecPad || p.cap > kLdsMaxCap || (int64_t)S * p.cap > UINT32_MAX)
+        return hipErrorInvalidValue;
+    const int64_t region = xattn_lds_region(p.B, S);
+    if (xattn_lds_records(p.B, S) >= INT32_MAX) return hipErrorInvalidValue;
     for (int b0 = 0; b0 < p.B; b0 += kPosPerLaunch) {
         const int nb = p.B - b0 < kPosPerLaunch ? p.B - b0 : kPosPerLaunch;
         PosBlock pos;
-        for (int i = 0; i < kPosPerLaunch; ++i) pos.v[i] = i < nb ? p.pos[b0 + i] : 0;
-        // items of this launch, at most (every position at T - 1)
-        const int64_t max_items = (int64_t)nb * p.Hkv * hblocks * p.n_split;
-        const unsigned grid = (unsigned)(max_items < ncu ? max_items : ncu);
+        int64_t keys = 0;
+        for (int i = 0; i < kPosPerLaunch; ++i) {
+            pos.v[i] = i < nb ? p.pos[b0 + i] : 0;
+            if (i < nb) keys += (pos.v[i] + 1) * S;
+        }
+        const unsigned grid = lds_grid(keys);
+        if (!grid) return hipErrorInvalidValue;
+        const int rbase = (int)(b0 / kPosPerLaunch * region);
         if (p.D == 64)
-            hipLaunchKernelGGL((xattn_lds_kernel<64, XattnParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, cshift, pos);
+            hipLaunchKernelGGL((xattn_lds_kernel<64, XattnParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, rbase, pos);
         else
-            hipLaunchKernelGGL((xattn_lds_kernel<128, XattnParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, cshift,
+            hipLaunchKernelGGL((xattn_lds_kernel<128, XattnParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, rbase,
                                pos);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    return launch_merge(p, st);
+    return launch_lds_merge(p, st);
 }
 
 hipError_t launch_decode_lds(const DecodeParams& p, hipStream_t st)
 {
-    const int cshift = chunk_shift(p.chunk);
-    if (p.D != 128 || p.rec != p.D + kXattnLdsRecPad || cshift < 0 || p.cap > kLdsMaxCap)
+    const int S = p.Hkv * ((p.Hq / p.Hkv) / 4);
+    const int nb_max = p.B < kPosPerLaunch ? p.B : kPosPerLaunch;
+    if (p.D != 128 || p.rec != p.D + kXattnLdsRecPad || p.cap > kLdsMaxCap || (int64_t)S * p.cap > UINT32_MAX ||
+        xattn_lds_records(p.B, S) >= INT32_MAX || !lds_grid((int64_t)nb_max * S * (p.max_len + 1)))
         return hipErrorInvalidValue;
     // the new token's K/V into slot L first: the streaming kernel reads
     // every key of [0, L] from the cache
     hipLaunchKernelGGL((decode_append_kernel<128>), dim3(p.B), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int hblocks = (p.Hq / p.Hkv) / 4;
-    const int ncu = cu_count();
+    const int64_t region = xattn_lds_region(p.B, S);
     PosBlock unused{};
     for (int b0 = 0; b0 < p.B; b0 += kPosPerLaunch) {
         const int nb = p.B - b0 < kPosPerLaunch ? p.B - b0 : kPosPerLaunch;
-        // items of this launch, at most (every length at max_len)
-        const int64_t max_items = (int64_t)nb * p.Hkv * hblocks * p.n_split;
-        const unsigned grid = (unsigned)(max_items < ncu ? max_items : ncu);
-        hipLaunchKernelGGL((xattn_lds_kernel<128, DecodeParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, cshift,
+        // keys of this launch, at most (every length at max_len)
+        const unsigned grid = lds_grid((int64_t)nb * S * (p.max_len + 1));
+        const int rbase = (int)(b0 / kPosPerLaunch * region);
+        hipLaunchKernelGGL((xattn_lds_kernel<128, DecodeParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, rbase,
                            unused);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    return launch_decode_merge(p, st);
+    return launch_lds_merge(p, st);
 }
 
 }  // namespace orthros

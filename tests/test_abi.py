@@ -95,41 +95,61 @@ def test_decode_bad_arguments():
     assert call(cap=100, hint=50, wsb=8) == -6
 
 
-@pytest.mark.parametrize("B,hint,lds", [(16, 132095, True), (4, 32767, False), (1, 4095, False), (1, 4096, False)],
-                         ids=["B16-128K-lds", "B4-32K-lane", "B1-4K-short", "B1-4K-plus-one-lane"])
+@pytest.mark.parametrize("B,hint,lds", [(16, 132095, True), (4, 32767, False), (1, 4095, False), (1, 4096, False),
+                                         (80, 24575, True), (11, 131071, False), (12, 131071, True)],
+                         ids=["B16-128K-lds", "B4-32K-lane", "B1-4K-short", "B1-4K-plus-one-lane",
+                              "B80-24K-lds-two-launches", "B11-128K-lane", "B12-128K-lds-at-threshold"])
 def test_decode_workspace_layout(B, hint, lds):
     """The decode workspace: 256-byte-aligned arrival counters and lengths,
-    then two kinds of split partials per (sequence, query head).  Long steps (bf16, 4-head groups,
-    d128, at least 1536-key chunks at about 8192 items) take the LDS-streamed
-    kernel's chunks -- the power of two nearest that -- and records of
-    d + 32 floats; shorter ones the lane kernel's power-of-two chunks (>= 256
-    keys, about 16384 workgroups) and records of d + 2 floats, or, up to 32
-    chunks of 128 keys, the one-launch short kernel's 128-key chunks and
-    records of d + 4 floats.  A workspace one
-    byte short is rejected before anything runs."""
+    then the partials.  Long steps (bf16, 4-head groups, d128, at least
+    12 * 2^20 keys over all streams) run on the LDS-streamed kernel: a
+    256-byte-aligned table of 3 record ids per stream, then records of
+    2 kinds x 4 heads x (d + 32) floats, ids for every stream of a launch
+    of up to 64 sequences plus one per workgroup (512 at most).  Shorter
+    steps take two kinds of split partials per (sequence, query head): the
+    lane kernel's power-of-two chunks (>= 256 keys, about 16384 workgroups)
+    and records of d + 2 floats, or, up to 32 chunks of 128 keys, the
+    one-launch short kernel's 128-key chunks and records of d + 4 floats.  A
+    workspace one byte short is rejected before anything runs."""
     Hq, Hkv, d = 32, 8, 128
     desc = mk(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=128, dtype=binding.BF16)
-    keys, streams = hint + 1, B * Hkv
-    want = -(-keys * streams // 8192)
+    keys, S = hint + 1, Hkv * (Hq // Hkv // 4)
+    streams = B * S
+    assert (keys * streams >= 12 << 20) == lds
+    counters = -(-B * (S + 1) * 4 // 256) * 256      # one per head block, one per sequence
+    lens = -(-B * 4 // 256) * 256
     if lds:
-        assert want >= 1536
-        chunk, rec = 1024, d + 32
-        while chunk * 3 // 2 < want:
-            chunk *= 2
-    elif keys <= 32 * 128:
-        chunk, rec = 128, d + 4                  # short bf16 steps: one launch over 128-key chunks
+        ids = -(-B // 64) * (min(B, 64) * S + 512)
+        need = counters + lens + -(-streams * 3 * 4 // 256) * 256 + ids * 2 * 4 * (d + 32) * 4
     else:
-        chunk, rec = 256, d + 2
-        while chunk < -(-keys * streams // 16384):
-            chunk *= 2
-    n_split = -(-keys // chunk)
-    counters = -(-B * (Hkv * (Hq // Hkv // 4) + 1) * 4 // 256) * 256      # one per head block, one per sequence
-    need = counters + -(-B * 4 // 256) * 256 + B * Hq * 2 * n_split * rec * 4
+        if keys <= 32 * 128:
+            chunk, rec = 128, d + 4              # short bf16 steps: one launch over 128-key chunks
+        else:
+            chunk, rec = 256, d + 2
+            while chunk < -(-keys * streams // 16384):
+                chunk *= 2
+        n_split = -(-keys // chunk)
+        need = counters + lens + B * Hq * 2 * n_split * rec * 4
     assert binding.decode_workspace_size(desc, hint) == need
     p = ctypes.c_void_p(FAKE)
     st = binding.lib().orthros_decode_step(ctypes.byref(desc), p, p, p, p, p, p, p, p, p, p, hint + 1, p, hint, p, p,
                                            p, need - 1, None)
     assert st == -6
+
+
+def test_prefill_workspace_layout():
+    """The prefill workspace of the separate cross-attention (orthros_global_xattn)
+    on the LDS-streamed kernel (bf16, 4-head groups): lengths, the record-id
+    table (3 per stream), then records of 4 heads x (d + 32) floats for every
+    stream of a launch of up to 64 sequences plus 512 -- independent of T.
+    The fused prefill (window <= 129) may need more: its size is the larger."""
+    for B, Hq, Hkv, d in ((2, 32, 8, 128), (70, 16, 2, 64)):
+        desc = mk(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=200, dtype=binding.BF16)
+        S = Hkv * (Hq // Hkv // 4)
+        ids = -(-B // 64) * (min(B, 64) * S + 512)
+        need = -(-B * 4 // 256) * 256 + -(-B * S * 3 * 4 // 256) * 256 + ids * 4 * (d + 32) * 4
+        for T in (1000, 131072):
+            assert binding.prefill_workspace_size(desc, T) == need
 
 
 def test_workspace_sizes():

@@ -120,15 +120,15 @@ def test_decode_short_kernel_edge(keys):
                                                       (80, 32, 20000, 24000, 1, 128),
                                                       (32, 32, 66000, 70000, 1, 5000),
                                                       (16, 64, 66000, 70000, 1, 128)],
-                         ids=["B32-70K", "B80-24K-two-launches", "B32-70K-window-over-chunks",
+                         ids=["B32-70K", "B80-24K-two-launches", "B32-70K-window-5000",
                               "B16-70K-G8-two-head-blocks"])
 def test_decode_lds_kernel_long_histories(B, Hq, len_lo, len_hi, steps, w):
     """bf16, 8 KV heads, d128: 32 sequences (32 query heads) with histories
     up to 70K keys, 16 with 64 query heads (two 4-head blocks per KV head),
     or 80 (two launches of 64 and 16 sequences) up to 24K -- large enough
-    that the step runs on the LDS-streamed kernel (2048-key chunks).  Lengths include 0 and the edges of a 128-key stage and of a
-    chunk; the base token's window straddles a chunk boundary (w = 128) or
-    spans several chunks (w = 5000).  Unused cache slots hold the NaN
+    that the step runs on the LDS-streamed kernel (equal runs of the step's
+    keys per workgroup).  Lengths include 0 and the edges of a 128-key
+    stage; windows of 128 and 5000 keys.  Unused cache slots hold the NaN
     sentinel, and one sequence's length is past the hint.  Every step
     against the oracle, caches and lengths in full."""
     Hkv, d = 8, 128
@@ -153,19 +153,18 @@ def test_decode_lds_kernel_long_histories(B, Hq, len_lo, len_hi, steps, w):
                  x["alpha_out"], x["beta_out"])
     from phase_aware_swa_amd import binding
     from phase_aware_swa_amd.runner import desc_for
-    # the LDS-streamed kernel's workspace: power-of-two chunks for about 8192
-    # items, records of d + 32 floats
-    keys = max_hint + 1
-    want = -(-keys * B * Hkv * (Hq // Hkv // 4) // 8192)
-    assert want >= 1536
-    chunk = 1024
-    while chunk * 3 // 2 < want:
-        chunk *= 2
-    n_split = -(-keys // chunk)
+    # the LDS-streamed kernel's workspace (at least 12 * 2^20 keys over all
+    # streams): counters, lengths, 3 record ids per stream, then 2 x 4
+    # records of d + 32 floats per id (every stream of a launch of up to 64
+    # sequences, plus 512)
+    S = Hkv * (Hq // Hkv // 4)
+    assert (max_hint + 1) * B * S >= 12 << 20
     len_bytes = -(-B * 4 // 256) * 256         # the per-sequence lengths, 256-byte aligned
-    cnt_bytes = -(-B * (Hkv * (Hq // Hkv // 4) + 1) * 4 // 256) * 256     # arrival counters
-    assert binding.decode_workspace_size(desc_for(cfg), max_hint) == (cnt_bytes + len_bytes +
-                                                                      B * Hq * 2 * n_split * (d + 32) * 4)
+    cnt_bytes = -(-B * (S + 1) * 4 // 256) * 256     # arrival counters
+    rng_bytes = -(-B * S * 3 * 4 // 256) * 256
+    ids = -(-B // 64) * (min(B, 64) * S + 512)
+    assert binding.decode_workspace_size(desc_for(cfg), max_hint) == (cnt_bytes + len_bytes + rng_bytes +
+                                                                      ids * 2 * 4 * (d + 32) * 4)
     kc, vc, lc = xc["k_cache"], xc["v_cache"], xc["cache_len"].clone()
     for s in range(steps):
         say(f"decode lds long histories: step {s}")

@@ -14,10 +14,11 @@ of its row, compared bit for bit (tests/probe_util.py).  Kernels covered:
     d 128 and 64), copies on segment edges and below T-1;
   prefill, generic sliding-window kernel + LDS-streamed cross-attention
     (w > 129), and orthros_global_xattn on its own;
-  decode, LDS-streamed kernel (32 sequences, histories around 64K keys,
-    2048-key chunks): the base token's window straddling chunk boundaries at
-    w = 128, spanning several chunks at w = 4096 and 5000, and the copy over
-    the whole history with marked keys at every chunk edge;
+  decode, LDS-streamed kernel (32 sequences; each workgroup takes an equal
+    run of the step's keys, in (sequence, KV head, key) order): the base
+    token's window straddling run boundaries at w = 128 and spanning several
+    runs at w = 4096 and 5000, and the copy over ~64K-key histories with
+    marked keys on both sides of every run boundary;
   decode, lane-parallel kernel (short histories, groups of 2 and 4, d 128
     and 64, windows 1, 128 and 300).
 (MI355X only.)"""
@@ -55,32 +56,54 @@ def onehot_rows(cols, d, dtype=BF16):
 
 def decode_split_of(B, Hq, Hkv, d, hint):
     """(uses the LDS-streamed kernel, workspace bytes) of a bf16 decode step,
-    from the split rule of orthros_decode_step: about 8192 items of
-    power-of-two chunks (at least 1536 keys asked for) on the LDS-streamed
-    kernel, else 128-key chunks when that makes at most 32 (the one-launch
-    kernel), else power-of-two chunks of at least 256 keys for about 16384
-    workgroups; records of d + 32, d + 4 or d + 2 floats; arrival counters
-    and lengths first."""
+    from the split rule of orthros_decode_step: the LDS-streamed kernel when
+    the step holds at least 12 * 2^20 keys over all streams at max_len
+    (record-id table, then 2 x 4 records of d + 32 floats per id: every
+    stream of a launch of up to 64 sequences plus 512), else 128-key chunks
+    when that makes at most 32 (the one-launch kernel), else power-of-two
+    chunks of at least 256 keys for about 16384 workgroups (records of d + 4
+    or d + 2 floats, two kinds per head); arrival counters and lengths
+    first."""
     G = Hq // Hkv
     hpw = 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
-    streams = B * Hkv * (G // hpw)
+    S = Hkv * (G // hpw)
+    streams = B * S
     keys = hint + 1
-    want = -(-keys * streams // 8192)
-    lds = G % 4 == 0 and d == 128 and want >= 1536
+    lds = G % 4 == 0 and d == 128 and keys * streams >= 12 << 20
+    head = -(-B * (S + 1) * 4 // 256) * 256 + -(-B * 4 // 256) * 256
     if lds:
-        chunk = 1024
-        while chunk * 3 // 2 < want:
-            chunk *= 2
-    elif keys <= 32 * 128:                       # short steps: one launch over 128-key chunks
+        ids = -(-B // 64) * (min(B, 64) * S + 512)
+        return True, head + -(-streams * 3 * 4 // 256) * 256 + ids * 2 * 4 * (d + 32) * 4
+    if keys <= 32 * 128:                         # short steps: one launch over 128-key chunks
         chunk = 128
     else:
         chunk, need = 256, -(-keys * streams // 16384)
         while chunk < need:
             chunk *= 2
-    rec = d + (32 if lds else 4 if chunk == 128 else 2)
+    rec = d + (4 if chunk == 128 else 2)
     n_split = -(-keys // chunk)
-    counters = -(-B * (Hkv * (G // hpw) + 1) * 4 // 256) * 256
-    return lds, counters + -(-B * 4 // 256) * 256 + B * Hq * 2 * n_split * rec * 4
+    return False, head + B * Hq * 2 * n_split * rec * 4
+
+
+def lds_run_starts(lens, S, hint):
+    """Where the LDS-streamed decode kernel's runs start, per (sequence,
+    stream): the keys of a step with cache lengths `lens` (the new keys
+    included) in (sequence, stream, key) order, cut into equal runs of
+    E = max(ceil(total / grid), 256) keys, grid = min(CUs, 512,
+    ceil(B * S * (hint + 1) / 256)).  Returns {(b, stream): [keys]}."""
+    B = len(lens)
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = max(1, min(ncu, 512, -(-B * S * (hint + 1) // 256)))
+    total = sum((L + 1) * S for L in lens)
+    E = max(-(-total // grid), 256)
+    starts, P = {}, 0
+    for b, L in enumerate(lens):
+        for j in range(S):
+            n = L + 1
+            first = -(-P // E) * E                      # the first run start at or after P
+            starts[(b, j)] = list(range(first - P, n, E))
+            P += n
+    return starts
 
 
 # ------------------------------------------------------------------ prefill
@@ -187,25 +210,33 @@ def test_window_one_and_first_position_exact(Hq, Hkv):
 
 # ------------------------------------------------------------------- decode
 
-def decode_probe(B, Hq, Hkv, d, w, lens, steps, seed, marked=False, expect_lds=None):
+def decode_probe(B, Hq, Hkv, d, w, lens, steps, seed, marked=False, expect_lds=None, hint=None):
     """Decode steps from histories `lens` with one-hot V (every key, or in
-    `marked` mode only keys 0 and 1, the two keys either side of every
-    2048-key boundary and the last keys of the history up to the step's new
-    key, each with a column of its own).  Every step's o and o_out against
-    count / |S|; the caches and lengths byte for byte."""
+    `marked` mode only keys 0 and 1, the two keys either side of every run
+    boundary of the LDS-streamed kernel in any stream of the sequence at any
+    step, and the last keys of the history up to the step's new key, each
+    with a column of its own).  Every step's o and o_out against count / |S|;
+    the caches and lengths byte for byte.  `hint` (max_len_hint) defaults to
+    the longest history at the last step."""
     cfg = dict(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=w, dtype=BF16)
     say(f"decode probe {cfg} lens[:12]={lens[:12]} steps={steps} marked={marked}")
     lens_t = torch.tensor(lens, dtype=torch.int64)
-    cap = int(lens_t.max()) + steps + 3
+    hint = int(lens_t.max()) + steps - 1 if hint is None else hint
+    cap = max(int(lens_t.max()) + steps + 3, hint + 1)
     sh = shifts(B, Hkv)
     slot = torch.arange(cap)
     if marked:
         # column of each marked slot per sequence, -1 for unmarked (zero rows)
         col = torch.full((B, cap), -1, dtype=torch.int64)
+        S = Hkv * (Hq // Hkv // 4)
+        edges = [set() for _ in range(B)]
+        for s in range(steps):
+            for (b, j), ks in lds_run_starts([L + s for L in lens], S, hint).items():
+                edges[b] |= {k + e for k in ks if k > 0 for e in (-1, 0)}
         for b, L in enumerate(lens):
             last = L + steps - 1                        # the last step's new key
-            keys = {0, 1}
-            keys |= {e + s for e in range(2048, last + 1, 2048) for s in (-1, 0)}
+            keys = {0, 1} | edges[b]
+            assert len(keys) <= d - 16, "too many marked run edges for the columns"
             keys |= set(range(max(0, last - (d - 1 - len(keys)) + 1), last + 1))
             keys = sorted(k for k in keys if k <= last)[:d]
             for c, k in enumerate(keys):
@@ -227,7 +258,6 @@ def decode_probe(B, Hq, Hkv, d, w, lens, steps, seed, marked=False, expect_lds=N
     q_out = torch.randn(steps, B, Hq, d, generator=g, device=dev).to(BF16)
     z = torch.zeros(Hq, d, dtype=BF16, device=dev)
     clen = lens_t.to(torch.int32).to(dev)
-    hint = int(lens_t.max()) + steps - 1
     dec = Decode(cfg, kc, vc, clen, hint, z, z, z, z)
     if expect_lds is not None:
         from phase_aware_swa_amd import binding
@@ -266,38 +296,56 @@ def decode_probe(B, Hq, Hkv, d, w, lens, steps, seed, marked=False, expect_lds=N
     say(f"decode probe ok ({und} elements next to a bf16 midpoint)")
 
 
-def lds_lens(B, deltas, base=65536):
-    """Histories for the LDS-streamed decode kernel: the window-straddling
-    deltas past a 2048-key boundary first, then edge lengths, then the rest
-    spread below base."""
-    lens = [base + dl for dl in deltas]
-    lens += [0, 1, 127, 128, 2047, 2048, 2049, 4096 + 126]
+def lds_lens(B, base=65536):
+    """Histories for the LDS-streamed decode kernel: edge lengths first, then
+    the rest spread below base."""
+    lens = [0, 1, 127, 128, 129, 255, 256, 4096 + 126]
     g = torch.Generator().manual_seed(B)
     while len(lens) < B:
         lens.append(int(torch.randint(8192, base, (1,), generator=g)))
     return lens[:B]
 
 
-def test_probe_decode_lds_window_straddles_chunks():
-    """w = 128 on the LDS-streamed kernel: new keys at 0..126 past a
-    2048-key boundary put the window across it; two steps (the second
-    window holds the first step's appended key)."""
-    lens = lds_lens(32, [0, 1, 2, 63, 64, 100, 125, 126, 127, 128])
-    decode_probe(32, 32, 8, 128, 128, lens, 2, seed=330, expect_lds=True)
+def straddling_windows(lens, S, hint, w):
+    """(b, stream) pairs whose window [L - w + 1, L] holds a run start past
+    its first key at the first step."""
+    out = []
+    for (b, j), ks in lds_run_starts(lens, S, hint).items():
+        lo = max(0, lens[b] - w + 1)
+        if any(lo < k <= lens[b] for k in ks):
+            out.append((b, j))
+    return out
+
+
+def test_probe_decode_lds_window_straddles_runs():
+    """w = 128 on the LDS-streamed kernel with short histories (1-3K keys)
+    under a large max_len_hint (the kernel is chosen by the hint): runs of a
+    few thousand keys, so run boundaries fall inside many streams' windows;
+    two steps (the second window holds the first step's appended key)."""
+    g = torch.Generator().manual_seed(7)
+    lens = [0, 1, 127, 128, 129] + [int(x) for x in torch.randint(1000, 3000, (27,), generator=g)]
+    hint = 65535
+    assert len(straddling_windows(lens, 8, hint, 128)) >= 8
+    decode_probe(32, 32, 8, 128, 128, lens, 2, seed=330, expect_lds=True, hint=hint)
 
 
 @pytest.mark.parametrize("w", [4096, 5000])
-def test_probe_decode_lds_window_spans_chunks(w):
-    lens = lds_lens(32, [0, 5, 2047, 3000, 4095, 4096, 4200])
-    decode_probe(32, 32, 8, 128, w, lens, 1, seed=331, expect_lds=True)
+def test_probe_decode_lds_window_spans_runs(w):
+    """Windows longer than a run (runs of ~2K keys): the base token's
+    partials come from several workgroups."""
+    g = torch.Generator().manual_seed(w)
+    lens = [0, 1, 4095, 4096, 5000] + [int(x) for x in torch.randint(1000, 9000, (27,), generator=g)]
+    hint = 65535
+    assert len(straddling_windows(lens, 8, hint, w)) >= 32
+    decode_probe(32, 32, 8, 128, w, lens, 1, seed=331, expect_lds=True, hint=hint)
 
 
-def test_probe_decode_lds_copy_marked_chunk_edges():
-    """The copy over ~64K keys: only keys 0, 1, both sides of every 2048-key
+def test_probe_decode_lds_copy_marked_run_edges():
+    """The copy over ~64K keys: only keys 0, 1, both sides of every run
     boundary and the last keys carry a column, so a key dropped or doubled
-    at a chunk edge, or a stray read past the new key (a NaN sentinel),
-    changes the output."""
-    lens = lds_lens(32, [0, 1, 126, 127, 2046, 2047])
+    where one workgroup's run ends and the next begins, or a stray read past
+    the new key (a NaN sentinel), changes the output."""
+    lens = lds_lens(32)
     decode_probe(32, 32, 8, 128, 128, lens, 2, seed=332, marked=True, expect_lds=True)
 
 

@@ -6,10 +6,11 @@ copy's original position P) -- against the fp64 oracle, through the C ABI
 
 The caches are filled by plain copies of K/V ([B][T][Hkv][d] -> [B][Hkv][cap][d]),
 so only the cross-attention kernels run.  bf16 with 4-head groups takes the
-LDS-streamed MFMA kernel (stages of 128 keys at d = 128, 256 at d = 64, key
-chunks of a power of two >= 256); the other shapes take the lane-parallel
-chunk kernel.  Positions sit on both sides of pair (32), stage and chunk
-edges."""
+LDS-streamed MFMA kernel (stages of 128 keys at d = 128, 256 at d = 64; each
+workgroup takes an equal run of the launch's keys, at least 256, in
+(sequence, stream, key) order, so runs cross stream boundaries); the other
+shapes take the lane-parallel chunk kernel (power-of-two chunks).
+Positions sit on both sides of pair (32), stage and chunk edges."""
 import pytest
 import torch
 
@@ -46,7 +47,7 @@ def run_xattn_case(B, Hq, Hkv, d, T, out_pos, dtype=BF16, seed=0, cap_extra=3):
 @pytest.mark.parametrize("B,Hq,Hkv,d,T,pos", [
     (1, 4, 1, 128, 1, [0]),                      # one key
     (6, 4, 1, 128, 300, [0, 31, 32, 127, 128, 299]),   # pair and stage edges (d = 128: 128 keys)
-    (5, 8, 2, 64, 1000, [255, 256, 257, 511, 999]),    # stage and chunk edges (d = 64: 256 keys)
+    (5, 8, 2, 64, 1000, [255, 256, 257, 511, 999]),    # stage edges (d = 64: 256 keys)
     (3, 16, 4, 128, 3000, [2999, 1, 1500]),      # 4 heads per group, several blocks of 4
     (2, 32, 4, 128, 2500, [2047, 2048]),         # 8 heads per group: two 4-head blocks
     (2, 8, 2, 128, 1234, [1233, 600]),
@@ -61,15 +62,16 @@ def test_xattn_fp32():
 
 
 def test_xattn_more_sequences_than_one_launch():
-    """67 sequences: positions travel 64 per launch."""
+    """67 sequences: positions travel 64 per launch; short streams, so each
+    workgroup's run of 256 keys spans several of them."""
     g = torch.Generator().manual_seed(4)
     run_xattn_case(67, 4, 1, 128, 200, torch.randint(0, 200, (67,), generator=g).tolist(), seed=4)
 
 
 @pytest.mark.parametrize("d", [128, 64])
 def test_xattn_long_chunks(d):
-    """One stream over 300000 keys: chunks of 1024 keys, i.e. 8 (d = 128) or
-    4 (d = 64) stages per workgroup, and a ragged last chunk."""
+    """One stream over 300000 keys: runs of 1172 keys per workgroup (a
+    ragged last stage in each, at an offset that moves from run to run)."""
     run_xattn_case(1, 4, 1, d, 300000, [299999 - 77 * (d == 64)], seed=5 + d)
 
 

@@ -1,8 +1,8 @@
 """orthros_decode_step_noalloc (the decode step on the library's own scratch
 array, for callers that cannot allocate) against orthros_decode_step with a
 caller workspace: the same kernels, so outputs, caches and lengths must
-match bit for bit.  Two calls in a row, the second with a smaller input
-(MI355X only)."""
+match bit for bit.  Three calls in a row, each with a smaller workspace than
+the one before (MI355X only)."""
 import pytest
 import torch
 
@@ -42,14 +42,21 @@ def run_both(cfg, seed, steps):
 
 
 def test_noalloc_decode_matches_workspace_decode():
-    # first call: batch 16, 32/8 heads, histories of 98K-110K keys -- the
-    # LDS-streamed kernel, about 35 MB of partials in the scratch array
+    # first call: batch 11, 32/8 heads, histories of 100K-120K keys -- the
+    # lane-parallel kernel (just under the LDS-streamed kernel's threshold),
+    # about 43 MB of partials in the scratch array
+    lane = dict(batch=11, n_q_heads=32, n_kv_heads=8, head_dim=128, window=128, dtype=torch.bfloat16,
+                len_lo=100000, len_hi=120000, steps=2)
+    ws_lane = run_both(lane, seed=70, steps=2)
+    assert 32 << 20 < ws_lane <= 64 << 20
+    # second call, smaller workspace: batch 16, histories of 98K-110K keys --
+    # the LDS-streamed kernel, over what the first call left in the array
     big = dict(batch=16, n_q_heads=32, n_kv_heads=8, head_dim=128, window=128, dtype=torch.bfloat16,
                len_lo=98000, len_hi=110000, steps=2)
     ws_big = run_both(big, seed=71, steps=2)
-    assert 16 << 20 < ws_big <= 64 << 20
-    # second call, smaller: batch 3, 8/2 heads, short histories -- the
-    # lane-parallel kernel over what the first call left in the array
+    assert ws_big < ws_lane
+    # third call, smaller still: batch 3, 8/2 heads, short histories -- the
+    # one-launch short-history kernel
     small = dict(batch=3, n_q_heads=8, n_kv_heads=2, head_dim=128, window=128, dtype=torch.bfloat16,
                  len_lo=100, len_hi=3000, steps=2)
     ws_small = run_both(small, seed=72, steps=2)
