@@ -170,22 +170,21 @@ Split decode_split(const orthros_desc* d, int64_t max_len)
 {
     Split s;
     const int64_t keys = max_len + 1;
-    // the LDS-streamed kernel: enough keys over all streams to keep one
-    // pipeline per CU busy
-    const bool lds = orthros::xattn_lds_applies(dt_of(d), d->n_q_heads, d->n_kv_heads) && d->head_dim == 128 &&
-                     keys * streams_of(d) >= orthros::kXattnLdsDecodeMinKeys;
-    s.lds = lds;
-    if (lds) {
+    // short bf16 steps: one launch over 128-key chunks (latency-bound, so
+    // each workgroup reads its whole chunk in one round trip)
+    s.fused = d->dtype == ORTHROS_BF16 &&
+              keys <= (int64_t)orthros::kDecodeShortChunk * orthros::kDecodeShortMaxSplits;
+    // longer steps in bf16 with 4-head groups and d = 128: the LDS-streamed
+    // kernel (equal runs of the step's keys per workgroup)
+    s.lds = !s.fused && orthros::xattn_lds_applies(dt_of(d), d->n_q_heads, d->n_kv_heads) && d->head_dim == 128;
+    if (s.lds) {
         s.chunk = 0;
         s.n_split = 0;
         s.rec = d->head_dim + orthros::kXattnLdsRecPad;
         s.bytes = cnt_bytes(d) + len_bytes(d) + rng_bytes(d, true) + lds_record_bytes(d, 2, s.rec);
         return s;
     }
-    // short bf16 steps: one launch over 128-key chunks (latency-bound, so
-    // each workgroup reads its whole chunk in one round trip)
-    s.fused = !lds && d->dtype == ORTHROS_BF16 &&
-              keys <= (int64_t)orthros::kDecodeShortChunk * orthros::kDecodeShortMaxSplits;
+    // the rest on the lane-parallel kernel
     s.chunk = s.fused ? orthros::kDecodeShortChunk : pick_chunk(keys, streams_of(d), kDecodeTargetWgs);
     s.n_split = (int)((keys + s.chunk - 1) / s.chunk);
     s.rec = d->head_dim + (s.fused ? 4 : 2);

@@ -132,20 +132,18 @@ hipError_t launch_xattn_lds(const XattnParams& p, hipStream_t s);
 // into o_out (and in decode o, then cache_len[b] += 1).
 hipError_t launch_lds_merge(const XattnParams& p, hipStream_t s);
 hipError_t launch_lds_merge(const DecodeParams& p, hipStream_t s);
-// The decode step: on the LDS-streamed kernel (append, stream, merge); for
-// bf16 steps of at most kDecodeShortMaxSplits chunks of kDecodeShortChunk
-// keys, on the one-launch short-history kernel (fused = 1); otherwise on the
+// The decode step: for bf16 steps of at most kDecodeShortMaxSplits chunks
+// of kDecodeShortChunk keys, on the one-launch short-history kernel (fused =
+// 1); longer ones in bf16 with 4-head groups and d = 128 on the
+// LDS-streamed kernel (append, stream, merge); otherwise on the
 // lane-parallel split kernel and a merge kernel.
 constexpr int kDecodeShortChunk = 128;
 constexpr int kDecodeShortMaxSplits = 32;
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 // The decode step on the LDS-streamed kernel (bf16, groups of 4 query heads,
-// d = 128): append, the copy and the base token in one streaming pass, then
-// the LSE merge of both kinds (which advances cache_len).  It is taken when
-// the step holds at least kXattnLdsDecodeMinKeys keys over all streams (at
-// max_len): smaller steps go to the lane-parallel kernel, whose many
-// resident workgroups hide latency better than one pipeline per CU.
-constexpr int64_t kXattnLdsDecodeMinKeys = int64_t(12) << 20;
+// d = 128, more keys than the one-launch short-history kernel takes):
+// append, the copy and the base token in one streaming pass, then the LSE
+// merge of both kinds (which advances cache_len).
 hipError_t launch_decode_lds(const DecodeParams& p, hipStream_t s);
 // LSE merge of decode partials [B][Hq][2][n_split][rec] into o_out and o,
 // then cache_len[b] += 1 for every valid sequence.

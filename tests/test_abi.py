@@ -95,35 +95,37 @@ def test_decode_bad_arguments():
     assert call(cap=100, hint=50, wsb=8) == -6
 
 
-@pytest.mark.parametrize("B,hint,lds", [(16, 132095, True), (4, 32767, False), (1, 4095, False), (1, 4096, False),
-                                         (80, 24575, True), (11, 131071, False), (12, 131071, True)],
-                         ids=["B16-128K-lds", "B4-32K-lane", "B1-4K-short", "B1-4K-plus-one-lane",
-                              "B80-24K-lds-two-launches", "B11-128K-lane", "B12-128K-lds-at-threshold"])
-def test_decode_workspace_layout(B, hint, lds):
+@pytest.mark.parametrize("B,Hq,Hkv,d,hint,kind", [(16, 32, 8, 128, 132095, "lds"), (4, 32, 8, 128, 32767, "lds"),
+                                                 (1, 32, 8, 128, 4095, "short"), (1, 32, 8, 128, 4096, "lds"),
+                                                 (80, 32, 8, 128, 24575, "lds"), (4, 16, 8, 128, 32767, "lane"),
+                                                 (11, 32, 8, 64, 131071, "lane"), (3, 16, 8, 64, 4095, "short")],
+                         ids=["B16-128K-lds", "B4-32K-lds", "B1-4K-short", "B1-4K-plus-one-lds",
+                              "B80-24K-lds-two-launches", "B4-32K-G2-lane", "B11-128K-d64-lane", "B3-4K-G2-d64-short"])
+def test_decode_workspace_layout(B, Hq, Hkv, d, hint, kind):
     """The decode workspace: 256-byte-aligned arrival counters and lengths,
-    then the partials.  Long steps (bf16, 4-head groups, d128, at least
-    12 * 2^20 keys over all streams) run on the LDS-streamed kernel: a
-    256-byte-aligned table of 3 record ids per stream, then records of
-    2 kinds x 4 heads x (d + 32) floats, ids for every stream of a launch
-    of up to 64 sequences plus one per workgroup (512 at most).  Shorter
-    steps take two kinds of split partials per (sequence, query head): the
-    lane kernel's power-of-two chunks (>= 256 keys, about 16384 workgroups)
-    and records of d + 2 floats, or, up to 32 chunks of 128 keys, the
-    one-launch short kernel's 128-key chunks and records of d + 4 floats.  A
-    workspace one byte short is rejected before anything runs."""
-    Hq, Hkv, d = 32, 8, 128
+    then the partials.  bf16 steps of at most 32 chunks of 128 keys run on
+    the one-launch short kernel (two kinds of records of d + 4 floats per
+    chunk and query head); longer ones with 4-head groups and d = 128 on the
+    LDS-streamed kernel (a 256-byte-aligned table of 3 record ids per
+    stream, then 2 kinds x 4 heads x (d + 32) floats per id, ids for every
+    stream of a launch of up to 64 sequences plus one per workgroup, 512 at
+    most); the rest on the lane kernel (power-of-two chunks >= 256 keys for
+    about 16384 workgroups, two kinds of records of d + 2 floats per chunk
+    and query head).  A workspace one byte short is rejected before
+    anything runs."""
     desc = mk(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=128, dtype=binding.BF16)
-    keys, S = hint + 1, Hkv * (Hq // Hkv // 4)
+    keys, G = hint + 1, Hq // Hkv
+    S = Hkv * (G // (4 if G % 4 == 0 else 2 if G % 2 == 0 else 1))
     streams = B * S
-    assert (keys * streams >= 12 << 20) == lds
     counters = -(-B * (S + 1) * 4 // 256) * 256      # one per head block, one per sequence
     lens = -(-B * 4 // 256) * 256
-    if lds:
+    if kind == "lds":
         ids = -(-B // 64) * (min(B, 64) * S + 512)
         need = counters + lens + -(-streams * 3 * 4 // 256) * 256 + ids * 2 * 4 * (d + 32) * 4
     else:
-        if keys <= 32 * 128:
-            chunk, rec = 128, d + 4              # short bf16 steps: one launch over 128-key chunks
+        if kind == "short":
+            assert keys <= 32 * 128
+            chunk, rec = 128, d + 4
         else:
             chunk, rec = 256, d + 2
             while chunk < -(-keys * streams // 16384):

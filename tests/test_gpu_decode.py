@@ -57,10 +57,10 @@ def test_decode_steps_parity(Hq, Hkv, d, w, dtype):
 
 @pytest.mark.parametrize("d", [128, 64])
 def test_decode_lengths_at_stage_and_chunk_edges(d):
-    """bf16, 4-head groups, short histories (the lane-parallel kernel):
-    lengths whose new key L is the first or last key of a 128- or 256-key
-    block and of a 256-key chunk, and one that leaves the last chunk a single
-    key; 3 steps each."""
+    """bf16, 4-head groups, short histories (d = 128: the LDS-streamed
+    kernel, d = 64: the lane-parallel kernel): lengths whose new key L is
+    the first or last key of a 128- or 256-key block and of a 256-key chunk,
+    and one that leaves the last chunk a single key; 3 steps each."""
     lens = [0, 127, 128, 255, 256, 511, 1023, 4095]
     steps = 3
     Hq, Hkv, w = 8, 2, 128
@@ -87,8 +87,8 @@ def test_decode_lengths_at_stage_and_chunk_edges(d):
 @pytest.mark.parametrize("keys", [4096, 4097], ids=["one-launch-32-chunks", "two-launches"])
 def test_decode_short_kernel_edge(keys):
     """bf16 steps of at most 32 chunks of 128 keys run as one launch of the
-    short-history kernel; a key more and they run on the lane-parallel split
-    kernel and a merge kernel: the step whose longest history makes
+    short-history kernel; a key more and they run on the LDS-streamed kernel
+    (append, stream, merge): the step whose longest history makes
     max_len_hint + 1 = 4096 keys and the one a key longer, three steps each,
     against the oracle."""
     steps = 3

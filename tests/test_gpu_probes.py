@@ -56,20 +56,20 @@ def onehot_rows(cols, d, dtype=BF16):
 
 def decode_split_of(B, Hq, Hkv, d, hint):
     """(uses the LDS-streamed kernel, workspace bytes) of a bf16 decode step,
-    from the split rule of orthros_decode_step: the LDS-streamed kernel when
-    the step holds at least 12 * 2^20 keys over all streams at max_len
-    (record-id table, then 2 x 4 records of d + 32 floats per id: every
-    stream of a launch of up to 64 sequences plus 512), else 128-key chunks
-    when that makes at most 32 (the one-launch kernel), else power-of-two
-    chunks of at least 256 keys for about 16384 workgroups (records of d + 4
-    or d + 2 floats, two kinds per head); arrival counters and lengths
+    from the split rule of orthros_decode_step: 128-key chunks when that
+    makes at most 32 (the one-launch kernel, records of d + 4 floats, two
+    kinds per query head); else, with 4-head groups and d = 128, the
+    LDS-streamed kernel (record-id table, then 2 x 4 records of d + 32
+    floats per id: every stream of a launch of up to 64 sequences plus 512);
+    else power-of-two chunks of at least 256 keys for about 16384
+    workgroups (records of d + 2 floats); arrival counters and lengths
     first."""
     G = Hq // Hkv
     hpw = 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
     S = Hkv * (G // hpw)
     streams = B * S
     keys = hint + 1
-    lds = G % 4 == 0 and d == 128 and keys * streams >= 12 << 20
+    lds = keys > 32 * 128 and G % 4 == 0 and d == 128
     head = -(-B * (S + 1) * 4 // 256) * 256 + -(-B * 4 // 256) * 256
     if lds:
         ids = -(-B // 64) * (min(B, 64) * S + 512)
@@ -351,14 +351,15 @@ def test_probe_decode_lds_copy_marked_run_edges():
 
 @pytest.mark.parametrize("Hq,Hkv,d,w,longest", [(8, 2, 128, 128, 4095), (8, 2, 128, 1, 4095),
                                                (8, 2, 64, 300, 4095), (4, 2, 128, 128, 4095),
-                                               (16, 2, 128, 128, 4095), (8, 2, 128, 128, 9000)],
-                         ids=["G4", "G4-w1", "G4-d64-w300", "G2", "G8", "G4-two-launches"])
+                                               (16, 2, 128, 128, 4095), (4, 2, 128, 128, 9000),
+                                               (8, 2, 64, 128, 9000)],
+                         ids=["G4", "G4-w1", "G4-d64-w300", "G2", "G8", "G2-two-launches", "G4-d64-two-launches"])
 def test_probe_decode_lane_kernel(Hq, Hkv, d, w, longest):
     """Short histories: lengths 0, 1, around the window, and on the edges of
     128- and 256-key chunks; three steps.  Up to 4096 keys the step is one
     launch of the short-history kernel (128-key chunks, merged in the
-    launch); with a 9000-key history it is the lane-parallel split kernel
-    and a merge kernel (256-key chunks)."""
+    launch); with a 9000-key history and groups of 2, or d = 64, it is the
+    lane-parallel split kernel and a merge kernel (256-key chunks)."""
     lens = [0, 1, 126, 127, 128, 255, 256, 1000, longest]
     if longest == 4095:
         lens[-1] = 4093                          # keys = max_len_hint + 1 = 4096: the one-launch kernel
