@@ -464,15 +464,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int64_t r0g = q0 + r0;
             const rsrc_t ro = make_rsrc((uint16_t*)a.o + q_seq + r0g * a.Hq * D,
                                         (T - r0g) * qrow_b - h0 * D * 2);
+            // lane (n, gq) holds dims 16 dt + 4 gq .. + 3 of row n; a
+            // permlane16 swap between the rows gq and gq ^ 1 of each dt pair
+            // leaves it 8 consecutive dims (32 m + 8 ((gq & 1) * 2 + (gq >> 1))),
+            // so the stores are 16 bytes a lane and 64 contiguous bytes a row
 #pragma unroll
             for (int hd = 0; hd < 2; ++hd) {
                 const float inv = __builtin_amdgcn_rcpf(lacc[hd][0]);
 #pragma unroll
-                for (int dt = 0; dt < ND; ++dt) {
-                    u32x2 w;
-                    w[0] = pack_bf16x2(oacc[hd][dt][0] * inv, oacc[hd][dt][1] * inv);
-                    w[1] = pack_bf16x2(oacc[hd][dt][2] * inv, oacc[hd][dt][3] * inv);
-                    buf_store8(w, ro, (uint32_t)(n * qrow_b + hd * D * 2 + 2 * (16 * dt + 4 * gq)));
+                for (int m = 0; m < ND / 2; ++m) {
+                    const f32x4 oa = oacc[hd][2 * m], ob = oacc[hd][2 * m + 1];
+                    u32x4 w;
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const auto r = __builtin_amdgcn_permlane16_swap(
+                            pack_bf16x2(oa[2 * i] * inv, oa[2 * i + 1] * inv),
+                            pack_bf16x2(ob[2 * i] * inv, ob[2 * i + 1] * inv), false, false);
+                        w[i] = r[0];
+                        w[2 + i] = r[1];
+                    }
+                    buf_store16(w, ro,
+                                (uint32_t)(n * qrow_b + hd * D * 2 + 2 * (32 * m + 8 * ((gq & 1) * 2 + (gq >> 1)))));
                 }
             }
         }
