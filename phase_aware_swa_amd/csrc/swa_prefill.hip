@@ -245,20 +245,31 @@ __global__ __launch_bounds__(256, 2) void swa_bf16_kernel(SwaParams a, int n_til
         __syncthreads();
     }
 
-    // ---- normalise and store: lane (n, half) holds d = 32 dt + 8 i + 4 half + 0..3
+    // ---- normalise and store: lane (n, half) holds d = 32 dt + 8 i + 4 half
+    // + 0..3; a permlane32 swap between the halves for each pair of i leaves
+    // it 8 consecutive dims (32 dt + 8 (2 k + half)), stored as 16 bytes
     const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = 1.f / l_tot;
+    u32x4 w[ND][2];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int i0 = 2 * k, i1 = 2 * k + 1;
+                const auto r = __builtin_amdgcn_permlane32_swap(
+                    pack_bf16x2(oacc[dt][4 * i0 + 2 * e] * inv, oacc[dt][4 * i0 + 2 * e + 1] * inv),
+                    pack_bf16x2(oacc[dt][4 * i1 + 2 * e] * inv, oacc[dt][4 * i1 + 2 * e + 1] * inv), false, false);
+                w[dt][k][e] = r[0];
+                w[dt][k][2 + e] = r[1];
+            }
     if (wave_on && t < T) {
-        const float inv = 1.f / l_tot;
         uint16_t* orow = (uint16_t*)a.o + (((int64_t)b * T + t) * a.Hq + h) * D;
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                u32x2 w;
-                w[0] = pack_bf16x2(oacc[dt][4 * i] * inv, oacc[dt][4 * i + 1] * inv);
-                w[1] = pack_bf16x2(oacc[dt][4 * i + 2] * inv, oacc[dt][4 * i + 3] * inv);
-                *(u32x2*)(orow + 32 * dt + 8 * i + 4 * half) = w;
-            }
+            for (int k = 0; k < 2; ++k) *(u32x4*)(orow + 32 * dt + 16 * k + 8 * half) = w[dt][k];
     }
 }
 
