@@ -429,49 +429,83 @@ __device__ __forceinline__ void rec_st(f32x4 v, rsrc_t r, uint32_t off)
 }
 
 // The merge of a whole head block by one workgroup, from records of D + 4
-// floats (max, sum, 0, 0, weighted values) read at device scope: D / 4
-// threads per (head, kind) row, one 4-value quad each, one pass over the
-// splits in order with a running maximum (RB splits' header and quad
-// loaded per round); the result is run-to-run identical.  Threads past the
-// 2 HG rows do nothing; no barrier.
+// floats (max, sum, 0, 0, weighted values) read at device scope.  The block's
+// (kind, split) records -- the copy's splits 0 .. s1, then the base token's
+// sw0 .. s1 -- are dealt round-robin to NG groups of D / 4 threads per head,
+// each thread one 4-value quad: a group issues the loads of up to RB records
+// at once (one memory round trip for the short steps' at most 32 + a few
+// records), folds them in order into a running (max, sum, values) per kind,
+// and the groups' states then combine through LDS in group order, so the
+// result is run-to-run identical.  Every thread of the workgroup takes part
+// (there is a barrier); `scratch` is LDS for 256 x 12 floats.
 template <int D, int HG>
 __device__ __forceinline__ void merge_block(rsrc_t part, int64_t head_stride, int64_t kind_stride, int sw0, int s1,
-                                            uint16_t* o_out, uint16_t* o, int64_t row0)
+                                            uint16_t* o_out, uint16_t* o, int64_t row0, float* scratch)
 {
     constexpr int TPR = D / 4;
-    constexpr int RB = 16;
+    constexpr int NG = 256 / (HG * TPR);         // groups per head
+    constexpr int RB = (36 + NG - 1) / NG;       // records per group and round
     constexpr int REC = D + 4;
-    const int u = threadIdx.x / TPR, qd = threadIdx.x % TPR;
-    if (u >= 2 * HG) return;
-    const int hh = u >> 1, kind = u & 1;
-    const uint32_t base = (uint32_t)((hh * head_stride + kind * kind_stride) * 4);
-    const int s0 = kind ? sw0 : 0;
-    float M = kNegBig, den = 0.f;
-    f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    for (int s = s0; s <= s1; s += RB) {
+    static_assert(NG >= 2 && HG * NG * TPR == 256, "thread layout");
+    const int tid = threadIdx.x;
+    const int hh = tid / (NG * TPR), grp = (tid / TPR) % NG, qd = tid % TPR;
+    const int n0 = s1 + 1, np = n0 + (s1 - sw0 + 1);   // the copy's records, then the base token's
+    float M[2] = {kNegBig, kNegBig}, den[2] = {0.f, 0.f};
+    f32x4 num[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int p0 = grp; p0 < np; p0 += NG * RB) {
         f32x4 hd[RB], v[RB];
 #pragma unroll
         for (int k = 0; k < RB; ++k) {
-            const uint32_t off = base + (uint32_t)((s + k <= s1 ? s + k : s1) * REC * 4);
+            const int pk = p0 + NG * k < np ? p0 + NG * k : np - 1;
+            const int kind = pk >= n0, sk = kind ? sw0 + pk - n0 : pk;
+            const uint32_t off = (uint32_t)((hh * head_stride + kind * kind_stride + (int64_t)sk * REC) * 4);
             hd[k] = rec_ld(part, off);
             v[k] = rec_ld(part, off + 16 + 16 * qd);
         }
 #pragma unroll
         for (int k = 0; k < RB; ++k) {
             // (no early exit: the arrays stay in registers)
-            if (s + k <= s1) {
-                const float mn = fmaxf(M, hd[k][0]);
-                const float sc = fast_exp2(M - mn), f = fast_exp2(hd[k][0] - mn);
-                den = den * sc + f * hd[k][1];
-                num = num * sc + f * v[k];
-                M = mn;
+            const int pk = p0 + NG * k;
+            if (pk < np) {
+                const int kind = pk >= n0;
+                const float mn = fmaxf(M[kind], hd[k][0]);
+                const float sc = fast_exp2(M[kind] - mn), f = fast_exp2(hd[k][0] - mn);
+                den[kind] = den[kind] * sc + f * hd[k][1];
+                num[kind] = num[kind] * sc + f * v[k];
+                M[kind] = mn;
             }
         }
     }
-    uint16_t* out = kind ? o : o_out;
-    const int64_t row = row0 + (int64_t)hh * D + 4 * qd;
-    const float inv = 1.f / den;
-    *(u32x2*)(out + row) = u32x2{pack_bf16x2(num[0] * inv, num[1] * inv), pack_bf16x2(num[2] * inv, num[3] * inv)};
+    // the groups' states: [head][kind][group][quad] x (max, sum, 4 values)
+    auto at = [&](int h, int kind, int g, int q) { return scratch + (((h * 2 + kind) * NG + g) * TPR + q) * 6; };
+#pragma unroll
+    for (int kind = 0; kind < 2; ++kind) {
+        float* w = at(hh, kind, grp, qd);
+        w[0] = M[kind];
+        w[1] = den[kind];
+        w[2] = num[kind][0];
+        w[3] = num[kind][1];
+        w[4] = num[kind][2];
+        w[5] = num[kind][3];
+    }
+    __syncthreads();
+    if (grp < 2) {
+        const int kind = grp;                     // group 0 finishes the copy, group 1 the base token
+        float Mt = kNegBig;
+        for (int g = 0; g < NG; ++g) Mt = fmaxf(Mt, at(hh, kind, g, qd)[0]);
+        float dt = 0.f;
+        f32x4 nt = {0.f, 0.f, 0.f, 0.f};
+        for (int g = 0; g < NG; ++g) {
+            const float* r = at(hh, kind, g, qd);
+            const float f = fast_exp2(r[0] - Mt);
+            dt += f * r[1];
+            nt += f * f32x4{r[2], r[3], r[4], r[5]};
+        }
+        uint16_t* out = kind ? o : o_out;
+        const int64_t row = row0 + (int64_t)hh * D + 4 * qd;
+        const float inv = 1.f / dt;
+        *(u32x2*)(out + row) = u32x2{pack_bf16x2(nt[0] * inv, nt[1] * inv), pack_bf16x2(nt[2] * inv, nt[3] * inv)};
+    }
 }
 
 // One launch per decode step when the histories are short (bf16, at most
@@ -742,8 +776,9 @@ __global__ __launch_bounds__(256) void decode_short_kernel(DecodeParams p)
     if (tid == 0) last = atomicAdd(blk_cnt, 1) == p.n_split - 1;
     __syncthreads();
     if (!last) return;
+    static_assert(256 * 12 * 4 <= 4 * PPW * R::SLOT * 2, "the merge's group states fit in the pair regions");
     merge_block<D, HG>(prs, head_stride, kind_stride, (int)(wlo / kDecodeShortChunk), (int)(L / kDecodeShortChunk),
-                       (uint16_t*)p.o_out, (uint16_t*)p.o, ((int64_t)b * p.Hq + h0) * D);
+                       (uint16_t*)p.o_out, (uint16_t*)p.o, ((int64_t)b * p.Hq + h0) * D, reinterpret_cast<float*>(lds));
     if (tid == 0) {
         __hip_atomic_store(blk_cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         int* seq_cnt = p.ws_cnt + (int64_t)p.B * nblk + b;
