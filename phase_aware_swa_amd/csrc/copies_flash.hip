@@ -14,8 +14,8 @@
 //     through a 4-slot LDS ring, two pairs per step: while a step computes,
 //     the next two pairs are in flight into registers, and the slots they
 //     land in are the previous step's, so one barrier per step suffices;
-//   - S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 (K layout in
-//     pair_tile.h); V stays row-major in LDS and its V^T operands come from
+//   - S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 (K in
+//     pair_tile.h's line-aligned layout); V stays row-major in LDS and its V^T operands come from
 //     the transposing LDS read; keys past a copy's position are masked in the pairs
 //     that reach past the smallest position of the wave's copies; a wave
 //     skips the pairs past its largest position;
@@ -43,7 +43,8 @@ template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void copies_flash_kernel(
     CopiesParams a, int n_tiles, int hblocks)
 {
-    using R = PairTile<D>;
+    using R = LinePairTile<D>;
+    using PV = PairTile<D>;                    // V's staging order
     constexpr int NT = 256;
     constexpr int C16 = D / 8;                 // 16-byte chunks per row
     constexpr int NQ = D / 32;                 // MFMA k-steps over the head dim
@@ -128,21 +129,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
     }
 
-    // staging of pairs (32 cache rows each): item tid + 256 j -> (row, chunk) by
-    // PairTile::kitem for K and PairTile::vitem for V; item + 256 is the same
-    // chunk 16 rows on (KCH is 2 only at d = 128)
+    // staging of pairs (32 cache rows each): K by LDS unit, thread tid
+    // taking units tid + 256 j of the pair's K part (LinePairTile::k_unit:
+    // 8 threads read 128 contiguous bytes of one row, and the LDS stores are
+    // contiguous); V item tid + 256 j -> (row, chunk) by PairTile::vitem,
+    // item + 256 being the same chunk 16 rows on (KCH is 2 only at d = 128)
     static_assert(KCH == 1 || NT / C16 == 16, "staging step");
     auto load_pair = [&](int64_t pr, u32x4 (&kr)[KCH], u32x4 (&vr)[KCH]) {
         const int64_t kbase = pr * 32;
         const int64_t avail = (T - kbase) * D * 2;
         const rsrc_t rk = make_rsrc((const uint16_t*)a.k_cache + c_seq + kbase * D, avail);
         const rsrc_t rv = make_rsrc((const uint16_t*)a.v_cache + c_seq + kbase * D, avail);
-        int kr_row, kr_c, vr_row, vr_c;
-        R::kitem(tid, kr_row, kr_c);
-        R::vitem(tid, vr_row, vr_c);
+        int vr_row, vr_c;
+        PV::vitem(tid, vr_row, vr_c);
 #pragma unroll
         for (int j = 0; j < KCH; ++j) {
-            kr[j] = buf_load16(rk, (uint32_t)((kr_row + 16 * j) * D * 2 + 16 * kr_c));
+            int kr_row, kr_c;
+            R::k_unit(tid + NT * j, kr_row, kr_c);
+            kr[j] = buf_load16(rk, (uint32_t)(kr_row * D * 2 + 16 * kr_c));
             vr[j] = buf_load16(rv, (uint32_t)((vr_row + 16 * j) * D * 2 + 16 * vr_c));
         }
     };
@@ -151,12 +155,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         uint16_t* Vt = Ks + R::KPART;
         int t = tid;
         asm volatile("" : "+v"(t));
-        int kr_row, kr_c, vr_row, vr_c;
-        R::kitem(t, kr_row, kr_c);
-        R::vitem(t, vr_row, vr_c);
+        int vr_row, vr_c;
+        PV::vitem(t, vr_row, vr_c);
 #pragma unroll
         for (int j = 0; j < KCH; ++j) {
-            *(u32x4*)(Ks + R::kofs(kr_row, kr_c) + j * R::K_KEY16) = kr[j];
+            *(u32x4*)(Ks + 8 * (t + NT * j)) = kr[j];
             *(u32x4*)(Vt + R::vofs16(vr_row, vr_c) + j * R::V_KEY16) = vr[j];
         }
     };
@@ -172,16 +175,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // probabilities are plain exp2 of the scores.
     auto attend = [&](auto first_tag, int64_t pr) {
         constexpr bool FIRST = decltype(first_tag)::value;
-        // one K base per pair (opaque, so that the steps stay immediate offsets)
-        int ko = (int)(pr & (kNs - 1)) * R::SLOT + R::kofs(n, gq);
-        asm volatile("" : "+v"(ko));
-        const uint16_t* kb = ring + ko;
+        // two K bases per pair, for even and odd k-steps (opaque, so that
+        // the steps stay immediate offsets)
+        int ko0 = (int)(pr & (kNs - 1)) * R::SLOT + R::kofs(n, gq);
+        int ko1 = (int)(pr & (kNs - 1)) * R::SLOT + R::kofs(n, 4 + gq);
+        asm volatile("" : "+v"(ko0), "+v"(ko1));
         const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
         f32x4 s[2][2];
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
-            const bf16x8 k0 = *(const bf16x8*)(kb + i * R::K_STEP);
-            const bf16x8 k1 = *(const bf16x8*)(kb + i * R::K_STEP + R::K_KEY16);
+            const uint16_t* kb = ring + ((i & 1) ? ko1 : ko0) + (i >> 1) * R::K_STEP2;
+            const bf16x8 k0 = *(const bf16x8*)kb;
+            const bf16x8 k1 = *(const bf16x8*)(kb + R::K_KEY16);
 #pragma unroll
             for (int hd = 0; hd < 2; ++hd) {
                 const f32x4 c = FIRST ? zero : negm[hd];
@@ -292,17 +297,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // compiled assuming no NaN arithmetic)
     const uint32_t nan_mask = myp_raw == -2 ? 0xffffffffu : 0u;
     constexpr uint32_t kNanPair = 0x7fc07fc0u;
+    // lane (n, gq) holds dims 16 dt + 4 gq .. + 3 of copy n; a permlane16
+    // swap between the rows gq and gq ^ 1 of each dt pair leaves it 8
+    // consecutive dims (32 m + 8 ((gq & 1) * 2 + (gq >> 1))): 16-byte stores
+    // (the NaN mask belongs to the copy, the same in both partner lanes)
 #pragma unroll
     for (int hd = 0; hd < 2; ++hd) {
         const float inv = __builtin_amdgcn_rcpf(lacc[hd][0]);
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) {
-            u32x2 w;
-            w[0] = pack_bf16x2(oacc[hd][dt][0] * inv, oacc[hd][dt][1] * inv);
-            w[1] = pack_bf16x2(oacc[hd][dt][2] * inv, oacc[hd][dt][3] * inv);
-            w[0] = (w[0] & ~nan_mask) | (kNanPair & nan_mask);
-            w[1] = (w[1] & ~nan_mask) | (kNanPair & nan_mask);
-            buf_store8(w, ro, (uint32_t)(n * qrow_b + hd * D * 2 + 2 * (16 * dt + 4 * gq)));
+        for (int m = 0; m < ND / 2; ++m) {
+            const f32x4 oa = oacc[hd][2 * m], ob = oacc[hd][2 * m + 1];
+            u32x4 w;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const auto r = __builtin_amdgcn_permlane16_swap(
+                    pack_bf16x2(oa[2 * i] * inv, oa[2 * i + 1] * inv),
+                    pack_bf16x2(ob[2 * i] * inv, ob[2 * i + 1] * inv), false, false);
+                w[i] = (r[0] & ~nan_mask) | (kNanPair & nan_mask);
+                w[2 + i] = (r[1] & ~nan_mask) | (kNanPair & nan_mask);
+            }
+            buf_store16(w, ro, (uint32_t)(n * qrow_b + hd * D * 2 + 2 * (32 * m + 8 * ((gq & 1) * 2 + (gq >> 1)))));
         }
     }
 }
