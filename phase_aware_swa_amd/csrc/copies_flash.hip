@@ -14,8 +14,8 @@
 //     through a 4-slot LDS ring, two pairs per step: while a step computes,
 //     the next two pairs are in flight into registers, and the slots they
 //     land in are the previous step's, so one barrier per step suffices;
-//   - S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 (K in
-//     pair_tile.h's line-aligned layout); V stays row-major in LDS and its V^T operands come from
+//   - S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 (K layout in
+//     pair_tile.h); V stays row-major in LDS and its V^T operands come from
 //     the transposing LDS read; keys past a copy's position are masked in the pairs
 //     that reach past the smallest position of the wave's copies; a wave
 //     skips the pairs past its largest position;
@@ -43,8 +43,7 @@ template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void copies_flash_kernel(
     CopiesParams a, int n_tiles, int hblocks)
 {
-    using R = LinePairTile<D>;
-    using PV = PairTile<D>;                    // V's staging order
+    using R = PairTile<D>;
     constexpr int NT = 256;
     constexpr int C16 = D / 8;                 // 16-byte chunks per row
     constexpr int NQ = D / 32;                 // MFMA k-steps over the head dim
@@ -130,7 +129,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 
     // staging of pairs (32 cache rows each): K by LDS unit, thread tid
-    // taking units tid + 256 j of the pair's K part (LinePairTile::k_unit:
+    // taking units tid + 256 j of the pair's K part (PairTile::k_unit:
     // 8 threads read 128 contiguous bytes of one row, and the LDS stores are
     // contiguous); V item tid + 256 j -> (row, chunk) by PairTile::vitem,
     // item + 256 being the same chunk 16 rows on (KCH is 2 only at d = 128)
@@ -141,7 +140,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const rsrc_t rk = make_rsrc((const uint16_t*)a.k_cache + c_seq + kbase * D, avail);
         const rsrc_t rv = make_rsrc((const uint16_t*)a.v_cache + c_seq + kbase * D, avail);
         int vr_row, vr_c;
-        PV::vitem(tid, vr_row, vr_c);
+        R::vitem(tid, vr_row, vr_c);
 #pragma unroll
         for (int j = 0; j < KCH; ++j) {
             int kr_row, kr_c;
@@ -156,7 +155,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         int t = tid;
         asm volatile("" : "+v"(t));
         int vr_row, vr_c;
-        PV::vitem(t, vr_row, vr_c);
+        R::vitem(t, vr_row, vr_c);
 #pragma unroll
         for (int j = 0; j < KCH; ++j) {
             *(u32x4*)(Ks + 8 * (t + NT * j)) = kr[j];

@@ -537,7 +537,7 @@ __device__ __forceinline__ void merge_block(rsrc_t part, int64_t head_stride, in
 template <int D, int HG>
 __global__ __launch_bounds__(256) void decode_short_kernel(DecodeParams p)
 {
-    using R = LinePairTile<D>;
+    using R = PairTile<D>;
     constexpr int NQ = D / 32, ND = D / 16;
     constexpr int NH = 2 * HG;                 // live query columns
     constexpr int PPW = kDecodeShortChunk / 128;   // 32-key pairs per wave

@@ -1,17 +1,22 @@
 // pair_tile.h -- LDS layout of one 32-key "pair" (two 16-key blocks) of K
 // and V for the 16x16x32 bf16 MFMA attention kernels (the streaming SWA
-// kernel and the many-copy kernel).
+// kernel, the cross-attention stream, the short decode kernel and the
+// many-copy kernel).
 //
 // S^T = K Q^T per 16-key block leaves each lane (n = query, gq = lane/16)
 // with keys 4gq..4gq+3 of the block; the P^T operand of O^T = V^T P^T over a
 // pair is then [block 0 keys 4gq..+3, block 1 keys 4gq..+3].
 //
-// K is stored by 16-byte chunk columns: chunk c = 4 i + q of key r at
-// 16-byte unit 128 i + 32 q + (r & 16) + ((r + 4 q) & 15).  The S^T operand
-// read of k-step i (lane (n, gq): key n of a block, chunk 4 i + gq) is then
-// one per-lane base plus the immediate 1024 i (+ 128 for block 1), and the
-// 16 lanes of a 16-byte access (16 keys, one chunk) hit 16 distinct 16-byte
-// bank groups; so do staging stores of 4 keys x 4 chunks.
+// K is stored line-aligned: the K part is a run of 16-byte units in blocks
+// of 64 (1 KB), each block holding 8 keys x 8 chunks, i.e. 128 contiguous
+// bytes of each of 8 key rows.  Filled in unit order -- a direct-to-LDS
+// load instruction, or 256 threads' 16-byte stores -- every 8 consecutive
+// lanes read 128 contiguous bytes of one cache row (whole lines, which lets
+// non-temporal loads stream at the full HBM rate) and the LDS stores are
+// contiguous.  Within a 16-key block, keys r and r + 8 take adjacent 8-unit
+// rows and chunk c of key r sits at position (c & 7) ^ (r & 7) of its row,
+// so the operand read of a k-step (16 keys, one chunk) hits 16 distinct
+// 16-byte bank groups, and any 8 consecutive of those keys 8 distinct ones.
 //
 // V is stored in 256-byte lines of 8 keys x 16 head dims,
 // [key / 8][d / 16][key % 8][d % 16], and read with ds_read_b64_tr_b16:
@@ -38,33 +43,26 @@ struct PairTile {
     // K: element offset of 16-byte chunk c (dims 8c .. 8c + 7) of key r.
     __device__ static int kofs(int r, int c)
     {
-        const int q = c & 3;
-        return ((c >> 2) * 128 + q * 32 + (r & 16) + ((r + 4 * q) & 15)) * 8;
+        const int row = ((r & 7) << 1) | ((r >> 3) & 1);
+        return ((r >> 4) * 2 * D + (c >> 3) * 128 + row * 8 + ((c & 7) ^ (r & 7))) * 8;
     }
-    // Immediate steps of kofs: k-step i + 1 (chunk c + 4), key r + 16.
-    static constexpr int K_STEP = 1024, K_KEY16 = 128;
-    // Staging order of K chunks: item it -> key row, 16-byte chunk.  The 16
-    // lanes of one 16-byte LDS store cover 4 keys x 4 chunks, and a wave's
-    // global loads cover whole rows.
-    __device__ static void kitem(int it, int& r, int& c)
+    // The operand of k-step i (chunk 4 i + gq of key n of block 0) is at
+    // kofs(n, 4 (i & 1) + gq) + (i >> 1) * K_STEP2; block 1 adds K_KEY16.
+    static constexpr int K_STEP2 = 128 * 8, K_KEY16 = 2 * D * 8;
+    // Inverse map for unit-order filling: key row r and chunk c held by
+    // 16-byte unit u of the K part.
+    __device__ static void k_unit(int u, int& r, int& c)
     {
-        constexpr int LNQ = D == 128 ? 2 : 1;        // log2(D / 32)
-        r = ((it >> (4 + LNQ)) << 2) | ((it >> 2) & 3);
-        c = (((it >> 4) & ((1 << LNQ) - 1)) << 2) | (it & 3);
+        const int row = (u >> 3) & 15;
+        r = 16 * (u / (2 * D)) + ((row & 1) << 3) + (row >> 1);
+        c = 8 * ((u % (2 * D)) >> 7) + ((u & 7) ^ (r & 7));
     }
     // V: element offset of head dims 16 dt + 4 q .. + 3 of key r (an 8-byte
     // transposing-read chunk), and of 16-byte chunk c (dims 8c .. 8c + 7).
     __device__ static int vofs_tr(int r, int dt, int q) { return (r >> 3) * 8 * D + dt * 128 + (r & 7) * 16 + 4 * q; }
     __device__ static int vofs16(int r, int c) { return (r >> 3) * 8 * D + (c >> 1) * 128 + (r & 7) * 16 + 8 * (c & 1); }
-    // Inverse maps for loads that write LDS in lane order: the key row r and
-    // 16-byte chunk c held by 16-byte unit u of the K part (kofs) and of the
-    // V part (vofs16) of a slot.
-    __device__ static void k_unit(int u, int& r, int& c)
-    {
-        const int q = (u >> 5) & 3;
-        r = (u & 16) | (((u & 15) - 4 * q) & 15);
-        c = 4 * (u >> 7) + q;
-    }
+    // Inverse map for loads that write the V part in lane order: the key row
+    // r and 16-byte chunk c held by 16-byte unit u (vofs16).
     __device__ static void v_unit(int u, int& r, int& c)
     {
         const int w = u % D;
@@ -74,51 +72,16 @@ struct PairTile {
     // Immediate steps of vofs_tr: dt + 1 is one line on, key r + 16
     // (r < 16) two 8-key groups on, and key r + 4 (r & 7 < 4) half a line.
     static constexpr int V_DT = 128, V_KEY16 = 16 * D, V_KEY8 = 8 * D, V_KEY4 = 64;
-    // Staging order of V chunks: item it -> key row, 16-byte chunk.  The 16
-    // lanes of one 16-byte LDS store cover one line (8 keys x 2 chunks), and
-    // a wave's global loads cover 8 keys x 128 contiguous bytes.
+    // Staging order of V chunks through registers: item it -> key row,
+    // 16-byte chunk.  The 16 lanes of one 16-byte LDS store cover one line
+    // (8 keys x 2 chunks), and a wave's global loads cover 8 keys x 128
+    // contiguous bytes.
     __device__ static void vitem(int it, int& r, int& c)
     {
         constexpr int LDT = D == 128 ? 3 : 2;        // log2(D / 16)
         r = ((it >> (4 + LDT)) << 3) | ((it >> 1) & 7);
         c = (((it >> 4) & ((1 << LDT) - 1)) << 1) | (it & 1);
     }
-};
-
-// The same pair with K in line-aligned form, for kernels whose direct loads
-// fill LDS in lane order (one 1 KB block per load instruction): block b of
-// 64 16-byte units holds 8 keys x 8 chunks, i.e. 128 contiguous bytes of each
-// of 8 key rows, so every load instruction reads whole 128-byte lines of the
-// cache (what lets non-temporal loads stream at the full HBM rate; a load
-// that reads part of a line leaves the rest to be fetched again).  Within a
-// 16-key block, keys r and r + 8 take adjacent 8-unit rows and chunk c of key
-// r sits at position (c & 7) ^ (r & 7) of its row, so the operand read of a
-// k-step (16 keys, one chunk) hits 16 distinct 16-byte bank groups, and any
-// 8 consecutive of those keys 8 distinct ones.  V is laid out as in PairTile.
-template <int D>
-struct LinePairTile {
-    using P = PairTile<D>;
-    static constexpr int KPART = P::KPART, VPART = P::VPART, SLOT = P::SLOT;
-    // K: element offset of 16-byte chunk c (dims 8c .. 8c + 7) of key r.
-    __device__ static int kofs(int r, int c)
-    {
-        const int row = ((r & 7) << 1) | ((r >> 3) & 1);
-        return ((r >> 4) * 2 * D + (c >> 3) * 128 + row * 8 + ((c & 7) ^ (r & 7))) * 8;
-    }
-    // The operand of k-step i (chunk 4 i + gq of key n of block 0) is at
-    // kofs(n, 4 (i & 1) + gq) + (i >> 1) * K_STEP2; block 1 adds K_KEY16.
-    static constexpr int K_STEP2 = 128 * 8, K_KEY16 = 2 * D * 8;
-    // Inverse map: key row r and chunk c held by 16-byte unit u of the K part.
-    __device__ static void k_unit(int u, int& r, int& c)
-    {
-        const int row = (u >> 3) & 15;
-        r = 16 * (u / (2 * D)) + ((row & 1) << 3) + (row >> 1);
-        c = 8 * ((u % (2 * D)) >> 7) + ((u & 7) ^ (r & 7));
-    }
-    __device__ static int vofs_tr(int r, int dt, int q) { return P::vofs_tr(r, dt, q); }
-    __device__ static int vofs16(int r, int c) { return P::vofs16(r, c); }
-    __device__ static void v_unit(int u, int& r, int& c) { P::v_unit(u, r, c); }
-    static constexpr int V_DT = P::V_DT, V_KEY16 = P::V_KEY16, V_KEY8 = P::V_KEY8, V_KEY4 = P::V_KEY4;
 };
 
 // Four bf16 of V^T through the transposing read (see above).

@@ -98,21 +98,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int64_t q_seq = (int64_t)b * T * a.Hq * D + (int64_t)h0 * D;
     const int64_t c_seq = ((int64_t)b * a.Hkv + g) * a.cap * D;
 
-    // staging of one pair (32 new keys): item tid + 256 j -> (row, chunk) by
-    // PairTile::kitem for K and PairTile::vitem for V; item + 256 is the same
-    // chunk 16 rows on (KCH is 2 only at d = 128)
+    // staging of one pair (32 new keys): K by LDS unit, thread tid taking
+    // units tid + 256 j of the pair's K part (PairTile::k_unit: 8
+    // threads read 128 contiguous bytes of a row, and the LDS stores are
+    // contiguous); V item tid + 256 j -> (row, chunk) by PairTile::vitem,
+    // item + 256 being the same chunk 16 rows on (KCH is 2 only at d = 128)
     static_assert(KCH == 1 || NT / C16 == 16, "staging step");
     auto load_pair = [&](int64_t pr, u32x4 (&kr)[KCH], u32x4 (&vr)[KCH]) {
         const int64_t kbase = pr * 32;
         const int64_t avail = (T - kbase) * krow_b - g * D * 2;
         const rsrc_t rk = make_rsrc((const uint16_t*)a.k + kv_seq + kbase * a.Hkv * D, avail);
         const rsrc_t rv = make_rsrc((const uint16_t*)a.v + kv_seq + kbase * a.Hkv * D, avail);
-        int kr_row, kr_c, vr_row, vr_c;
-        R::kitem(tid, kr_row, kr_c);
+        int vr_row, vr_c;
         R::vitem(tid, vr_row, vr_c);
 #pragma unroll
         for (int j = 0; j < KCH; ++j) {
-            kr[j] = buf_load16(rk, (uint32_t)((kr_row + 16 * j) * krow_b + 16 * kr_c));
+            int kr_row, kr_c;
+            R::k_unit(tid + NT * j, kr_row, kr_c);
+            kr[j] = buf_load16(rk, (uint32_t)(kr_row * krow_b + 16 * kr_c));
             vr[j] = buf_load16(rv, (uint32_t)((vr_row + 16 * j) * krow_b + 16 * vr_c));
         }
     };
@@ -123,12 +126,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // across the tile (they would only take registers the tile needs)
         int t = tid;
         asm volatile("" : "+v"(t));
-        int kr_row, kr_c, vr_row, vr_c;
-        R::kitem(t, kr_row, kr_c);
+        int vr_row, vr_c;
         R::vitem(t, vr_row, vr_c);
 #pragma unroll
         for (int j = 0; j < KCH; ++j) {
-            *(u32x4*)(Ks + R::kofs(kr_row, kr_c) + j * R::K_KEY16) = kr[j];
+            *(u32x4*)(Ks + 8 * (t + NT * j)) = kr[j];
             *(u32x4*)(Vt + R::vofs16(vr_row, vr_c) + j * R::V_KEY16) = vr[j];
         }
         if (own && writer) {
@@ -138,7 +140,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const rsrc_t cv = make_rsrc((uint16_t*)a.v_cache + c_seq + kbase * D, avail);
 #pragma unroll
             for (int j = 0; j < KCH; ++j) {
-                buf_store16(kr[j], ck, (uint32_t)((kr_row + 16 * j) * D * 2 + 16 * kr_c));
+                int kr_row, kr_c;
+                R::k_unit(t + NT * j, kr_row, kr_c);
+                buf_store16(kr[j], ck, (uint32_t)(kr_row * D * 2 + 16 * kr_c));
                 buf_store16(vr[j], cv, (uint32_t)((vr_row + 16 * j) * D * 2 + 16 * vr_c));
             }
         }
@@ -359,16 +363,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // from zero (no clearing, no rescale).
         auto attend = [&](auto first_tag, int64_t pr) {
             constexpr bool FIRST = decltype(first_tag)::value;
-            // one K base per pair (opaque, so that the steps stay immediate offsets)
-            int ko = (int)(pr % NS) * R::SLOT + R::kofs(n, gq);
-            asm volatile("" : "+v"(ko));
-            const uint16_t* kb = ring + ko;
+            // two K bases per pair, for even and odd k-steps (opaque, so that
+            // the steps stay immediate offsets)
+            int ko0 = (int)(pr % NS) * R::SLOT + R::kofs(n, gq);
+            int ko1 = (int)(pr % NS) * R::SLOT + R::kofs(n, 4 + gq);
+            asm volatile("" : "+v"(ko0), "+v"(ko1));
             const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
             f32x4 s[2][2];
 #pragma unroll
             for (int i = 0; i < NQ; ++i) {
-                const bf16x8 k0 = *(const bf16x8*)(kb + i * R::K_STEP);
-                const bf16x8 k1 = *(const bf16x8*)(kb + i * R::K_STEP + R::K_KEY16);
+                const uint16_t* kb = ring + ((i & 1) ? ko1 : ko0) + (i >> 1) * R::K_STEP2;
+                const bf16x8 k0 = *(const bf16x8*)kb;
+                const bf16x8 k1 = *(const bf16x8*)(kb + R::K_KEY16);
 #pragma unroll
                 for (int hd = 0; hd < 2; ++hd) {
                     const f32x4 c0 = i ? s[hd][0] : (FIRST ? dbias[0] : zero);

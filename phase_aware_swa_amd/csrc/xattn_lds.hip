@@ -32,7 +32,7 @@
 //     stage's wait lets exactly those stay in flight;
 //   - each load instruction fills 1 KB of a slot in lane order, so each lane
 //     fetches the cache chunk that belongs at its 16-byte unit of the pair
-//     layout (LinePairTile's inverse maps: every instruction reads whole
+//     layout (PairTile's inverse maps: every instruction reads whole
 //     128-byte lines, 8 key rows x 128 bytes, which the loads mark
 //     non-temporal -- the cache is read once per call); the stage's buffer
 //     range ends at the item's last key, so keys past it land as zeros;
@@ -105,7 +105,7 @@ template <int D, typename PT>
 __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, int rbase, PosBlock pos)
 {
     constexpr bool DEC = std::is_same<PT, DecodeParams>::value;
-    using R = LinePairTile<D>;
+    using R = PairTile<D>;
     constexpr int NP = 128 / D * 4;       // pairs per stage: 64 KB
     constexpr int SK = 32 * NP;           // keys per stage
     constexpr int PAIRB = 32 * D * 2;     // bytes of one pair's K (or V) rows in the cache
