@@ -286,9 +286,10 @@ orthros_status orthros_decode_step(const orthros_desc* desc,
  * Limits and errors: a step whose workspace (orthros_decode_workspace_size
  * of desc and max_len_hint) exceeds 64 MiB is rejected with
  * ORTHROS_E_WORKSPACE before anything is queued (the batch-16 step with
- * 128K-key histories needs about 3.3 MB on the streaming kernel; the same
- * at d = 64, which runs on the lane-parallel kernel, about 35 MB).  Every
- * call on one GPU shares that
+ * 128K-key histories needs about 3.3 MB; steps on the lane-parallel
+ * kernel -- fp32, and short bf16 steps of groups that are not multiples of
+ * 4 -- need far more: about 60 MB for fp32 at batch 16 with 120K-key
+ * histories).  Every call on one GPU shares that
  * GPU's array, which keeps the last call's contents; each step writes what
  * it reads, so no clearing is needed, but calls that can overlap on one GPU
  * (other streams, other host threads) race on it: serialise them.

@@ -121,7 +121,9 @@ bool fused_prefill(const orthros_desc* d)
 Split prefill_split(const orthros_desc* d, int64_t T)
 {
     Split s;
-    const bool lds = orthros::xattn_lds_applies(dt_of(d), d->n_q_heads, d->n_kv_heads);
+    const bool lds = orthros::xattn_lds_applies(dt_of(d), d->n_q_heads, d->n_kv_heads) &&
+                     ((d->n_q_heads / d->n_kv_heads) % 4 == 0 ||
+                      T * streams_of(d) >= orthros::kXattnLdsPrefillMinKeys);
     s.lds = lds;
     if (lds) {
         s.chunk = 0;
@@ -174,9 +176,12 @@ Split decode_split(const orthros_desc* d, int64_t max_len)
     // each workgroup reads its whole chunk in one round trip)
     s.fused = d->dtype == ORTHROS_BF16 &&
               keys <= (int64_t)orthros::kDecodeShortChunk * orthros::kDecodeShortMaxSplits;
-    // longer steps in bf16 with 4-head groups and d = 128: the LDS-streamed
-    // kernel (equal runs of the step's keys per workgroup)
-    s.lds = !s.fused && orthros::xattn_lds_applies(dt_of(d), d->n_q_heads, d->n_kv_heads) && d->head_dim == 128;
+    // longer bf16 steps: the LDS-streamed kernel (equal runs of the step's
+    // keys per workgroup) for groups that are multiples of 4, and for other
+    // groups once the step is long enough for its runs to pay
+    s.lds = !s.fused && orthros::xattn_lds_applies(dt_of(d), d->n_q_heads, d->n_kv_heads) &&
+            ((d->n_q_heads / d->n_kv_heads) % 4 == 0 || keys * streams_of(d) >= orthros::kXattnLdsDecodeMinKeys ||
+             keys >= orthros::kXattnLdsDecodeLongKeys);
     if (s.lds) {
         s.chunk = 0;
         s.n_split = 0;
@@ -184,7 +189,8 @@ Split decode_split(const orthros_desc* d, int64_t max_len)
         s.bytes = cnt_bytes(d) + len_bytes(d) + rng_bytes(d, true) + lds_record_bytes(d, 2, s.rec);
         return s;
     }
-    // the rest on the lane-parallel kernel
+    // the rest (fp32, and short bf16 steps of other groups) on the
+    // lane-parallel kernel
     s.chunk = s.fused ? orthros::kDecodeShortChunk : pick_chunk(keys, streams_of(d), kDecodeTargetWgs);
     s.n_split = (int)((keys + s.chunk - 1) / s.chunk);
     s.rec = d->head_dim + (s.fused ? 4 : 2);
@@ -279,7 +285,7 @@ orthros::XattnParams xattn_params(const orthros_desc* d, const Split& sp, const 
     p.pos = out_pos;
     p.cap = cap;
     p.B = d->batch; p.Hq = d->n_q_heads; p.Hkv = d->n_kv_heads; p.D = d->head_dim;
-    p.chunk = sp.chunk; p.n_split = sp.n_split; p.rec = sp.rec;
+    p.chunk = sp.chunk; p.n_split = sp.n_split; p.rec = sp.rec; p.lds = sp.lds ? 1 : 0;
     p.qscale = qscale_of(d);
     p.dt = dt_of(d);
     return p;

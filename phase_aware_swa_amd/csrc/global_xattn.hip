@@ -858,7 +858,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* ws_part, const 
 // The LDS-streamed kernel's records: one workgroup per (sequence, query
 // head) merges the record ids its stream's range lists (ws_rng: first, first
 // holding keys of the base token's window, last) -- records [id][kinds][4
-// heads of the block][rec].  kinds = 2 (decode) also advances cache_len.
+// head slots, the block's hg used][rec].  kinds = 2 (decode) also advances
+// cache_len.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void lds_merge_kernel(const float* ws_part, const int32_t* ws_rng,
                                                         const int32_t* ws_len, int32_t* cache_len, int64_t max_len,
@@ -875,13 +876,13 @@ __global__ __launch_bounds__(256) void lds_merge_kernel(const float* ws_part, co
         }
         return;
     }
-    const int hblocks = G / 4, S = (Hq / G) * hblocks;
-    const int j = (h / G) * hblocks + (h % G) / 4;          // the head's stream: KV head, 4-head block
+    const int hg = xattn_heads_per_wg(G), hblocks = G / hg, S = (Hq / G) * hblocks;
+    const int j = (h / G) * hblocks + (h % G) / hg;         // the head's stream: KV head, head block
     const int32_t* rg = ws_rng + ((int64_t)b * S + j) * 3;
     const int64_t stride = (int64_t)kinds * 4 * rec;
     for (int kind = 0; kind < kinds; ++kind)
-        merge_splits<E, D>(ws_part + ((int64_t)kind * 4 + h % 4) * rec, stride, rec - D, kind == 0 ? rg[0] : rg[1],
-                           rg[2], kind == 0 ? o_out : o, row);
+        merge_splits<E, D>(ws_part + ((int64_t)kind * 4 + (h % G) % hg) * rec, stride, rec - D,
+                           kind == 0 ? rg[0] : rg[1], rg[2], kind == 0 ? o_out : o, row);
     if (cache_len && h == 0 && tid == 0) cache_len[b] = (int32_t)(L + 1);
 }
 
@@ -948,7 +949,7 @@ hipError_t decode_by_hg(const DecodeParams& p, hipStream_t st)
 
 hipError_t launch_xattn(const XattnParams& p, hipStream_t st)
 {
-    if (xattn_lds_applies(p.dt, p.Hq, p.Hkv)) return launch_xattn_lds(p, st);
+    if (p.lds) return launch_xattn_lds(p, st);
     if (p.dt == Dt::F32) return p.D == 64 ? xattn_by_hg<float, 64>(p, st) : xattn_by_hg<float, 128>(p, st);
     return p.D == 64 ? xattn_by_hg<uint16_t, 64>(p, st) : xattn_by_hg<uint16_t, 128>(p, st);
 }
@@ -1002,10 +1003,13 @@ hipError_t launch_lds_merge(const XattnParams& p, hipStream_t st)
 
 hipError_t launch_lds_merge(const DecodeParams& p, hipStream_t st)
 {
-    if (p.dt != Dt::BF16 || p.D != 128) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((lds_merge_kernel<uint16_t, 128>), dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part, p.ws_rng,
-                       p.ws_len, p.cache_len, p.max_len, p.Hq, p.Hq / p.Hkv, p.rec, 2, (uint16_t*)p.o_out,
-                       (uint16_t*)p.o);
+    if (p.dt != Dt::BF16 || (p.D != 64 && p.D != 128)) return hipErrorInvalidValue;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part, p.ws_rng, p.ws_len, p.cache_len,
+                           p.max_len, p.Hq, p.Hq / p.Hkv, p.rec, 2, (uint16_t*)p.o_out, (uint16_t*)p.o);
+    };
+    if (p.D == 64) go(lds_merge_kernel<uint16_t, 64>);
+    else go(lds_merge_kernel<uint16_t, 128>);
     return hipGetLastError();
 }
 

@@ -50,6 +50,7 @@ struct XattnParams {
     // at rec - D); D + 2, except on the LDS-streamed kernel (D +
     // kXattnLdsRecPad: the values start on a 128-byte line)
     int32_t rec;
+    int32_t lds;          // nonzero: the LDS-streamed kernel (chosen with the split)
     float qscale;
     Dt dt;
 };
@@ -85,7 +86,7 @@ struct DecodeParams {
 };
 
 // Heads of one KV group that one workgroup of the chunked kernels serves.
-inline int xattn_heads_per_wg(int G) { return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
+__host__ __device__ inline int xattn_heads_per_wg(int G) { return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
 
 hipError_t launch_swa(const SwaParams& p, hipStream_t s);
 // Streaming sliding-window kernel: bf16, Hq/Hkv a multiple of 4, window <= kRingMaxWindow.
@@ -108,14 +109,30 @@ hipError_t launch_swa_ring_fused(const SwaParams& p, const XattnParams& x, hipSt
 hipError_t launch_xattn(const XattnParams& p, hipStream_t s);
 // LSE merge of bf16 prefill partials [B][Hq][1][n_split][rec] into o_out.
 hipError_t launch_merge(const XattnParams& p, hipStream_t s);
-// The LDS-streamed MFMA form of the prefill cross-attention (bf16, groups of
-// 4 query heads): a persistent kernel, one workgroup per CU (at most
-// kXattnLdsMaxGrid), each taking an equal run of the launch's keys (at least
-// kXattnLdsSegMin), then the LSE merge.  A launch serves up to
-// kPosPerLaunch sequences; its records take ids rbase .. rbase + region - 1
-// (one per segment: a run's piece of one stream, at most streams + grid of
-// them), where launch i has rbase = i * region.
-inline bool xattn_lds_applies(Dt dt, int Hq, int Hkv) { return dt == Dt::BF16 && (Hq / Hkv) % 4 == 0; }
+// The LDS-streamed MFMA form of the cross-attention (bf16, any group size:
+// streams of xattn_heads_per_wg(G) query heads): a persistent kernel, one
+// workgroup per CU (at most kXattnLdsMaxGrid), each taking an equal run of
+// the launch's keys (at least kXattnLdsSegMin), then the LSE merge.  A
+// launch serves up to kPosPerLaunch sequences; its records take ids
+// rbase .. rbase + region - 1 (one per segment: a run's piece of one stream,
+// at most streams + grid of them), where launch i has rbase = i * region.
+inline bool xattn_lds_applies(Dt dt, int, int) { return dt == Dt::BF16; }
+// In prefill the LDS-streamed kernel takes groups that are multiples of 4,
+// and other groups when the copies read at least kXattnLdsPrefillMinKeys
+// keys over all streams: below that its runs are a few stages long and the
+// lane-parallel kernel's many resident workgroups (and cached loads, which
+// can hit what the SWA pass just wrote) do better (8K MHA: 67 against 70 us).
+constexpr int64_t kXattnLdsPrefillMinKeys = int64_t(1) << 20;
+// In decode, past the one-launch short kernel, it takes groups that are
+// multiples of 4, and other groups when max_len_hint + 1 keys over all
+// streams reach kXattnLdsDecodeMinKeys or one history reaches
+// kXattnLdsDecodeLongKeys; below both the lane-parallel kernel's many
+// workgroups hide the latency better.  Measured per step, lane-parallel
+// against LDS-streamed, MHA d128 with 8K-32K histories: batch 4 62.6
+// against 67.2 us, batch 8 150 against 133; batch 1 with 64K-128K
+// histories 101 against 89.
+constexpr int64_t kXattnLdsDecodeMinKeys = int64_t(3) << 19;
+constexpr int64_t kXattnLdsDecodeLongKeys = int64_t(1) << 16;
 constexpr int kXattnLdsRecPad = 32;   // floats before the values in a partial record
 constexpr int kXattnLdsMaxGrid = 512;
 constexpr int64_t kXattnLdsSegMin = 256;
@@ -134,16 +151,16 @@ hipError_t launch_lds_merge(const XattnParams& p, hipStream_t s);
 hipError_t launch_lds_merge(const DecodeParams& p, hipStream_t s);
 // The decode step: for bf16 steps of at most kDecodeShortMaxSplits chunks
 // of kDecodeShortChunk keys, on the one-launch short-history kernel (fused =
-// 1); longer ones in bf16 with 4-head groups and d = 128 on the
-// LDS-streamed kernel (append, stream, merge); otherwise on the
+// 1); longer bf16 ones on the LDS-streamed kernel (append, stream, merge)
+// when the rule above takes it; the rest (fp32 among them) on the
 // lane-parallel split kernel and a merge kernel.
 constexpr int kDecodeShortChunk = 128;
 constexpr int kDecodeShortMaxSplits = 32;
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
-// The decode step on the LDS-streamed kernel (bf16, groups of 4 query heads,
-// d = 128, more keys than the one-launch short-history kernel takes):
-// append, the copy and the base token in one streaming pass, then the LSE
-// merge of both kinds (which advances cache_len).
+// The decode step on the LDS-streamed kernel (bf16, more keys than the
+// one-launch short-history kernel takes): append, the copy and the base
+// token in one streaming pass, then the LSE merge of both kinds (which
+// advances cache_len).
 hipError_t launch_decode_lds(const DecodeParams& p, hipStream_t s);
 // LSE merge of decode partials [B][Hq][2][n_split][rec] into o_out and o,
 // then cache_len[b] += 1 for every valid sequence.

@@ -1,6 +1,6 @@
-// xattn_lds.hip -- the output copy's full-history cross-attention in
-// prefill for bf16 and groups of 4 query heads per KV head, for gfx950: the
-// cache streams through LDS by direct loads and the contractions run on MFMA.
+// xattn_lds.hip -- the output copy's full-history cross-attention (prefill)
+// and the decode step's copy and base token, for bf16, for gfx950: the cache
+// streams through LDS by direct loads and the contractions run on MFMA.
 //
 // "Orthros:阶段感知异构注意力精读笔记" §2.3 Eq. (5): the copy at original
 // position P attends over every cached key j <= P (§2.4: the mask follows the
@@ -8,24 +8,26 @@
 //
 // One query per head over the whole cache is a pure stream of K/V bytes
 // (about 2 flop per byte per head), so the design is about keeping HBM busy:
-//   - the keys of one (sequence, KV head) are cut into chunks (split-K); an
-//     item is one chunk of one (sequence, KV head, 4-head block): the 4
-//     query heads of the block are served at once, so every K/V byte is read
-//     from HBM once;
-//   - the kernel is persistent: one workgroup per CU walks the items
-//     k = blockIdx, blockIdx + grid, ... of an order that lists every
-//     stream's full chunks before the streams' (possibly short) last
-//     chunks, which balances the workgroups' bytes (each wave holds one
-//     sequence per lane and finds an item's sequence with one ballot over
-//     the lanes' prefix sums);
-//   - an item's keys stream through two 64 KB LDS slots in stages of 4
+//   - a stream is one (sequence, KV head, block of hg query heads): hg = 4
+//     when the group size is a multiple of 4, else 2 or 1; the block's heads
+//     are served at once, so every K/V byte is read from HBM once;
+//   - the kernel is persistent, one workgroup per CU: the launch's keys, in
+//     (sequence, stream, key) order, are cut into one equal run per
+//     workgroup, and a run that crosses from one stream into the next is
+//     worked as segments, each with its own partial records -- every
+//     workgroup gets the same bytes whatever the mix of lengths, and writes
+//     records for one to three segments (each wave holds one sequence per
+//     lane and finds a segment's sequence with one ballot over the lanes'
+//     prefix sums);
+//   - a segment's keys stream through two 64 KB LDS slots in stages of 4
 //     (d = 128) or 8 (d = 64) 32-key pairs, by buffer loads that write LDS
 //     directly (16 per lane per stage, no register staging).  The stage
-//     sequence runs on across items, and stage t + 2 is issued into stage
-//     t's slot as soon as every wave is done with it, while stage t + 1 is
-//     still landing in the other slot: the load queue never runs dry, and a
-//     new item costs no pipeline refill.  The item's query rows and their
-//     scale-offsets come the same way into a small double-buffered LDS area;
+//     sequence runs on across segments, and stage t + 2 is issued into
+//     stage t's slot as soon as every wave is done with it, while stage
+//     t + 1 is still landing in the other slot: the load queue never runs
+//     dry, and a new segment costs no pipeline refill.  The segment's query
+//     rows and their scale-offsets come the same way into a small
+//     double-buffered LDS area;
 //   - the waits are explicit vmcnt counts: each wave counts what it issued
 //     after a stage's loads (the next stage's loads and rows, partial
 //     stores), and vector memory operations retire in issue order, so the
@@ -35,15 +37,16 @@
 //     layout (PairTile's inverse maps: every instruction reads whole
 //     128-byte lines, 8 key rows x 128 bytes, which the loads mark
 //     non-temporal -- the cache is read once per call); the stage's buffer
-//     range ends at the item's last key, so keys past it land as zeros;
+//     range ends at the segment's last key, so keys past it land as zeros;
 //   - pair p of a stage is consumed by wave p % 4: S^T = K Q^T and
-//     O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 with the 4 heads' queries as
-//     columns 0..3 of the B operand (the other 12 are zero: the MFMAs are
+//     O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 with the block's queries as
+//     columns 0 .. hg - 1 of the B operand (the rest are zero: the MFMAs are
 //     idle most of the time either way), V^T from the transposing LDS read,
 //     online softmax per column in exp2 units with a lazy rescale;
-//   - at an item's last stage the 4 waves' states merge through LDS into one
-//     (max, sum, weighted sum of values) record per head, in the layout the
-//     LSE merge reads, padded so that the values start on a 128-byte line.
+//   - at a segment's last stage the 4 waves' states merge through LDS into
+//     one (max, sum, weighted sum of values) record per head, in the layout
+//     the LSE merge reads, padded so that the values start on a 128-byte
+//     line.
 
 #include <atomic>
 #include <type_traits>
@@ -83,26 +86,27 @@ __device__ __forceinline__ int64_t run_keys(int64_t total, int nwg)
     return e > kXattnLdsSegMin ? e : kXattnLdsSegMin;
 }
 
-// One segment: keys lo .. hi (len keys) of stream j = (KV head g, 4-head
-// block hb) of sequence b, hi <= P (the copy's position), nst stages, its
-// partial records under record id `id`.  In decode, P is the cache length L
+// One segment: keys lo .. hi (len keys) of stream j = (KV head g, the block
+// of query heads from h0) of sequence b, hi <= P (the copy's position), nst
+// stages, its partial records under record id `id`.  In decode, P is the cache length L
 // and `win` marks a segment that holds keys of the base token's window
 // [wlo, L].  Key indices fit 32 bits (positions are below 2^31); cache
 // offsets and positions in the launch's key order take 64.
 struct Item {
-    int b, g, hb, id, nst, len;
+    int b, g, h0, id, nst, len;
     int lo, hi, wlo;
     bool win;
 };
 
 // PT = XattnParams: prefill, the copy's positions by value in `pos`.
 // PT = DecodeParams: a decode step, L = cache_len[b] read on the device (the
-// new token's K/V are already in slot L), and the base token's 4 heads ride
-// along as query columns 4..7 of the same MFMAs (their keys are a subset of
-// the copy's), leaving a second partial per head for the chunks that hold
-// its window.  Record ids of this launch start at rbase.
+// new token's K/V are already in slot L), and the base token's heads ride
+// along as query columns 4 .. 3 + hg of the same MFMAs (their keys are a
+// subset of the copy's), leaving a second partial per head for the segments
+// that hold its window.  Record ids of this launch start at rbase.
 template <int D, typename PT>
-__global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, int rbase, PosBlock pos)
+__global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, int rbase, int hg, int hblocks,
+                                                        PosBlock pos)
 {
     constexpr bool DEC = std::is_same<PT, DecodeParams>::value;
     using R = PairTile<D>;
@@ -130,7 +134,10 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, gq = lane >> 4;
-    const int hblocks = (a.Hq / a.Hkv) / 4;
+    // a stream is one KV head's block of hg = xattn_heads_per_wg(G) query
+    // heads (4, or 2 or 1 when the group size G is not a multiple of 4;
+    // hblocks = G / hg blocks per KV head): the block's heads are MFMA query
+    // columns 0 .. hg - 1 (and hg more for the base token in decode)
     const int S = a.Hkv * hblocks;        // streams of a sequence
     const uint16_t* k_cache = (const uint16_t*)a.k_cache;
     const uint16_t* v_cache = (const uint16_t*)a.v_cache;
@@ -209,8 +216,12 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
         // the launchers check S * cap)
         const uint32_t off = (uint32_t)(at - readlane64(excl, bl));
         const int j = (int)(off / (uint32_t)(L + 1));
-        it.g = j / hblocks;
-        it.hb = j - it.g * hblocks;
+        // (g only addresses the cache: a vector division, so that no scalar
+        // reciprocal of hblocks is held across the loop)
+        int hbv = hblocks;
+        asm volatile("" : "+v"(hbv));
+        it.g = (int)((unsigned)j / (unsigned)hbv);
+        it.h0 = j * hg;                   // = g * G + (j - g * hblocks) * hg
         it.lo = (int)(off - (uint32_t)j * (uint32_t)(L + 1));
         it.hi = run - rel > L - it.lo ? L : it.lo + (run - rel) - 1;
         it.len = it.hi - it.lo + 1;
@@ -254,7 +265,7 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
     // the item's query rows and scale-offsets into qa[q]: region i by wave
     // i % 4, one load instruction of D / 2 lanes each
     auto row_src = [&](const Item& it, int r) -> const uint16_t* {
-        const int h0 = it.g * (a.Hq / a.Hkv) + it.hb * 4;
+        const int h0 = it.h0;
         const int64_t qrow = ((int64_t)it.b * a.Hq + h0) * D;
         if constexpr (DEC) {
             if (r == 3) return (const uint16_t*)a.q + qrow;
@@ -271,7 +282,8 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
         asm volatile("" : "+s"(w0));
 #pragma unroll
         for (int r = w0; r < NREG; r += 4) {
-            const i32x4 rs = buffer_words(row_src(it, r), HRE * 2);
+            // the block's hg rows; rows past them read as zeros
+            const i32x4 rs = buffer_words(row_src(it, r), (int64_t)hg * D * 2);
             if (lane < HRE / 8) load_lds16(rs, 16 * lane, 0, &qa[q][r * HRE]);
         }
     };
@@ -300,7 +312,7 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
         // leaves the scalar file room for the rest without spilling (its
         // stage count and length stay scalar: the cursor's branches must
         // stay uniform)
-        asm volatile("" : "+v"(ii.b), "+v"(ii.g), "+v"(ii.hb), "+v"(ii.lo), "+v"(ii.hi));
+        asm volatile("" : "+v"(ii.b), "+v"(ii.g), "+v"(ii.h0), "+v"(ii.lo), "+v"(ii.hi));
         si = 0;
         qi ^= 1;
     };
@@ -355,7 +367,7 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
             }
         }
         if constexpr (DEC) {
-            // the base token's columns 4..7: keys below its window
+            // the base token's columns 4 .. 3 + hg: keys below its window
             if (win && key0 < wlo) {
                 const int lim = wlo - key0 < 64 ? wlo - key0 - 4 * gq : 64;
                 if ((n >> 2) == 1) {
@@ -415,7 +427,7 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
             // n - 4 when the item holds keys of its window; zero
             // otherwise), dims 32 i + 8 gq .. + 7 -- and fresh softmax states
             const float qs = a.qscale;
-            const bool live = (n >> 2) == 0 || (DEC && (n >> 2) == 1 && ci.win);
+            const bool live = ((n >> 2) == 0 || (DEC && (n >> 2) == 1 && ci.win)) && (n & 3) < hg;
             const uint16_t* qr = qa[qc] + (DEC && (n >> 2) == 1 ? 3 * HRE : 0) + (n & 3) * D;
 #pragma unroll
             for (int i = 0; i < NQ; ++i) {
@@ -475,10 +487,13 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
         wait_lgkm0();
         block_barrier();
         {
-            const int nkind = DEC && ci.win ? 2 : 1;
+            const int nkind = wv >= hg ? 0 : DEC && ci.win ? 2 : 1;   // wave w writes head w of the block
+            // (the wave index read afresh: no record base is held across the loop)
+            int w0 = wv;
+            asm volatile("" : "+s"(w0));
             for (int kind = 0; kind < nkind; ++kind) {
                 const int col = 4 * kind + wv;
-                float* o = a.ws_part + (((int64_t)ci.id * KINDS + kind) * 4 + wv) * REC;
+                float* o = a.ws_part + (((int64_t)ci.id * KINDS + kind) * 4 + w0) * REC;
                 float mw[4], M = kNegBig;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
@@ -571,7 +586,8 @@ unsigned lds_grid(int64_t keys)
 
 hipError_t launch_xattn_lds(const XattnParams& p, hipStream_t st)
 {
-    const int S = p.Hkv * ((p.Hq / p.Hkv) / 4);
+    const int G = p.Hq / p.Hkv, hg = xattn_heads_per_wg(G);
+    const int S = p.Hkv * (G / hg);
     if (p.rec != p.D + kXattnLdsRecPad || p.cap > kLdsMaxCap || (int64_t)S * p.cap > UINT32_MAX)
         return hipErrorInvalidValue;
     const int64_t region = xattn_lds_region(p.B, S);
@@ -588,10 +604,11 @@ hipError_t launch_xattn_lds(const XattnParams& p, hipStream_t st)
         if (!grid) return hipErrorInvalidValue;
         const int rbase = (int)(b0 / kPosPerLaunch * region);
         if (p.D == 64)
-            hipLaunchKernelGGL((xattn_lds_kernel<64, XattnParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, rbase, pos);
+            hipLaunchKernelGGL((xattn_lds_kernel<64, XattnParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, rbase, hg,
+                               G / hg, pos);
         else
-            hipLaunchKernelGGL((xattn_lds_kernel<128, XattnParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, rbase,
-                               pos);
+            hipLaunchKernelGGL((xattn_lds_kernel<128, XattnParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, rbase, hg,
+                               G / hg, pos);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -600,14 +617,17 @@ hipError_t launch_xattn_lds(const XattnParams& p, hipStream_t st)
 
 hipError_t launch_decode_lds(const DecodeParams& p, hipStream_t st)
 {
-    const int S = p.Hkv * ((p.Hq / p.Hkv) / 4);
+    const int G = p.Hq / p.Hkv, hg = xattn_heads_per_wg(G);
+    const int S = p.Hkv * (G / hg);
     const int nb_max = p.B < kPosPerLaunch ? p.B : kPosPerLaunch;
-    if (p.D != 128 || p.rec != p.D + kXattnLdsRecPad || p.cap > kLdsMaxCap || (int64_t)S * p.cap > UINT32_MAX ||
-        xattn_lds_records(p.B, S) >= INT32_MAX || !lds_grid((int64_t)nb_max * S * (p.max_len + 1)))
+    if ((p.D != 64 && p.D != 128) || p.rec != p.D + kXattnLdsRecPad || p.cap > kLdsMaxCap ||
+        (int64_t)S * p.cap > UINT32_MAX || xattn_lds_records(p.B, S) >= INT32_MAX ||
+        !lds_grid((int64_t)nb_max * S * (p.max_len + 1)))
         return hipErrorInvalidValue;
     // the new token's K/V into slot L first: the streaming kernel reads
     // every key of [0, L] from the cache
-    hipLaunchKernelGGL((decode_append_kernel<128>), dim3(p.B), dim3(256), 0, st, p);
+    if (p.D == 64) hipLaunchKernelGGL((decode_append_kernel<64>), dim3(p.B), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((decode_append_kernel<128>), dim3(p.B), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t region = xattn_lds_region(p.B, S);
@@ -617,8 +637,12 @@ hipError_t launch_decode_lds(const DecodeParams& p, hipStream_t st)
         // keys of this launch, at most (every length at max_len)
         const unsigned grid = lds_grid((int64_t)nb * S * (p.max_len + 1));
         const int rbase = (int)(b0 / kPosPerLaunch * region);
-        hipLaunchKernelGGL((xattn_lds_kernel<128, DecodeParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, rbase,
-                           unused);
+        if (p.D == 64)
+            hipLaunchKernelGGL((xattn_lds_kernel<64, DecodeParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, rbase, hg,
+                               G / hg, unused);
+        else
+            hipLaunchKernelGGL((xattn_lds_kernel<128, DecodeParams>), dim3(grid), dim3(256), 0, st, p, b0, nb, rbase,
+                               hg, G / hg, unused);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -97,23 +97,31 @@ def test_decode_bad_arguments():
 
 @pytest.mark.parametrize("B,Hq,Hkv,d,hint,kind", [(16, 32, 8, 128, 132095, "lds"), (4, 32, 8, 128, 32767, "lds"),
                                                  (1, 32, 8, 128, 4095, "short"), (1, 32, 8, 128, 4096, "lds"),
-                                                 (80, 32, 8, 128, 24575, "lds"), (4, 16, 8, 128, 32767, "lane"),
-                                                 (11, 32, 8, 64, 131071, "lane"), (3, 16, 8, 64, 4095, "short")],
+                                                 (80, 32, 8, 128, 24575, "lds"), (8, 16, 8, 128, 32767, "lds"),
+                                                 (4, 16, 8, 128, 32767, "lane16"), (4, 16, 8, 128, 65535, "lds"),
+                                                 (11, 32, 8, 64, 131071, "lds"), (3, 16, 8, 64, 4095, "short"),
+                                                 (5, 8, 8, 128, 65535, "lds"), (5, 8, 8, 128, 9000, "lane16"),
+                                                 (4, 32, 8, 128, 32767, "lane"), (3, 16, 8, 64, 4095, "lane")],
                          ids=["B16-128K-lds", "B4-32K-lds", "B1-4K-short", "B1-4K-plus-one-lds",
-                              "B80-24K-lds-two-launches", "B4-32K-G2-lane", "B11-128K-d64-lane", "B3-4K-G2-d64-short"])
+                              "B80-24K-lds-two-launches", "B8-32K-G2-lds", "B4-32K-G2-bf16-lane", "B4-64K-G2-lds",
+                              "B11-128K-d64-lds", "B3-4K-G2-d64-short", "B5-64K-MHA-lds", "B5-9K-MHA-bf16-lane",
+                              "B4-32K-f32-lane", "B3-4K-G2-d64-f32-lane"])
 def test_decode_workspace_layout(B, Hq, Hkv, d, hint, kind):
     """The decode workspace: 256-byte-aligned arrival counters and lengths,
     then the partials.  bf16 steps of at most 32 chunks of 128 keys run on
     the one-launch short kernel (two kinds of records of d + 4 floats per
-    chunk and query head); longer ones with 4-head groups and d = 128 on the
-    LDS-streamed kernel (a 256-byte-aligned table of 3 record ids per
-    stream, then 2 kinds x 4 heads x (d + 32) floats per id, ids for every
-    stream of a launch of up to 64 sequences plus one per workgroup, 512 at
-    most); the rest on the lane kernel (power-of-two chunks >= 256 keys for
-    about 16384 workgroups, two kinds of records of d + 2 floats per chunk
-    and query head).  A workspace one byte short is rejected before
-    anything runs."""
-    desc = mk(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=128, dtype=binding.BF16)
+    chunk and query head); longer bf16 ones on the LDS-streamed kernel (a
+    256-byte-aligned table of 3 record ids per stream -- a stream being a
+    KV head's block of 4, 2 or 1 query heads -- then 2 kinds x 4 head slots
+    x (d + 32) floats per id, ids for every stream of a launch of up to 64
+    sequences plus one per workgroup, 512 at most) when the group is a
+    multiple of 4, the keys over all streams reach 3 x 2^19 or the history 2^16
+    keys; the rest (fp32 among them) on the lane kernel (power-of-two
+    chunks >= 256 keys for about 16384 workgroups, two kinds of records of
+    d + 2 floats per chunk and query head).  A workspace one byte short is
+    rejected before anything runs."""
+    dt = binding.F32 if kind == "lane" else binding.BF16
+    desc = mk(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=128, dtype=dt)
     keys, G = hint + 1, Hq // Hkv
     S = Hkv * (G // (4 if G % 4 == 0 else 2 if G % 2 == 0 else 1))
     streams = B * S
@@ -140,18 +148,30 @@ def test_decode_workspace_layout(B, Hq, Hkv, d, hint, kind):
 
 
 def test_prefill_workspace_layout():
-    """The prefill workspace of the separate cross-attention (orthros_global_xattn)
-    on the LDS-streamed kernel (bf16, 4-head groups): lengths, the record-id
-    table (3 per stream), then records of 4 heads x (d + 32) floats for every
-    stream of a launch of up to 64 sequences plus 512 -- independent of T.
-    The fused prefill (window <= 129) may need more: its size is the larger."""
-    for B, Hq, Hkv, d in ((2, 32, 8, 128), (70, 16, 2, 64)):
+    """The prefill workspace of the separate cross-attention (orthros_global_xattn).
+    On the LDS-streamed kernel -- bf16 groups that are multiples of 4, and
+    other bf16 groups once the copies read at least 2^20 keys over all
+    streams -- lengths, the record-id table (3 per stream), then records of 4
+    head slots x (d + 32) floats for every stream of a launch of up to 64
+    sequences plus 512, independent of T; else lengths and partials of
+    d + 2 floats per power-of-two chunk (>= 256 keys, about 2048 workgroups)
+    and query head.  (The fused prefill, window <= 129, may need more: its
+    size is the larger; window 200 here.)"""
+    for B, Hq, Hkv, d in ((2, 32, 8, 128), (70, 16, 2, 64), (3, 8, 4, 128), (2, 16, 16, 128)):
         desc = mk(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=200, dtype=binding.BF16)
-        S = Hkv * (Hq // Hkv // 4)
-        ids = -(-B // 64) * (min(B, 64) * S + 512)
-        need = -(-B * 4 // 256) * 256 + -(-B * S * 3 * 4 // 256) * 256 + ids * 4 * (d + 32) * 4
+        G = Hq // Hkv
+        S = Hkv * (G // (4 if G % 4 == 0 else 2 if G % 2 == 0 else 1))
+        lens = -(-B * 4 // 256) * 256
         for T in (1000, 131072):
-            assert binding.prefill_workspace_size(desc, T) == need
+            if G % 4 == 0 or T * B * S >= 1 << 20:
+                ids = -(-B // 64) * (min(B, 64) * S + 512)
+                need = lens + -(-B * S * 3 * 4 // 256) * 256 + ids * 4 * (d + 32) * 4
+            else:
+                chunk = 256
+                while chunk < -(-T * B * S // 2048):
+                    chunk *= 2
+                need = lens + B * Hq * -(-T // chunk) * (d + 2) * 4
+            assert binding.prefill_workspace_size(desc, T) == need, (B, Hq, Hkv, d, T)
 
 
 def test_workspace_sizes():

@@ -57,8 +57,8 @@ def test_decode_steps_parity(Hq, Hkv, d, w, dtype):
 
 @pytest.mark.parametrize("d", [128, 64])
 def test_decode_lengths_at_stage_and_chunk_edges(d):
-    """bf16, 4-head groups, short histories (d = 128: the LDS-streamed
-    kernel, d = 64: the lane-parallel kernel): lengths whose new key L is
+    """bf16, 4-head groups, short histories (the LDS-streamed kernel, at
+    d = 128 and d = 64): lengths whose new key L is
     the first or last key of a 128- or 256-key block and of a 256-key chunk,
     and one that leaves the last chunk a single key; 3 steps each."""
     lens = [0, 127, 128, 255, 256, 511, 1023, 4095]

@@ -19,8 +19,9 @@ of its row, compared bit for bit (tests/probe_util.py).  Kernels covered:
     token's window straddling run boundaries at w = 128 and spanning several
     runs at w = 4096 and 5000, and the copy over ~64K-key histories with
     marked keys on both sides of every run boundary;
-  decode, lane-parallel kernel (short histories, groups of 2 and 4, d 128
-    and 64, windows 1, 128 and 300).
+  decode, one-launch short-history kernel (groups of 2, 4 and 8, d 128
+    and 64, windows 1, 128 and 300), and the LDS-streamed kernel past
+    4096 keys with groups of 2 and d = 64.
 (MI355X only.)"""
 import pytest
 import torch
@@ -58,31 +59,29 @@ def decode_split_of(B, Hq, Hkv, d, hint):
     """(uses the LDS-streamed kernel, workspace bytes) of a bf16 decode step,
     from the split rule of orthros_decode_step: 128-key chunks when that
     makes at most 32 (the one-launch kernel, records of d + 4 floats, two
-    kinds per query head); else, with 4-head groups and d = 128, the
-    LDS-streamed kernel (record-id table, then 2 x 4 records of d + 32
-    floats per id: every stream of a launch of up to 64 sequences plus 512);
-    else power-of-two chunks of at least 256 keys for about 16384
-    workgroups (records of d + 2 floats); arrival counters and lengths
-    first."""
+    kinds per query head); else the LDS-streamed kernel (record-id table,
+    then 2 x 4 records of d + 32 floats per id: every stream -- a KV head's
+    block of 4, 2 or 1 query heads -- of a launch of up to 64 sequences plus
+    512) when the group is a multiple of 4, the keys over all streams reach
+    3 x 2^19 or the history 2^16 keys; else the lane-parallel kernel
+    (power-of-two chunks >= 256 keys for about 16384 workgroups, records of
+    d + 2 floats); arrival counters and lengths first."""
     G = Hq // Hkv
     hpw = 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
     S = Hkv * (G // hpw)
     streams = B * S
     keys = hint + 1
-    lds = keys > 32 * 128 and G % 4 == 0 and d == 128
     head = -(-B * (S + 1) * 4 // 256) * 256 + -(-B * 4 // 256) * 256
-    if lds:
+    if keys <= 32 * 128:
+        n_split = -(-keys // 128)                # short steps: one launch over 128-key chunks
+        return False, head + B * Hq * 2 * n_split * (d + 4) * 4
+    if G % 4 == 0 or keys * streams >= 3 << 19 or keys >= 1 << 16:
         ids = -(-B // 64) * (min(B, 64) * S + 512)
         return True, head + -(-streams * 3 * 4 // 256) * 256 + ids * 2 * 4 * (d + 32) * 4
-    if keys <= 32 * 128:                         # short steps: one launch over 128-key chunks
-        chunk = 128
-    else:
-        chunk, need = 256, -(-keys * streams // 16384)
-        while chunk < need:
-            chunk *= 2
-    rec = d + (4 if chunk == 128 else 2)
-    n_split = -(-keys // chunk)
-    return False, head + B * Hq * 2 * n_split * rec * 4
+    chunk = 256
+    while chunk < -(-keys * streams // 16384):
+        chunk *= 2
+    return False, head + B * Hq * 2 * -(-keys // chunk) * (d + 2) * 4
 
 
 def lds_run_starts(lens, S, hint):
@@ -349,18 +348,23 @@ def test_probe_decode_lds_copy_marked_run_edges():
     decode_probe(32, 32, 8, 128, 128, lens, 2, seed=332, marked=True, expect_lds=True)
 
 
-@pytest.mark.parametrize("Hq,Hkv,d,w,longest", [(8, 2, 128, 128, 4095), (8, 2, 128, 1, 4095),
-                                               (8, 2, 64, 300, 4095), (4, 2, 128, 128, 4095),
-                                               (16, 2, 128, 128, 4095), (4, 2, 128, 128, 9000),
-                                               (8, 2, 64, 128, 9000)],
-                         ids=["G4", "G4-w1", "G4-d64-w300", "G2", "G8", "G2-two-launches", "G4-d64-two-launches"])
-def test_probe_decode_lane_kernel(Hq, Hkv, d, w, longest):
+@pytest.mark.parametrize("Hq,Hkv,d,w,longest,hint,lds",
+                         [(8, 2, 128, 128, 4095, None, False), (8, 2, 128, 1, 4095, None, False),
+                          (8, 2, 64, 300, 4095, None, False), (4, 2, 128, 128, 4095, None, False),
+                          (16, 2, 128, 128, 4095, None, False), (4, 2, 128, 128, 9000, None, False),
+                          (4, 2, 128, 128, 9000, 65535, True), (2, 2, 64, 128, 9000, 65535, True),
+                          (8, 2, 64, 128, 9000, None, True)],
+                         ids=["G4", "G4-w1", "G4-d64-w300", "G2", "G8", "G2-lane", "G2-lds", "MHA-d64-lds",
+                              "G4-d64-lds"])
+def test_probe_decode_short_kernel(Hq, Hkv, d, w, longest, hint, lds):
     """Short histories: lengths 0, 1, around the window, and on the edges of
     128- and 256-key chunks; three steps.  Up to 4096 keys the step is one
     launch of the short-history kernel (128-key chunks, merged in the
-    launch); with a 9000-key history and groups of 2, or d = 64, it is the
-    lane-parallel split kernel and a merge kernel (256-key chunks)."""
+    launch); with a 9000-key history it is the LDS-streamed kernel for
+    groups of 4 (d = 64: 8 pairs per stage) and, for other groups, the
+    lane-parallel kernel -- or the LDS-streamed one once max_len_hint + 1
+    reaches 2^16 keys (2- and 1-head streams)."""
     lens = [0, 1, 126, 127, 128, 255, 256, 1000, longest]
     if longest == 4095:
         lens[-1] = 4093                          # keys = max_len_hint + 1 = 4096: the one-launch kernel
-    decode_probe(len(lens), Hq, Hkv, d, w, lens, 3, seed=340 + w + d + Hq, expect_lds=False)
+    decode_probe(len(lens), Hq, Hkv, d, w, lens, 3, seed=340 + w + d + Hq, expect_lds=lds, hint=hint)

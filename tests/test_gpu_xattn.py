@@ -5,11 +5,13 @@ copy's original position P) -- against the fp64 oracle, through the C ABI
 (MI355X only).
 
 The caches are filled by plain copies of K/V ([B][T][Hkv][d] -> [B][Hkv][cap][d]),
-so only the cross-attention kernels run.  bf16 with 4-head groups takes the
-LDS-streamed MFMA kernel (stages of 128 keys at d = 128, 256 at d = 64; each
-workgroup takes an equal run of the launch's keys, at least 256, in
-(sequence, stream, key) order, so runs cross stream boundaries); the other
-shapes take the lane-parallel chunk kernel (power-of-two chunks).
+so only the cross-attention kernels run.  bf16 with groups of 4 (or any
+group, once the copies read at least 2^20 keys over all streams) takes the
+LDS-streamed MFMA kernel (streams of 4, 2 or 1 query heads per KV head;
+stages of 128 keys at d = 128, 256 at d = 64; each workgroup takes an equal
+run of the launch's keys, at least 256, in (sequence, stream, key) order, so
+runs cross stream boundaries); the rest takes the lane-parallel chunk
+kernel (power-of-two chunks).
 Positions sit on both sides of pair (32), stage and chunk edges."""
 import pytest
 import torch
@@ -51,7 +53,11 @@ def run_xattn_case(B, Hq, Hkv, d, T, out_pos, dtype=BF16, seed=0, cap_extra=3):
     (3, 16, 4, 128, 3000, [2999, 1, 1500]),      # 4 heads per group, several blocks of 4
     (2, 32, 4, 128, 2500, [2047, 2048]),         # 8 heads per group: two 4-head blocks
     (2, 8, 2, 128, 1234, [1233, 600]),
-    (2, 4, 2, 128, 700, [699, 100]),             # G = 2: the lane-parallel kernel
+    (2, 4, 2, 128, 700, [699, 100]),             # G = 2, few keys: the lane-parallel kernel
+    (3, 3, 3, 64, 900, [899, 0, 450]),           # MHA, d = 64: the lane-parallel kernel
+    (1, 8, 8, 128, 140000, [139999]),            # MHA, 1.1M keys: the LDS kernel, 1-head streams
+    (2, 4, 2, 64, 300000, [299999, 123456]),     # G = 2, d = 64, 1.2M keys: the LDS kernel, 2-head streams
+    (2, 6, 2, 128, 180000, [179999, 90000]),     # G = 3: 1-head streams, three per KV head
 ])
 def test_xattn_parity(B, Hq, Hkv, d, T, pos):
     run_xattn_case(B, Hq, Hkv, d, T, pos, seed=T + B)
