@@ -428,83 +428,113 @@ __device__ __forceinline__ void rec_st(f32x4 v, rsrc_t r, uint32_t off)
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kCachePolicySc1);
 }
 
+// Maximum and sum over the whole wave, every lane given the result (DPP
+// inside rows of 16 lanes, then row broadcasts into lane 63; fixed order).
+__device__ __forceinline__ float wave_max(float x)
+{
+    x = fmaxf(x, dpp_mov<kDppXor1>(x));
+    x = fmaxf(x, dpp_mov<kDppXor2>(x));
+    x = fmaxf(x, dpp_mov<kDppHalfMirror>(x));
+    x = fmaxf(x, dpp_mov<kDppMirror>(x));
+    return wave_max_of_rows(x);
+}
+__device__ __forceinline__ float wave_sum(float x)
+{
+    constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+    x = group_sum<16>(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kRowBcast15, 0xa, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kRowBcast31, 0xc, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
 // The merge of a whole head block by one workgroup, from records of D + 4
-// floats (max, sum, 0, 0, weighted values) read at device scope.  The block's
+// floats (max, sum, 0, 0, weighted values) read at device scope.  A head's
 // (kind, split) records -- the copy's splits 0 .. s1, then the base token's
-// sw0 .. s1 -- are dealt round-robin to NG groups of D / 4 threads per head,
-// each thread one 4-value quad: a group issues the loads of up to RB records
-// at once (one memory round trip for the short steps' at most 32 + a few
-// records), folds them in order into a running (max, sum, values) per kind,
-// and the groups' states then combine through LDS in group order, so the
-// result is run-to-run identical.  Every thread of the workgroup takes part
-// (there is a barrier); `scratch` is LDS for 256 x 12 floats.
+// sw0 .. s1, at most 64 -- are indexed k = 0 .. np - 1.  Each of the head's
+// W = 4 / HG waves loads every header in one instruction (lane k: record
+// k), takes the per-kind maximum and the weights f_k = 2^(max_k - max) by
+// wave reductions, and so the denominators; the values are then dealt
+// round-robin to the head's groups of D / 4 threads (one 4-value quad
+// each), which issue all their loads of a round at once (one memory round
+// trip for up to NG RB records) and accumulate f_k-weighted sums with no
+// rescaling.  The groups' sums combine in a fixed order (shuffles within a
+// wave, LDS across waves), so the result is run-to-run identical.  Every
+// thread of the workgroup takes part; with W > 1 there is a barrier.
+// `scratch` is LDS for 8 D + 4 x 130 floats.
 template <int D, int HG>
-__device__ __forceinline__ void merge_block(rsrc_t part, int64_t head_stride, int64_t kind_stride, int sw0, int s1,
+__device__ __forceinline__ void merge_block(rsrc_t part, uint32_t head_bytes, uint32_t kind_bytes, int sw0, int s1,
                                             uint16_t* o_out, uint16_t* o, int64_t row0, float* scratch)
 {
-    constexpr int TPR = D / 4;
-    constexpr int NG = 256 / (HG * TPR);         // groups per head
+    constexpr int TPR = D / 4;                   // threads per record
+    constexpr int NGW = 64 / TPR;                // groups per wave
+    constexpr int W = 4 / HG;                    // waves per head
+    constexpr int NG = NGW * W;                  // groups per head
     constexpr int RB = (36 + NG - 1) / NG;       // records per group and round
     constexpr int REC = D + 4;
-    static_assert(NG >= 2 && HG * NG * TPR == 256, "thread layout");
-    const int tid = threadIdx.x;
-    const int hh = tid / (NG * TPR), grp = (tid / TPR) % NG, qd = tid % TPR;
+    static_assert(HG * W == 4 && NGW >= 2, "thread layout");
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int hh = wv / W, grp = (wv % W) * NGW + lane / TPR, qd = lane % TPR;
     const int n0 = s1 + 1, np = n0 + (s1 - sw0 + 1);   // the copy's records, then the base token's
-    float M[2] = {kNegBig, kNegBig}, den[2] = {0.f, 0.f};
-    f32x4 num[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    const uint32_t hbase = hh * head_bytes;
+    auto rec_off = [&](int k) {
+        const int kind = k >= n0, sk = kind ? sw0 + k - n0 : k;
+        return hbase + (kind ? kind_bytes : 0u) + (uint32_t)sk * (REC * 4);
+    };
+    // headers: lane k holds record k's (max, sum); per-kind maxima and sums
+    const f32x4 h4 = rec_ld(part, rec_off(lane < np ? lane : np - 1));
+    const bool own = lane < np, hk = lane >= n0;
+    const float m0 = wave_max(own && !hk ? h4[0] : kNegBig), m1 = wave_max(own && hk ? h4[0] : kNegBig);
+    const float f = own ? fast_exp2(h4[0] - (hk ? m1 : m0)) : 0.f;
+    const float d0 = wave_sum(hk ? 0.f : f * h4[1]), d1 = wave_sum(hk ? f * h4[1] : 0.f);
+    // the weights per kind, [k][kind] in this wave's LDS slot (k = 64: zero),
+    // so the value loop needs no per-record lane masks (a wave reads back
+    // its own writes in order: no barrier)
+    float2* wts = reinterpret_cast<float2*>(scratch + 8 * D) + wv * 65;
+    wts[lane] = float2{hk ? 0.f : f, hk ? f : 0.f};
+    if (lane == 0) wts[64] = float2{0.f, 0.f};
+    // values: group grp takes records grp, grp + NG, ...
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 a0 = zero, a1 = zero;
     for (int p0 = grp; p0 < np; p0 += NG * RB) {
-        f32x4 hd[RB], v[RB];
+        f32x4 v[RB];
+#pragma unroll
+        for (int k = 0; k < RB; ++k) v[k] = rec_ld(part, rec_off(min(p0 + NG * k, np - 1)) + 16 + 16 * qd);
 #pragma unroll
         for (int k = 0; k < RB; ++k) {
-            const int pk = p0 + NG * k < np ? p0 + NG * k : np - 1;
-            const int kind = pk >= n0, sk = kind ? sw0 + pk - n0 : pk;
-            const uint32_t off = (uint32_t)((hh * head_stride + kind * kind_stride + (int64_t)sk * REC) * 4);
-            hd[k] = rec_ld(part, off);
-            v[k] = rec_ld(part, off + 16 + 16 * qd);
-        }
-#pragma unroll
-        for (int k = 0; k < RB; ++k) {
-            // (no early exit: the arrays stay in registers)
-            const int pk = p0 + NG * k;
-            if (pk < np) {
-                const int kind = pk >= n0;
-                const float mn = fmaxf(M[kind], hd[k][0]);
-                const float sc = fast_exp2(M[kind] - mn), f = fast_exp2(hd[k][0] - mn);
-                den[kind] = den[kind] * sc + f * hd[k][1];
-                num[kind] = num[kind] * sc + f * v[k];
-                M[kind] = mn;
-            }
+            const float2 w = wts[min(p0 + NG * k, 64)];
+            a0 += w.x * v[k];
+            a1 += w.y * v[k];
         }
     }
-    // the groups' states: [head][kind][group][quad] x (max, sum, 4 values)
-    auto at = [&](int h, int kind, int g, int q) { return scratch + (((h * 2 + kind) * NG + g) * TPR + q) * 6; };
+    // the groups' sums in a fixed order: lanes 0..31 end with the copy's,
+    // 32..63 with the base token's (the swap hands each half the other's)
+    if constexpr (TPR == 16)
 #pragma unroll
-    for (int kind = 0; kind < 2; ++kind) {
-        float* w = at(hh, kind, grp, qd);
-        w[0] = M[kind];
-        w[1] = den[kind];
-        w[2] = num[kind][0];
-        w[3] = num[kind][1];
-        w[4] = num[kind][2];
-        w[5] = num[kind][3];
-    }
-    __syncthreads();
-    if (grp < 2) {
-        const int kind = grp;                     // group 0 finishes the copy, group 1 the base token
-        float Mt = kNegBig;
-        for (int g = 0; g < NG; ++g) Mt = fmaxf(Mt, at(hh, kind, g, qd)[0]);
-        float dt = 0.f;
-        f32x4 nt = {0.f, 0.f, 0.f, 0.f};
-        for (int g = 0; g < NG; ++g) {
-            const float* r = at(hh, kind, g, qd);
-            const float f = fast_exp2(r[0] - Mt);
-            dt += f * r[1];
-            nt += f * f32x4{r[2], r[3], r[4], r[5]};
+        for (int e = 0; e < 4; ++e) {
+            a0[e] += __shfl_xor(a0[e], 16);
+            a1[e] += __shfl_xor(a1[e], 16);
         }
+    f32x4 t;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0[e]), __float_as_uint(a1[e]), false, false);
+        t[e] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    const int kind = lane >> 5;                  // the lanes (lane & 31) < TPR finish quad qd of this kind
+    if constexpr (W > 1) {
+        auto at = [&](int j) { return scratch + (((hh * W + j) * 2 + kind) * TPR + qd) * 4; };   // [head][wave][kind][quad]
+        if ((lane & 31) < TPR) *(f32x4*)at(wv % W) = t;
+        __syncthreads();
+        if (wv % W == 0) {
+            t = *(const f32x4*)at(0);
+            for (int j = 1; j < W; ++j) t += *(const f32x4*)at(j);
+        }
+    }
+    if (wv % W == 0 && (lane & 31) < TPR) {
+        const float inv = 1.f / (kind ? d1 : d0);
         uint16_t* out = kind ? o : o_out;
         const int64_t row = row0 + (int64_t)hh * D + 4 * qd;
-        const float inv = 1.f / dt;
-        *(u32x2*)(out + row) = u32x2{pack_bf16x2(nt[0] * inv, nt[1] * inv), pack_bf16x2(nt[2] * inv, nt[3] * inv)};
+        *(u32x2*)(out + row) = u32x2{pack_bf16x2(t[0] * inv, t[1] * inv), pack_bf16x2(t[2] * inv, t[3] * inv)};
     }
 }
 
@@ -518,7 +548,8 @@ __device__ __forceinline__ void merge_block(rsrc_t part, int64_t head_stride, in
 //     direct buffer-to-LDS loads in the pair layout of the streaming kernels
 //     (keys past L land as zeros), issued together with the query rows, and
 //     the new token's key L is then written over its slot there from
-//     k_new / v_new (the cache slot is being written by this launch);
+//     k_new / v_new, and the wave of the first head block stores that row
+//     into cache slot L (the append);
 //   - S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16 with
 //     the copy's HG heads as query columns 0..HG-1 and the base token's as
 //     columns HG..2HG-1 (live when the chunk holds keys of its window;
@@ -528,9 +559,10 @@ __device__ __forceinline__ void merge_block(rsrc_t part, int64_t head_stride, in
 //     partial record per (head, kind), D + 4 floats (max, sum, 0, 0,
 //     weighted values), stored at device scope in 16-byte quads.
 // The workgroup then counts itself in on the block's counter; the last of
-// the block's n_split workgroups to arrive merges the block into o_out and
-// o, and the last block of the sequence to finish merging advances
-// cache_len[b].  Every workgroup of the grid arrives, those past the history
+// the block's n_split workgroups to arrive counts the block in on the
+// sequence's counter (at once, its result read later) and merges the block
+// into o_out and o, and the last block of the sequence to arrive then
+// advances cache_len[b].  Every workgroup of the grid arrives, those past the history
 // too, so cache_len[b] changes only once every workgroup of sequence b has
 // read it.  The counters live at the start of the workspace, start at zero
 // and are left at zero.
@@ -571,20 +603,12 @@ __global__ __launch_bounds__(256) void decode_short_kernel(DecodeParams p)
     const int64_t crow = ((int64_t)b * p.Hkv + g) * p.cap * D;
     const uint16_t* knew = (const uint16_t*)p.k_new + ((int64_t)b * p.Hkv + g) * D;
     const uint16_t* vnew = (const uint16_t*)p.v_new + ((int64_t)b * p.Hkv + g) * D;
-    if (s == 0 && hb == 0) {
-        // append the new base token's K/V at slot L (this launch takes key L
-        // from k_new / v_new, never from that slot)
-        for (int d = tid; d < D; d += 256) {
-            ((uint16_t*)p.k_cache)[crow + L * D + d] = knew[d];
-            ((uint16_t*)p.v_cache)[crow + L * D + d] = vnew[d];
-        }
-    }
     const int64_t lo = (int64_t)s * kDecodeShortChunk;
     const int64_t wlo = L - p.window + 1 > 0 ? L - p.window + 1 : 0;
-    const int64_t kind_stride = (int64_t)p.n_split * (D + 4);
-    const int64_t head_stride = 2 * kind_stride;
+    // record offsets in bytes (the head block's records span less than 4 GB)
+    const uint32_t kind_bytes = (uint32_t)p.n_split * ((D + 4) * 4), head_bytes = 2 * kind_bytes;
     // this head block's records, through a buffer resource (device-scope 16-byte accesses)
-    const rsrc_t prs = make_rsrc(p.ws_part + ((int64_t)b * p.Hq + h0) * head_stride, HG * head_stride * 4);
+    const rsrc_t prs = make_rsrc(p.ws_part + ((int64_t)b * p.Hq + h0) * (head_bytes / 4), (int64_t)HG * head_bytes);
     const bool any = lo <= L;                                    // the chunk holds keys of the history
     const bool win = any && lo + kDecodeShortChunk - 1 >= wlo;    // ... and of the base token's window
     if (any) {
@@ -641,6 +665,12 @@ __global__ __launch_bounds__(256) void decode_short_kernel(DecodeParams p)
             uint16_t* sl = slots + (r >> 5) * R::SLOT;
             uint16_t* dst = lane < CPR ? sl + R::kofs(r & 31, lane) : sl + R::KPART + R::vofs16(r & 31, lane - CPR);
             *(u32x4*)dst = nrow;
+            // the append: the new token's K/V row into cache slot L, once per
+            // KV head (this launch reads key L from k_new / v_new only)
+            if (hb == 0) {
+                uint16_t* cache = (uint16_t*)(lane < CPR ? p.k_cache : p.v_cache);
+                *(u32x4*)(cache + crow + L * D + 8 * (lane < CPR ? lane : lane - CPR)) = nrow;
+            }
         }
         // scale-offset queries in exp2 units as the B operand (zero columns past the live ones)
         bf16x8 qf[NQ];
@@ -761,8 +791,8 @@ __global__ __launch_bounds__(256) void decode_short_kernel(DecodeParams p)
                     q4[e] = x;
                 }
             }
-            const int64_t off = (r % HG) * head_stride + (r >= HG ? kind_stride : 0) + (int64_t)s * (D + 4) + 4 * qd;
-            rec_st(q4, prs, (uint32_t)(off * 4));
+            const uint32_t off = (r % HG) * head_bytes + (r >= HG ? kind_bytes : 0u) + (uint32_t)s * ((D + 4) * 4) + 16 * qd;
+            rec_st(q4, prs, off);
         }
     }
     // count in once this workgroup's records are written at device scope:
@@ -773,16 +803,24 @@ __global__ __launch_bounds__(256) void decode_short_kernel(DecodeParams p)
     wait_vmcnt<0>();
     __syncthreads();
     int* blk_cnt = p.ws_cnt + (int64_t)b * nblk + blockIdx.y;
-    if (tid == 0) last = atomicAdd(blk_cnt, 1) == p.n_split - 1;
+    int* seq_cnt = p.ws_cnt + (int64_t)p.B * nblk + b;
+    int ns = 0;
+    if (tid == 0) {
+        last = atomicAdd(blk_cnt, 1) == p.n_split - 1;
+        // the block's last arrival counts the block in on the sequence's
+        // counter at once; the count is read after the merge
+        if (last) ns = atomicAdd(seq_cnt, 1) + 1;
+    }
     __syncthreads();
     if (!last) return;
-    static_assert(256 * 12 * 4 <= 4 * PPW * R::SLOT * 2, "the merge's group states fit in the pair regions");
-    merge_block<D, HG>(prs, head_stride, kind_stride, (int)(wlo / kDecodeShortChunk), (int)(L / kDecodeShortChunk),
+    static_assert((8 * D + 4 * 130) * 4 <= 4 * PPW * R::SLOT * 2, "the merge's LDS fits in the pair regions");
+    merge_block<D, HG>(prs, head_bytes, kind_bytes, (int)(wlo / kDecodeShortChunk), (int)(L / kDecodeShortChunk),
                        (uint16_t*)p.o_out, (uint16_t*)p.o, ((int64_t)b * p.Hq + h0) * D, reinterpret_cast<float*>(lds));
     if (tid == 0) {
         __hip_atomic_store(blk_cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        int* seq_cnt = p.ws_cnt + (int64_t)p.B * nblk + b;
-        if (atomicAdd(seq_cnt, 1) == nblk - 1) {
+        if (ns == nblk) {
+            // every block's workgroups have arrived, so all have read L
+            // (cache_len[b] is not read by the merges)
             __hip_atomic_store(seq_cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             p.cache_len[b] = (int32_t)(L + 1);
         }

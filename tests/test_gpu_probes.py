@@ -353,14 +353,18 @@ def test_probe_decode_lds_copy_marked_run_edges():
                           (8, 2, 64, 300, 4095, None, False), (4, 2, 128, 128, 4095, None, False),
                           (16, 2, 128, 128, 4095, None, False), (4, 2, 128, 128, 9000, None, False),
                           (4, 2, 128, 128, 9000, 65535, True), (2, 2, 64, 128, 9000, 65535, True),
-                          (8, 2, 64, 128, 9000, None, True)],
+                          (8, 2, 64, 128, 9000, None, True), (4, 1, 128, 128, 4095, None, False),
+                          (4, 1, 64, 300, 4095, None, False), (2, 1, 128, 1, 4095, None, False),
+                          (1, 1, 128, 128, 4095, None, False)],
                          ids=["G4", "G4-w1", "G4-d64-w300", "G2", "G8", "G2-lane", "G2-lds", "MHA-d64-lds",
-                              "G4-d64-lds"])
+                              "G4-d64-lds", "G4-Hkv1", "G4-d64-w300-Hkv1", "G2-w1-Hkv1", "MHA-Hkv1"])
 def test_probe_decode_short_kernel(Hq, Hkv, d, w, longest, hint, lds):
     """Short histories: lengths 0, 1, around the window, and on the edges of
     128- and 256-key chunks; three steps.  Up to 4096 keys the step is one
     launch of the short-history kernel (128-key chunks, merged in the
-    launch); with a 9000-key history it is the LDS-streamed kernel for
+    launch; with one KV head, groups of 4, 2 and 1 give merges by one, two
+    and four waves per head); with a 9000-key history it is the
+    LDS-streamed kernel for
     groups of 4 (d = 64: 8 pairs per stage) and, for other groups, the
     lane-parallel kernel -- or the LDS-streamed one once max_len_hint + 1
     reaches 2^16 keys (2- and 1-head streams)."""
