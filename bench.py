@@ -413,7 +413,8 @@ def main():
         peak = FP32_PEAK_TFLOPS if es == 4 else BF16_PEAK_TFLOPS
         configs[name] = {"us_per_call": t * 1e6, "tokens_per_s": cB * cT / t, "dtype": "f32" if es == 4 else "bf16",
                          "kernels": "swa_f32_kernel + xattn_split_kernel + merge_kernel" if es == 4 else
-                                    "swa_bf16_kernel + xattn_split_kernel + merge_kernel",
+                                    "swa_ring_kernel<128, true, 1, 2> (the copy fused; one head a block, "
+                                    "the head dims split over the waves) + merge_kernel",
                          "bytes": nbytes, "flops": fl, **hbm_fracs(nbytes, fl, t, peak),
                          "note": f"{nbytes / 2**20:.0f} MiB per call: much of it can be served from the 256 MB "
                                  "last-level cache between back-to-back calls, so GB/s is an effective rate"}

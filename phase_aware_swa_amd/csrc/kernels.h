@@ -89,21 +89,22 @@ struct DecodeParams {
 __host__ __device__ inline int xattn_heads_per_wg(int G) { return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
 
 hipError_t launch_swa(const SwaParams& p, hipStream_t s);
-// Streaming sliding-window kernel: bf16, Hq/Hkv a multiple of 4, window <= kRingMaxWindow.
+// Streaming sliding-window kernel: bf16, window <= kRingMaxWindow, any group
+// (blocks of ring_heads_per_block(G) query heads per KV head: 4 for groups
+// that are multiples of 4, 2 for other even ones, else 1), with or without
+// the output copy's global query folded in.
 constexpr int kRingMaxWindow = 129;
-inline bool ring_applies(Dt dt, int Hq, int Hkv, int window)
-{
-    return dt == Dt::BF16 && (Hq / Hkv) % 4 == 0 && window <= kRingMaxWindow;
-}
+inline bool ring_applies(Dt dt, int, int, int window) { return dt == Dt::BF16 && window <= kRingMaxWindow; }
+inline int ring_heads_per_block(int G) { return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
 // Launch geometry of the streaming kernel: ceil(T / 32) tiles of 32 rows per
-// (sequence, KV head, 4-head block) stream, cut into n_seg segments of tps
+// (sequence, KV head, head block) stream, cut into n_seg segments of tps
 // tiles (about two workgroups per CU of the 256).
 struct RingGeom { int n_tiles, hblocks, n_seg, tps; };
 RingGeom ring_geometry(int B, int Hq, int Hkv, int64_t T);
 hipError_t launch_swa_ring(const SwaParams& p, hipStream_t s);
 // The streaming kernel with the output copy's global query fused in: each
-// workgroup attends the copy's query of its 4 heads to the pairs it brings
-// in and leaves one partial per segment (x.chunk = 32 tps keys, x.n_split =
+// workgroup attends the copy's query of its block's heads (a wave each) to
+// the pairs it brings in and leaves one partial per head and segment (x.chunk = 32 tps keys, x.n_split =
 // n_seg); the LSE merge follows.  x.k_cache / v_cache are not read.
 hipError_t launch_swa_ring_fused(const SwaParams& p, const XattnParams& x, hipStream_t s);
 hipError_t launch_xattn(const XattnParams& p, hipStream_t s);

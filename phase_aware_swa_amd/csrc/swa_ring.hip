@@ -1,14 +1,18 @@
 // swa_ring.hip -- streaming variant of the base-stream sliding-window
-// attention for bf16, GQA groups of >= 4 query heads and windows w <= 129
-// (the pages' w = 128).  Same result as swa_bf16_kernel in swa_prefill.hip
+// attention for bf16 and windows w <= 129 (the pages' w = 128), any group
+// size.  Same result as swa_bf16_kernel in swa_prefill.hip
 // ("Orthros:阶段感知异构注意力精读笔记" §2.3 Eq. (4), the fused cache
 // write of §2.1), organised for HBM streaming:
 //
 //   - a workgroup of 4 waves walks one segment of one KV head's sequence,
-//     32 rows at a time, for the 4 query heads it serves: wave (sub-tile s,
-//     head pair p) owns rows 16 s .. 16 s + 15 of both heads of the pair,
-//     so every K/V fragment it reads from LDS feeds two MFMAs, and two
-//     workgroups share a CU (2 waves per SIMD, up to 256 registers each);
+//     32 rows at a time, for the block of query heads it serves: wave
+//     (sub-tile s, column c) owns rows 16 s .. 16 s + 15 of its heads.  In
+//     blocks of 4 heads (groups that are multiples of 4) column c is a head
+//     pair, so every K/V fragment it reads from LDS feeds two MFMAs; in
+//     blocks of 2 (other even groups) it is one head; with one head (odd
+//     groups) the two columns split the head dims of O (each computes the
+//     scores of all of them).  Two workgroups share a CU (2 waves per SIMD,
+//     up to 256 registers each);
 //   - the window of a 32-row tile spans at most 5 blocks of 32 keys, kept in
 //     a 5-slot ring of K and V blocks in LDS (16 KB per slot at d = 128,
 //     XOR-swizzled instead of padded so that two workgroups fit in one CU's
@@ -55,7 +59,7 @@ struct GlobalArgs {
     int32_t* ws_len;      // [B]: the copy position, for the merge
 };
 
-template <int D, bool GQ>
+template <int D, bool GQ, int HPW, int DS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void swa_ring_kernel(
     SwaParams a, int n_tiles, int hblocks, int n_seg, int tps, int b0, GlobalArgs ga, PosBlock pos)
 {
@@ -65,13 +69,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int C16 = D / 8;                 // 16-byte chunks per row
     constexpr int NQ = D / 32;                 // MFMA k-steps over the head dim (32 each)
     constexpr int ND = D / 16;                 // 16-wide d tiles of O^T
+    constexpr int NDW = ND / DS;               // ... of one wave
+    constexpr int HB = DS == 1 ? 2 * HPW : HPW;   // query heads of the workgroup
+    static_assert((HPW == 2 && DS == 1) || (HPW == 1 && (DS == 1 || DS == 2)), "wave layout");
     constexpr int KCH = 32 * C16 / NT;         // K (and V) chunks per thread per pair
     static_assert(KCH >= 1, "head dim");
     __shared__ __align__(16) uint16_t ring[NS * R::SLOT];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hp = wv & 1, sub = wv >> 1;       // head pair, 16-row sub-tile
+    // 16-row sub-tile, and the wave's column of the block: its HPW heads
+    // (DS = 1), or its half of the head dims (DS = 2)
+    const int hp = wv & 1, sub = wv >> 1;
     const int n = lane & 15, gq = lane >> 4;
     int64_t id = blockIdx.x;
     const int seg = (int)(id % n_seg);
@@ -81,8 +90,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int g = (int)(id % a.Hkv);
     const int b = b0 + (int)(id / a.Hkv);
     const int G = a.Hq / a.Hkv;
-    const int hbase = g * G + hb * 4;
-    const int h0 = hbase + 2 * hp;              // the wave's heads: h0, h0 + 1
+    const int hbase = g * G + hb * HB;
+    const int h0 = hbase + (DS == 1 ? HPW * hp : 0);   // the wave's heads: h0 .. h0 + HPW - 1
+    const int dt0 = DS == 1 ? 0 : hp * NDW;             // its first 16-wide d tile of O^T
     const int64_t T = a.T;
     const int W = a.window;
     const int t_begin = seg * tps;
@@ -147,13 +157,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
     };
-    // raw Q rows of the wave's 16-row sub-tile for both heads:
+    // raw Q rows of the wave's 16-row sub-tile for its heads:
     // lane (n, gq) holds q[row][head][32 i + 8 gq + 0..7]
-    auto load_q = [&](int64_t r0, u32x4 (&qr)[2][NQ]) {
+    auto load_q = [&](int64_t r0, u32x4 (&qr)[HPW][NQ]) {
         const rsrc_t rq = make_rsrc((const uint16_t*)a.q + q_seq + r0 * a.Hq * D,
                                     (T - r0) * qrow_b - h0 * D * 2);
 #pragma unroll
-        for (int hd = 0; hd < 2; ++hd)
+        for (int hd = 0; hd < HPW; ++hd)
 #pragma unroll
             for (int i = 0; i < NQ; ++i)
                 qr[hd][i] = buf_load16(rq, (uint32_t)(n * qrow_b + hd * D * 2 + 64 * i + 16 * gq));
@@ -163,10 +173,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // v_dot2_f32_bf16 of (q_e masked to its half of the word) with the alpha
     // word, accumulated onto beta_e.  All alpha/beta loads go out together
     // (one L1/L2 round trip); the pair loop's registers are free by then.
-    auto scale_offset = [&](const u32x4 (&qr)[2][NQ], bf16x8 (&qf)[2][NQ]) {
-        u32x4 av[2][NQ], bv[2][NQ];
+    auto scale_offset = [&](const u32x4 (&qr)[HPW][NQ], bf16x8 (&qf)[HPW][NQ]) {
+        u32x4 av[HPW][NQ], bv[HPW][NQ];
 #pragma unroll
-        for (int hd = 0; hd < 2; ++hd)
+        for (int hd = 0; hd < HPW; ++hd)
 #pragma unroll
             for (int i = 0; i < NQ; ++i) {
                 const int d0 = hd * D + 32 * i + 8 * gq;
@@ -174,7 +184,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 bv[hd][i] = *(const u32x4*)(be + d0);
             }
 #pragma unroll
-        for (int hd = 0; hd < 2; ++hd)
+        for (int hd = 0; hd < HPW; ++hd)
 #pragma unroll
             for (int i = 0; i < NQ; ++i) {
                 u32x4 r;
@@ -194,8 +204,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     u32x4 kreg[KCH];
     u32x4 vreg[KCH];
-    u32x4 qraw[2][NQ];
-    bf16x8 qf[2][NQ];
+    u32x4 qraw[HPW][NQ];
+    bf16x8 qf[HPW][NQ];
     const bf16x8 kOnes = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
     // Causal mask of the diagonal pair (keys q0 .. q0 + 31 of a tile against
@@ -213,9 +223,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     }
 
-    // ---- the output copy's global query (Eq. (5)), fused: wave w serves
-    // head hbase + w over every key of the pairs this workgroup brings in
-    // (keys j <= P only).  Lanes (group kg, chunk kc): a group of LPK lanes
+    // ---- the output copy's global query (Eq. (5)), fused: wave w < HB
+    // serves head hbase + w over every key of the pairs this workgroup
+    // brings in (keys j <= P only); the other waves have no copy head.  Lanes (group kg, chunk kc): a group of LPK lanes
     // covers STEPS keys, each lane dotting its 16-byte K chunk with the
     // scaled query for every key of the group, in the order s ^ m with
     // m = kc / 2; a transposing DPP reduction then leaves lane (kg, kc)
@@ -234,7 +244,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int r = 0; r < RPL; ++r) gacc[r] = 0.f;
     int64_t P = -1;
-    if constexpr (GQ) {
+    const bool gwave = GQ && (HB == 4 || wv < HB);   // wave-uniform
+    if (gwave) {
         const int hg = hbase + wv;
         P = pos.v[b - b0];
         const int64_t o = (int64_t)hg * D + 8 * kc;
@@ -354,10 +365,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int64_t lo = q0 - W + 1 > 0 ? q0 - W + 1 : 0;
         const int r0 = 16 * sub;                    // wave's first row relative to q0
 
-        f32x4 oacc[2][ND];
-        f32x4 lacc[2];                              // row sums of the bf16 P, from an all-ones V^T tile
-        float m_run[2];                             // running maxima, in scaled (exp2) units
-        // One pair of 16-key blocks against both heads.  The diagonal pair
+        f32x4 oacc[HPW][NDW];
+        f32x4 lacc[HPW];                            // row sums of the bf16 P, from an all-ones V^T tile
+        float m_run[HPW];                           // running maxima, in scaled (exp2) units
+        // One pair of 16-key blocks against the wave's heads.  The diagonal pair
         // goes first: every row has its own key there, so its row maxima
         // start the running maxima, and its MFMAs start the accumulators
         // from zero (no clearing, no rescale).
@@ -369,14 +380,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             int ko1 = (int)(pr % NS) * R::SLOT + R::kofs(n, 4 + gq);
             asm volatile("" : "+v"(ko0), "+v"(ko1));
             const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
-            f32x4 s[2][2];
+            f32x4 s[HPW][2];
 #pragma unroll
             for (int i = 0; i < NQ; ++i) {
                 const uint16_t* kb = ring + ((i & 1) ? ko1 : ko0) + (i >> 1) * R::K_STEP2;
                 const bf16x8 k0 = *(const bf16x8*)kb;
                 const bf16x8 k1 = *(const bf16x8*)(kb + R::K_KEY16);
 #pragma unroll
-                for (int hd = 0; hd < 2; ++hd) {
+                for (int hd = 0; hd < HPW; ++hd) {
                     const f32x4 c0 = i ? s[hd][0] : (FIRST ? dbias[0] : zero);
                     const f32x4 c1 = i ? s[hd][1] : (FIRST ? dbias[1] : zero);
                     s[hd][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[hd][i], c0, 0, 0, 0);
@@ -396,16 +407,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     for (int r = 0; r < 4; ++r) {
                         const bool m0 = (uint32_t)(r - c) > wm1, m1 = (uint32_t)(16 + r - c) > wm1;
 #pragma unroll
-                        for (int hd = 0; hd < 2; ++hd) {
+                        for (int hd = 0; hd < HPW; ++hd) {
                             if (m0) s[hd][0][r] = -INFINITY;
                             if (m1) s[hd][1][r] = -INFINITY;
                         }
                     }
                 }
             }
-            bf16x8 pb[2];
+            bf16x8 pb[HPW];
 #pragma unroll
-            for (int hd = 0; hd < 2; ++hd) {
+            for (int hd = 0; hd < HPW; ++hd) {
                 const f32x4 s0 = s[hd][0], s1 = s[hd][1];
                 float lmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
                                    fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
@@ -421,7 +432,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     m_run[hd] = m_new;
                     lacc[hd] *= corr;
 #pragma unroll
-                    for (int i = 0; i < ND; ++i) oacc[hd][i] *= corr;
+                    for (int i = 0; i < NDW; ++i) oacc[hd][i] *= corr;
                 }
                 float p[8];
 #pragma unroll
@@ -435,18 +446,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 lacc[hd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pb[hd], FIRST ? zero : lacc[hd], 0, 0, 0);
             }
             // V^T operands by transposing reads: this lane addresses key row
-            // 4 gq + (n >> 2) of each block, dims 16 dt + 4 (n & 3).  One
-            // base per pair (opaque, so that the steps stay immediate offsets).
-            int vo = (int)(pr % NS) * R::SLOT + R::KPART + R::vofs_tr(4 * gq + (n >> 2), 0, n & 3);
+            // 4 gq + (n >> 2) of each block, dims 16 (dt0 + dt) + 4 (n & 3).
+            // One base per pair (opaque, so that the steps stay immediate
+            // offsets).
+            int vo = (int)(pr % NS) * R::SLOT + R::KPART + R::vofs_tr(4 * gq + (n >> 2), dt0, n & 3);
             asm volatile("" : "+v"(vo));
             const uint16_t* vb = ring + vo;
 #pragma unroll
-            for (int dt = 0; dt < ND; ++dt) {
+            for (int dt = 0; dt < NDW; ++dt) {
                 const u32x2 w0 = __builtin_bit_cast(u32x2, lds_read_tr(vb + dt * R::V_DT));
                 const u32x2 w1 = __builtin_bit_cast(u32x2, lds_read_tr(vb + R::V_KEY16 + dt * R::V_DT));
                 const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
 #pragma unroll
-                for (int hd = 0; hd < 2; ++hd)
+                for (int hd = 0; hd < HPW; ++hd)
                     oacc[hd][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[hd], FIRST ? zero : oacc[hd][dt],
                                                                            0, 0, 0);
             }
@@ -460,7 +472,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // the copy's step on this tile's own pair (LDS and ALU only) runs
         // while the next tile's Q rows may still be arriving
         if constexpr (GQ) {
-            if (q0 <= P) global_pair(q0 >> 5);
+            if (gwave && q0 <= P) global_pair(q0 >> 5);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (has_next) scale_offset(qraw, qf);
@@ -475,10 +487,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // leaves it 8 consecutive dims (32 m + 8 ((gq & 1) * 2 + (gq >> 1))),
             // so the stores are 16 bytes a lane and 64 contiguous bytes a row
 #pragma unroll
-            for (int hd = 0; hd < 2; ++hd) {
+            for (int hd = 0; hd < HPW; ++hd) {
                 const float inv = __builtin_amdgcn_rcpf(lacc[hd][0]);
 #pragma unroll
-                for (int m = 0; m < ND / 2; ++m) {
+                for (int m = 0; m < NDW / 2; ++m) {
                     const f32x4 oa = oacc[hd][2 * m], ob = oacc[hd][2 * m + 1];
                     u32x4 w;
 #pragma unroll
@@ -489,8 +501,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         w[i] = r[0];
                         w[2 + i] = r[1];
                     }
-                    buf_store16(w, ro,
-                                (uint32_t)(n * qrow_b + hd * D * 2 + 2 * (32 * m + 8 * ((gq & 1) * 2 + (gq >> 1)))));
+                    buf_store16(w, ro, (uint32_t)(n * qrow_b + hd * D * 2 +
+                                                  2 * (16 * dt0 + 32 * m + 8 * ((gq & 1) * 2 + (gq >> 1)))));
                 }
             }
         }
@@ -498,7 +510,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (has_next) store_pair((q0 >> 5) + 1, true, kreg, vreg);
         __syncthreads();
     }
-    if constexpr (GQ) {
+    if (gwave) {
         float* part = ga.ws_part + (((int64_t)b * a.Hq + hbase + wv) * n_seg + seg) * (D + 2);
 #pragma unroll
         for (int r = 0; r < RPL; ++r) part[2 + lane + 64 * r] = gacc[r];
@@ -512,6 +524,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             part[0] = gm;
             part[1] = 0.5f * lsum;
         }
+    }
+    if constexpr (GQ) {
         if (seg == 0 && g == 0 && hb == 0 && tid == 0) ga.ws_len[b] = (int32_t)P;
     }
 }
@@ -521,7 +535,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 RingGeom ring_geometry(int B, int Hq, int Hkv, int64_t T)
 {
     RingGeom r;
-    r.hblocks = (Hq / Hkv) / 4;
+    r.hblocks = (Hq / Hkv) / ring_heads_per_block(Hq / Hkv);
     r.n_tiles = (int)((T + 31) / 32);
     const int64_t streams = (int64_t)B * Hkv * r.hblocks;
     constexpr int64_t kTargetWgs = 512;
@@ -535,6 +549,24 @@ RingGeom ring_geometry(int B, int Hq, int Hkv, int64_t T)
 
 namespace {
 
+template <int D, bool GQ>
+void launch_ring_d(dim3 grid, const SwaParams& p, const RingGeom& r, int b0, const GlobalArgs& ga,
+                   const PosBlock& pos, hipStream_t s)
+{
+    // groups of 4k: two heads a wave; of 2: one head a wave; odd: the two
+    // waves of a sub-tile split the head dims
+    const int hpb = ring_heads_per_block(p.Hq / p.Hkv);
+    if (hpb == 4)
+        hipLaunchKernelGGL((swa_ring_kernel<D, GQ, 2, 1>), grid, dim3(256), 0, s, p, r.n_tiles, r.hblocks, r.n_seg,
+                           r.tps, b0, ga, pos);
+    else if (hpb == 2)
+        hipLaunchKernelGGL((swa_ring_kernel<D, GQ, 1, 1>), grid, dim3(256), 0, s, p, r.n_tiles, r.hblocks,
+                           r.n_seg, r.tps, b0, ga, pos);
+    else
+        hipLaunchKernelGGL((swa_ring_kernel<D, GQ, 1, 2>), grid, dim3(256), 0, s, p, r.n_tiles, r.hblocks,
+                           r.n_seg, r.tps, b0, ga, pos);
+}
+
 template <bool GQ>
 hipError_t launch_ring(const SwaParams& p, const GlobalArgs& ga, const int64_t* pos_host, hipStream_t s)
 {
@@ -546,11 +578,9 @@ hipError_t launch_ring(const SwaParams& p, const GlobalArgs& ga, const int64_t* 
         for (int i = 0; i < kPosPerLaunch; ++i) pos.v[i] = (GQ && i < nb) ? pos_host[b0 + i] : 0;
         const int64_t n_wg = (int64_t)nb * p.Hkv * r.hblocks * r.n_seg;
         if (p.D == 64)
-            hipLaunchKernelGGL((swa_ring_kernel<64, GQ>), dim3((unsigned)n_wg), dim3(256), 0, s, p, r.n_tiles,
-                               r.hblocks, r.n_seg, r.tps, b0, ga, pos);
+            launch_ring_d<64, GQ>(dim3((unsigned)n_wg), p, r, b0, ga, pos, s);
         else
-            hipLaunchKernelGGL((swa_ring_kernel<128, GQ>), dim3((unsigned)n_wg), dim3(256), 0, s, p, r.n_tiles,
-                               r.hblocks, r.n_seg, r.tps, b0, ga, pos);
+            launch_ring_d<128, GQ>(dim3((unsigned)n_wg), p, r, b0, ga, pos, s);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -560,7 +590,7 @@ hipError_t launch_ring(const SwaParams& p, const GlobalArgs& ga, const int64_t* 
 }  // namespace
 
 // Workgroups of the streaming kernel: about two per CU of the 256, each
-// walking an equal share of one (sequence, KV head, 4-head block) stream.
+// walking an equal share of one (sequence, KV head, head block) stream.
 hipError_t launch_swa_ring(const SwaParams& p, hipStream_t s)
 {
     return launch_ring<false>(p, GlobalArgs{}, nullptr, s);

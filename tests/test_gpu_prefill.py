@@ -57,6 +57,14 @@ CASES = [
     (1, 4, 1, 128, 64, 4100),
     (1, 8, 1, 128, 100, 2000),
     (1, 4, 1, 128, 128, 40000),
+    # other groups with w <= 129 (the streaming kernel: blocks of 2 or 1 heads)
+    (2, 8, 8, 128, 128, 3000),
+    (1, 4, 2, 64, 128, 1000),
+    (1, 12, 2, 128, 128, 700),
+    (2, 3, 3, 64, 129, 333),
+    # groups of 1 and 3 past w = 129 (the generic kernel)
+    (1, 4, 4, 128, 200, 700),
+    (2, 6, 2, 128, 130, 500),
 ]
 
 
@@ -176,15 +184,17 @@ def test_base_stream_isolated_from_output_stream():
     assert not torch.equal(bits(run.o_out), bits(oo))
 
 
-@pytest.mark.parametrize("G", [4, 2], ids=["fused", "separate"])
-def test_stages_match_one_call(G):
+@pytest.mark.parametrize("G,w", [(4, 128), (2, 128), (1, 128), (2, 200)],
+                         ids=["fused-G4", "fused-G2", "fused-G1", "separate-G2-w200"])
+def test_stages_match_one_call(G, w):
     """orthros_swa_prefill then orthros_global_xattn against orthros_prefill.
-    o and the caches are bit-identical.  With G = 4 the one call takes the
+    o and the caches are bit-identical.  With w <= 129 the one call takes the
     fused path (the copy's query rides on the streaming SWA kernel, other
-    key splits), so o_out of both is checked against the oracle; with G = 2
-    the one call runs the same two kernels and o_out is bit-identical."""
-    cfg = make_cfg(2, 2 * G, 2, 128, 128, torch.bfloat16)
-    say("stages vs one call, G =", G)
+    key splits), so o_out of both is checked against the oracle; with
+    w = 200 the one call runs the same two kernels and o_out is
+    bit-identical."""
+    cfg = make_cfg(2, 2 * G, 2, 128, w, torch.bfloat16)
+    say("stages vs one call, G =", G, "w =", w)
     xc = inputs.prefill_inputs(T=1234, seed=15, **cfg)
     xc["out_pos"] = [1233, 600]
     x = to_dev(xc)
@@ -196,10 +206,10 @@ def test_stages_match_one_call(G):
     torch.cuda.synchronize()
     assert torch.equal(bits(a.o), bits(b.o))
     assert torch.equal(bits(a.k_cache), bits(b.k_cache)) and torch.equal(bits(a.v_cache), bits(b.v_cache))
-    if G == 2:
+    if w > 129:
         assert torch.equal(bits(a.o_out), bits(b.o_out))
     else:
-        ref = oracle_prefill(xc, 128)
+        ref = oracle_prefill(xc, w)
         assert_parity(a.o_out, ref["o_out"], torch.bfloat16, "o_out (one call)")
         assert_parity(b.o_out, ref["o_out"], torch.bfloat16, "o_out (stages)")
 

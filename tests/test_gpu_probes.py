@@ -12,8 +12,11 @@ of its row, compared bit for bit (tests/probe_util.py).  Kernels covered:
 
   prefill, fused streaming kernel (groups of 4 and 8 query heads, w <= 129,
     d 128 and 64), copies on segment edges and below T-1;
+  prefill, the fused streaming kernel for groups of 1, 2, 3 and 6
+    (w <= 129: blocks of 2 heads, or of 1 with the head dims split);
   prefill, generic sliding-window kernel + LDS-streamed cross-attention
-    (w > 129), and orthros_global_xattn on its own;
+    (w > 129, groups of 4; and groups of 2 and 1), and
+    orthros_global_xattn on its own;
   decode, LDS-streamed kernel (32 sequences; each workgroup takes an equal
     run of the step's keys, in (sequence, KV head, key) order): the base
     token's window straddling run boundaries at w = 128 and spanning several
@@ -177,12 +180,26 @@ def test_probe_stages_lds_xattn():
     prefill_probe(4, 32, 8, 128, 128, 4096, [4095, 2048, 2047, 5], seed=312, stages=True)
 
 
-# Groups of 2 (the generic kernels), for completeness of the fallbacks.
-def test_probe_generic_g2():
-    prefill_probe(2, 4, 2, 128, 128, 1500, [1499, 999], seed=313)
+# The fused streaming kernel for other groups: groups of 2 (a head a wave),
+# 1 and 3 (the waves of a sub-tile split the head dims), 6 (three 2-head
+# blocks per KV head); the copy's query on the first waves of the block.
+@pytest.mark.parametrize("B,Hq,Hkv,d,w,T,pos", [(2, 4, 2, 128, 128, 1500, [1499, 999]),
+                                                (2, 4, 4, 128, 128, 1500, [1499, 31]),
+                                                (2, 2, 2, 64, 129, 1100, [1099, 640]),
+                                                (2, 6, 2, 128, 100, 1000, [999, 128]),
+                                                (1, 12, 2, 128, 128, 700, [699])],
+                         ids=["G2", "G1", "G1-d64-w129", "G3-w100", "G6"])
+def test_probe_streaming_other_groups(B, Hq, Hkv, d, w, T, pos):
+    prefill_probe(B, Hq, Hkv, d, w, T, pos, seed=313 + Hq + d + w)
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (8, 2), (16, 2)], ids=["G2", "G4", "G8"])
+# Groups of 2 and 1 on the generic kernels (w > 129).
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (4, 4)], ids=["G2", "G1"])
+def test_probe_generic_g2_g1(Hq, Hkv):
+    prefill_probe(2, Hq, Hkv, 128, 200, 1500, [1499, 999], seed=330 + Hq + Hkv)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (8, 2), (16, 2), (4, 4), (6, 2)], ids=["G2", "G4", "G8", "G1", "G3"])
 def test_window_one_and_first_position_exact(Hq, Hkv):
     """Random inputs.  w = 1: o = v exactly (one key, weight 1).  A copy at
     position 0 and base row 0 (w = 128) see key 0 alone: exactly v_0."""
