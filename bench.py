@@ -613,7 +613,7 @@ def main():
         result["roofline"] = {"bound": "hbm", "achieved": s["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": s["GBps"] / HBM_PEAK_GBS,
                               "traffic": measured_traffic("traffic_prefill_fused_gqa_8b_128k.md"),
-                              "kernel": "orthros_prefill: swa_ring_kernel<128, true> (+ merge_kernel)",
+                              "kernel": "orthros_prefill: swa_ring_kernel<128, true, 2, 1> (+ merge_kernel)",
                               "algorithmic_bytes": s["bytes"],
                               "two_pass_bytes": two_pass,
                               "achieved_two_pass_bytes": two_pass / (s["us"] * 1e-6) / 1e9,
@@ -631,7 +631,7 @@ def main():
         result["roofline_swa"] = {"bound": "hbm", "achieved": s["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": s["GBps"] / HBM_PEAK_GBS,
                                   "traffic": measured_traffic("traffic_swa_prefill_gqa_8b_128k.md"),
-                                  "kernel": "orthros_swa_prefill: swa_ring_kernel<128, false>"}
+                                  "kernel": "orthros_swa_prefill: swa_ring_kernel<128, false, 2, 1>"}
     if "xattn" in out:
         x = out["xattn"]
         result["roofline_xattn"] = {"bound": "hbm", "achieved": x["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
