@@ -644,8 +644,8 @@ def main():
         result["roofline_decode"] = {"bound": "hbm", "achieved": dd["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                      "frac": dd["GBps"] / HBM_PEAK_GBS,
                                      "traffic": measured_traffic("traffic_decode_gqa_8b_b16.md"),
-                                     "kernel": "orthros_decode_step: decode_append_kernel + "
-                                               "xattn_lds_kernel<128, DecodeParams> + lds_merge_kernel (per step)"}
+                                     "kernel": "orthros_decode_step: "
+                                               "xattn_lds_kernel<128, DecodeParams> + lds_decode_merge_kernel (per step)"}
     if args.only == "all" and "ceilings" not in args.skip:
         progress("practical HBM ceilings")
         result["hbm_practical"] = practical_ceilings()

@@ -268,11 +268,14 @@ __device__ __forceinline__ void attend_chunk(const float (*qs)[D], const E* kc, 
 // kind) at pk (record s at pk + s * stride floats: max, sum, ..., weighted
 // values at aoff) into out[row .. row + D):
 //   o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
+// With xv set, one more key takes part: score xm (exp2 units), weight 1,
+// values the bf16 row xv (a decode step's new token, which no record holds).
 // 256 threads.  Thread t owns head-dim values 4 (t % (D/4)) .. +3 of split
 // group t / (D/4); the split groups are then added in a fixed order, so the
 // result is run-to-run identical.  Ends with a barrier (LDS reusable).
 template <typename E, int D>
-__device__ void merge_splits(const float* pk, int64_t stride, int aoff, int s0, int s1, E* out, int64_t row)
+__device__ void merge_splits(const float* pk, int64_t stride, int aoff, int s0, int s1, E* out, int64_t row,
+                             float xm = 0.f, const uint16_t* xv = nullptr)
 {
     constexpr int TPR = D / 4;            // threads per head-dim row
     constexpr int NG = 256 / TPR;         // split groups
@@ -287,7 +290,8 @@ __device__ void merge_splits(const float* pk, int64_t stride, int aoff, int s0, 
     for (int x = 32; x > 0; x >>= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
     if (lane == 0) wmax[wv] = mx;
     __syncthreads();
-    const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float M0 = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float M = xv ? fmaxf(M0, xm) : M0;
     // this thread's split group: weighted sums of 4 head-dim values and of
     // l, eight splits per round with every load of the round issued first
     // (one L2 round trip per round, not per split); a round's splits past
@@ -315,6 +319,16 @@ __device__ void merge_splits(const float* pk, int64_t stride, int aoff, int s0, 
             n2 += f * c[k].x;
             n3 += f * c[k].y;
         }
+    }
+    if (xv && gp == 0) {
+        // the extra key, in split group 0
+        const float f = fast_exp2(xm - M);
+        const u32x2 w = *(const u32x2*)(xv + 4 * d4);
+        den += f;
+        n0 += f * bf16_lo(w[0]);
+        n1 += f * bf16_hi(w[0]);
+        n2 += f * bf16_lo(w[1]);
+        n3 += f * bf16_hi(w[1]);
     }
     red[gp][4 * d4] = n0;
     red[gp][4 * d4 + 1] = n1;
@@ -893,35 +907,101 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* ws_part, const 
     if (cache_len && h == 0 && tid == 0) cache_len[b] = (int32_t)(L + 1);
 }
 
-// The LDS-streamed kernel's records: one workgroup per (sequence, query
-// head) merges the record ids its stream's range lists (ws_rng: first, first
-// holding keys of the base token's window, last) -- records [id][kinds][4
-// head slots, the block's hg used][rec].  kinds = 2 (decode) also advances
-// cache_len.
-template <typename E, int D>
+// The LDS-streamed kernel's records in prefill: one workgroup per
+// (sequence, query head) merges the record ids its stream's range lists
+// (ws_rng: first, -, last) -- records [id][1][4 head slots, the block's hg
+// used][rec] -- into o_out.
+template <int D>
 __global__ __launch_bounds__(256) void lds_merge_kernel(const float* ws_part, const int32_t* ws_rng,
-                                                        const int32_t* ws_len, int32_t* cache_len, int64_t max_len,
-                                                        int Hq, int G, int rec, int kinds, E* o_out, E* o)
+                                                        const int32_t* ws_len, int64_t max_len, int Hq, int G,
+                                                        int rec, uint16_t* o_out)
 {
     const int tid = threadIdx.x;
     const int b = blockIdx.x / Hq, h = blockIdx.x % Hq;
     const int64_t L = ws_len[b];
     const int64_t row = ((int64_t)b * Hq + h) * D;
     if (L < 0 || L > max_len) {
-        for (int d = tid; d < D; d += 256) {
-            st_elem(o_out, row + d, __builtin_nanf(""));
-            if (kinds == 2) st_elem(o, row + d, __builtin_nanf(""));
-        }
+        for (int d = tid; d < D; d += 256) st_elem(o_out, row + d, __builtin_nanf(""));
         return;
     }
     const int hg = xattn_heads_per_wg(G), hblocks = G / hg, S = (Hq / G) * hblocks;
     const int j = (h / G) * hblocks + (h % G) / hg;         // the head's stream: KV head, head block
     const int32_t* rg = ws_rng + ((int64_t)b * S + j) * 3;
-    const int64_t stride = (int64_t)kinds * 4 * rec;
-    for (int kind = 0; kind < kinds; ++kind)
-        merge_splits<E, D>(ws_part + ((int64_t)kind * 4 + (h % G) % hg) * rec, stride, rec - D,
-                           kind == 0 ? rg[0] : rg[1], rg[2], kind == 0 ? o_out : o, row);
-    if (cache_len && h == 0 && tid == 0) cache_len[b] = (int32_t)(L + 1);
+    merge_splits<uint16_t, D>(ws_part + (h % G) % hg * rec, (int64_t)4 * rec, rec - D, rg[0], rg[2], o_out, row);
+}
+
+// The decode step's merge after the LDS-streamed kernel, which read the
+// history 0 .. L - 1: one workgroup per (sequence, query head) merges its
+// stream's records of both kinds (the copy's over the whole history, the
+// base token's over the segments holding its window) together with the new
+// token's key L from k_new / v_new -- its score from the same bf16
+// scale-offset query the streaming kernel used -- into o_out and o.  The
+// workgroup of head 0 then appends the new token's K/V rows at slot L of
+// every KV head of the sequence (nothing reads the cache after the
+// streaming kernel) and advances cache_len[b].  A length outside
+// [0, max_len] gives NaN outputs and touches nothing.
+template <int D>
+__global__ __launch_bounds__(256) void lds_decode_merge_kernel(DecodeParams p)
+{
+    __shared__ float wsum[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int b = blockIdx.x / p.Hq, h = blockIdx.x % p.Hq;
+    const int64_t L = p.ws_len[b];
+    const int64_t row = ((int64_t)b * p.Hq + h) * D;
+    uint16_t* o_out = (uint16_t*)p.o_out;
+    uint16_t* o = (uint16_t*)p.o;
+    if (L < 0 || L > p.max_len) {
+        for (int d = tid; d < D; d += 256) {
+            st_elem(o_out, row + d, __builtin_nanf(""));
+            st_elem(o, row + d, __builtin_nanf(""));
+        }
+        return;
+    }
+    const int G = p.Hq / p.Hkv, hg = xattn_heads_per_wg(G), hblocks = G / hg, S = p.Hkv * hblocks;
+    const int g = h / G, j = g * hblocks + (h % G) / hg;     // the head's KV head and stream
+    const uint16_t* knew = (const uint16_t*)p.k_new + ((int64_t)b * p.Hkv + g) * D;
+    const uint16_t* vnew = (const uint16_t*)p.v_new + ((int64_t)b * p.Hkv + g) * D;
+    // the new key's score per kind (thread kind * D + d takes dim d; kind 0
+    // the copy's query, kind 1 the base token's), in exp2 units
+    float part = 0.f;
+    if (tid < 2 * D) {
+        const int kind = tid / D, d = tid % D;
+        const uint16_t* q = (const uint16_t*)(kind ? p.q : p.q_out) + row + d;
+        const uint16_t* al = (const uint16_t*)(kind ? p.alpha : p.alpha_out) + (int64_t)h * D + d;
+        const uint16_t* be = (const uint16_t*)(kind ? p.beta : p.beta_out) + (int64_t)h * D + d;
+        const float qh = bf16_lo(pack_bf16x2(__builtin_fmaf(bf16_lo(*q), bf16_lo(*al), bf16_lo(*be)) * p.qscale, 0.f));
+        part = qh * bf16_lo(knew[d]);
+    }
+    part = wave_sum(part);
+    if (lane == 0) wsum[wv] = part;
+    __syncthreads();
+    constexpr int WPK = D / 64;                              // waves per kind
+    float sk[2];
+#pragma unroll
+    for (int kind = 0; kind < 2; ++kind) {
+        sk[kind] = wsum[kind * WPK];
+#pragma unroll
+        for (int w = 1; w < WPK; ++w) sk[kind] += wsum[kind * WPK + w];
+    }
+    const int32_t* rg = p.ws_rng + ((int64_t)b * S + j) * 3;
+    const int64_t stride = (int64_t)2 * 4 * p.rec;
+#pragma unroll
+    for (int kind = 0; kind < 2; ++kind)
+        merge_splits<uint16_t, D>(p.ws_part + ((int64_t)kind * 4 + (h % G) % hg) * p.rec, stride, p.rec - D,
+                                  kind == 0 ? rg[0] : rg[1], rg[2], kind == 0 ? o_out : o, row, sk[kind], vnew);
+    if (h == 0) {
+        constexpr int UPR = D / 8;                           // 16-byte units per row
+        const int units = p.Hkv * UPR;
+        for (int u = tid; u < 2 * units; u += 256) {
+            const bool isv = u >= units;
+            const int uu = isv ? u - units : u;
+            const int gg = uu / UPR, c = uu - gg * UPR;
+            const int64_t kv = (int64_t)b * p.Hkv + gg;
+            const u32x4 w = *((const u32x4*)((const uint16_t*)(isv ? p.v_new : p.k_new) + kv * D) + c);
+            *((u32x4*)((uint16_t*)(isv ? p.v_cache : p.k_cache) + (kv * p.cap + L) * D) + c) = w;
+        }
+        if (tid == 0) p.cache_len[b] = (int32_t)(L + 1);
+    }
 }
 
 template <typename E, int D, int HG>
@@ -1029,25 +1109,20 @@ hipError_t launch_lds_merge(const XattnParams& p, hipStream_t st)
 {
     int64_t max_len = 0;
     for (int b = 0; b < p.B; ++b) max_len = p.pos[b] > max_len ? p.pos[b] : max_len;
-    auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part, p.ws_rng, p.ws_len,
-                           (int32_t*)nullptr, max_len, p.Hq, p.Hq / p.Hkv, p.rec, 1, (uint16_t*)p.o_out,
-                           (uint16_t*)nullptr);
-    };
-    if (p.D == 64) go(lds_merge_kernel<uint16_t, 64>);
-    else go(lds_merge_kernel<uint16_t, 128>);
+    if (p.D == 64)
+        hipLaunchKernelGGL((lds_merge_kernel<64>), dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part, p.ws_rng, p.ws_len,
+                           max_len, p.Hq, p.Hq / p.Hkv, p.rec, (uint16_t*)p.o_out);
+    else
+        hipLaunchKernelGGL((lds_merge_kernel<128>), dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part, p.ws_rng, p.ws_len,
+                           max_len, p.Hq, p.Hq / p.Hkv, p.rec, (uint16_t*)p.o_out);
     return hipGetLastError();
 }
 
 hipError_t launch_lds_merge(const DecodeParams& p, hipStream_t st)
 {
     if (p.dt != Dt::BF16 || (p.D != 64 && p.D != 128)) return hipErrorInvalidValue;
-    auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3(p.B * p.Hq), dim3(256), 0, st, p.ws_part, p.ws_rng, p.ws_len, p.cache_len,
-                           p.max_len, p.Hq, p.Hq / p.Hkv, p.rec, 2, (uint16_t*)p.o_out, (uint16_t*)p.o);
-    };
-    if (p.D == 64) go(lds_merge_kernel<uint16_t, 64>);
-    else go(lds_merge_kernel<uint16_t, 128>);
+    if (p.D == 64) hipLaunchKernelGGL((lds_decode_merge_kernel<64>), dim3(p.B * p.Hq), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((lds_decode_merge_kernel<128>), dim3(p.B * p.Hq), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

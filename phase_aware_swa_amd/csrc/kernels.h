@@ -147,21 +147,23 @@ inline int64_t xattn_lds_records(int B, int streams)
 }
 hipError_t launch_xattn_lds(const XattnParams& p, hipStream_t s);
 // LSE merge of the LDS-streamed kernel's records (the ranges in ws_rng)
-// into o_out (and in decode o, then cache_len[b] += 1).
+// into o_out; in decode into o_out and o with the new token's key L added,
+// then that key appended at slot L and cache_len[b] += 1.
 hipError_t launch_lds_merge(const XattnParams& p, hipStream_t s);
 hipError_t launch_lds_merge(const DecodeParams& p, hipStream_t s);
 // The decode step: for bf16 steps of at most kDecodeShortMaxSplits chunks
 // of kDecodeShortChunk keys, on the one-launch short-history kernel (fused =
-// 1); longer bf16 ones on the LDS-streamed kernel (append, stream, merge)
-// when the rule above takes it; the rest (fp32 among them) on the
+// 1); longer bf16 ones on the LDS-streamed kernel (stream, then the merge
+// that adds the new key and appends it) when the rule above takes it; the rest (fp32 among them) on the
 // lane-parallel split kernel and a merge kernel.
 constexpr int kDecodeShortChunk = 128;
 constexpr int kDecodeShortMaxSplits = 32;
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 // The decode step on the LDS-streamed kernel (bf16, more keys than the
-// one-launch short-history kernel takes): append, the copy and the base
-// token in one streaming pass, then the LSE merge of both kinds (which
-// advances cache_len).
+// one-launch short-history kernel takes): the copy and the base token over
+// the history 0 .. L - 1 in one streaming pass, then the LSE merge of both
+// kinds with the new token's key L from k_new / v_new, which also appends
+// that key at slot L and advances cache_len.
 hipError_t launch_decode_lds(const DecodeParams& p, hipStream_t s);
 // LSE merge of decode partials [B][Hq][2][n_split][rec] into o_out and o,
 // then cache_len[b] += 1 for every valid sequence.

@@ -88,9 +88,9 @@ __device__ __forceinline__ int64_t run_keys(int64_t total, int nwg)
 
 // One segment: keys lo .. hi (len keys) of stream j = (KV head g, the block
 // of query heads from h0) of sequence b, hi <= P (the copy's position), nst
-// stages, its partial records under record id `id`.  In decode, P is the cache length L
-// and `win` marks a segment that holds keys of the base token's window
-// [wlo, L].  Key indices fit 32 bits (positions are below 2^31); cache
+// stages, its partial records under record id `id`.  In decode the keys are
+// the history 0 .. L - 1 (L = cache_len[b]), and `win` marks a segment that
+// holds keys of the base token's window [wlo, L - 1].  Key indices fit 32 bits (positions are below 2^31); cache
 // offsets and positions in the launch's key order take 64.
 struct Item {
     int b, g, h0, id, nst, len;
@@ -99,11 +99,12 @@ struct Item {
 };
 
 // PT = XattnParams: prefill, the copy's positions by value in `pos`.
-// PT = DecodeParams: a decode step, L = cache_len[b] read on the device (the
-// new token's K/V are already in slot L), and the base token's heads ride
-// along as query columns 4 .. 3 + hg of the same MFMAs (their keys are a
-// subset of the copy's), leaving a second partial per head for the segments
-// that hold its window.  Record ids of this launch start at rbase.
+// PT = DecodeParams: a decode step, L = cache_len[b] read on the device; the
+// kernel reads the history 0 .. L - 1 (key L, the new token's, is added by
+// the merge from k_new / v_new), and the base token's heads ride along as
+// query columns 4 .. 3 + hg of the same MFMAs (their keys are a subset of
+// the copy's), leaving a second partial per head for the segments that hold
+// its window.  Record ids of this launch start at rbase.
 template <int D, typename PT>
 __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, int rbase, int hg, int hblocks,
                                                         PosBlock pos)
@@ -163,7 +164,11 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
     // (t = sequence * S + stream, counted in the launch) in run w has record
     // id rbase + t + w: those of one stream are consecutive, and no two
     // segments share one.
-    const int64_t cnt = Lv >= 0 ? (int64_t)(Lv + 1) * S : 0;   // keys of sequence b0 + lane
+    // keys per stream: the copy's 0 .. P in prefill; in decode the history
+    // 0 .. L - 1 (the new token's key L comes from k_new / v_new in the
+    // merge, which also appends it to the cache)
+    constexpr int KX = DEC ? 0 : 1;
+    const int64_t cnt = Lv >= 0 ? (int64_t)(Lv + KX) * S : 0;   // keys of sequence b0 + lane
     int64_t incl = cnt;                   // inclusive prefix sum over the lanes
 #pragma unroll
     for (int x = 1; x < 64; x <<= 1) {
@@ -183,17 +188,19 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
             const int64_t ex = __shfl(excl, bl);
             if (t < nb * S) {
                 int32_t* rg = a.ws_rng + ((int64_t)b0 * S + t) * 3;
-                if (L < 0) {
+                const int nk = L + KX;            // the stream's keys
+                if (L < 0 || nk == 0) {
                     rg[0] = 0;
                     rg[1] = 0;
                     rg[2] = -1;
                 } else {
-                    const int64_t P = ex + (int64_t)(t - bl * S) * (L + 1);
+                    const int64_t P = ex + (int64_t)(t - bl * S) * nk;
                     int wlo = 0;
                     if constexpr (DEC) wlo = L - a.window + 1 > 0 ? L - a.window + 1 : 0;
                     rg[0] = rbase + t + (int)(P / E);
-                    rg[1] = rbase + t + (int)((P + wlo) / E);
-                    rg[2] = rbase + t + (int)((P + L) / E);
+                    rg[2] = rbase + t + (int)((P + nk - 1) / E);
+                    // no segment holds window keys when the window is the new key alone
+                    rg[1] = wlo <= nk - 1 ? rbase + t + (int)((P + wlo) / E) : rg[2] + 1;
                 }
             }
         }
@@ -212,18 +219,19 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
         const int bl = __popcll(m) - 1;
         it.b = b0 + bl;
         const int L = __builtin_amdgcn_readlane(Lv, bl);
-        // the key's place among the sequence's S * (L + 1) keys (below 2^32:
+        // the key's place among the sequence's S * (L + KX) keys (below 2^32:
         // the launchers check S * cap)
         const uint32_t off = (uint32_t)(at - readlane64(excl, bl));
-        const int j = (int)(off / (uint32_t)(L + 1));
+        const int j = (int)(off / (uint32_t)(L + KX));
         // (g only addresses the cache: a vector division, so that no scalar
         // reciprocal of hblocks is held across the loop)
         int hbv = hblocks;
         asm volatile("" : "+v"(hbv));
         it.g = (int)((unsigned)j / (unsigned)hbv);
         it.h0 = j * hg;                   // = g * G + (j - g * hblocks) * hg
-        it.lo = (int)(off - (uint32_t)j * (uint32_t)(L + 1));
-        it.hi = run - rel > L - it.lo ? L : it.lo + (run - rel) - 1;
+        it.lo = (int)(off - (uint32_t)j * (uint32_t)(L + KX));
+        const int last = L + KX - 1;      // the stream's last key
+        it.hi = run - rel > last - it.lo ? last : it.lo + (run - rel) - 1;
         it.len = it.hi - it.lo + 1;
         it.nst = (it.hi - it.lo) / SK + 1;
         it.id = rbase + bl * S + j + (int)blockIdx.x;
@@ -528,29 +536,6 @@ __global__ __launch_bounds__(256) void xattn_lds_kernel(PT a, int b0, int nb, in
     }
 }
 
-// Decode: the new base token's K/V rows into slot L = cache_len[b] of each
-// KV head's cache stream (bit-exact copies), one workgroup per sequence.  A
-// length outside [0, max_len] writes nothing (the host guarantees
-// max_len + 1 <= cap, so slot L is inside the cache).
-template <int D>
-__global__ __launch_bounds__(256) void decode_append_kernel(DecodeParams p)
-{
-    const int b = blockIdx.x;
-    const int64_t L = p.cache_len[b];
-    if (L < 0 || L > p.max_len) return;
-    constexpr int UPR = D / 8;                  // 16-byte units per row
-    const int units = p.Hkv * UPR;
-    for (int u = threadIdx.x; u < 2 * units; u += blockDim.x) {
-        const bool isv = u >= units;
-        const int uu = isv ? u - units : u;
-        const int g = uu / UPR, c = uu - g * UPR;
-        const int64_t row = (int64_t)b * p.Hkv + g;
-        const uint4* src = (const uint4*)((const uint16_t*)(isv ? p.v_new : p.k_new) + row * D) + c;
-        uint4* dst = (uint4*)((uint16_t*)(isv ? p.v_cache : p.k_cache) + (row * p.cap + L) * D) + c;
-        *dst = *src;
-    }
-}
-
 // Compute units of the current device (one persistent workgroup each),
 // looked up once per device.
 int cu_count()
@@ -624,12 +609,7 @@ hipError_t launch_decode_lds(const DecodeParams& p, hipStream_t st)
         (int64_t)S * p.cap > UINT32_MAX || xattn_lds_records(p.B, S) >= INT32_MAX ||
         !lds_grid((int64_t)nb_max * S * (p.max_len + 1)))
         return hipErrorInvalidValue;
-    // the new token's K/V into slot L first: the streaming kernel reads
-    // every key of [0, L] from the cache
-    if (p.D == 64) hipLaunchKernelGGL((decode_append_kernel<64>), dim3(p.B), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((decode_append_kernel<128>), dim3(p.B), dim3(256), 0, st, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
     const int64_t region = xattn_lds_region(p.B, S);
     PosBlock unused{};
     for (int b0 = 0; b0 < p.B; b0 += kPosPerLaunch) {
@@ -646,6 +626,7 @@ hipError_t launch_decode_lds(const DecodeParams& p, hipStream_t st)
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    // the merge adds the new token's key L and appends it to the cache
     return launch_lds_merge(p, st);
 }
 

@@ -89,19 +89,20 @@ def decode_split_of(B, Hq, Hkv, d, hint):
 
 def lds_run_starts(lens, S, hint):
     """Where the LDS-streamed decode kernel's runs start, per (sequence,
-    stream): the keys of a step with cache lengths `lens` (the new keys
-    included) in (sequence, stream, key) order, cut into equal runs of
-    E = max(ceil(total / grid), 256) keys, grid = min(CUs, 512,
-    ceil(B * S * (hint + 1) / 256)).  Returns {(b, stream): [keys]}."""
+    stream): the history keys 0 .. L - 1 of a step with cache lengths `lens`
+    (the new key L is added by the merge) in (sequence, stream, key) order,
+    cut into equal runs of E = max(ceil(total / grid), 256) keys, grid =
+    min(CUs, 512, ceil(B * S * (hint + 1) / 256)).  Returns {(b, stream):
+    [keys]}."""
     B = len(lens)
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
     grid = max(1, min(ncu, 512, -(-B * S * (hint + 1) // 256)))
-    total = sum((L + 1) * S for L in lens)
+    total = sum(L * S for L in lens)
     E = max(-(-total // grid), 256)
     starts, P = {}, 0
     for b, L in enumerate(lens):
         for j in range(S):
-            n = L + 1
+            n = L
             first = -(-P // E) * E                      # the first run start at or after P
             starts[(b, j)] = list(range(first - P, n, E))
             P += n
@@ -323,12 +324,12 @@ def lds_lens(B, base=65536):
 
 
 def straddling_windows(lens, S, hint, w):
-    """(b, stream) pairs whose window [L - w + 1, L] holds a run start past
-    its first key at the first step."""
+    """(b, stream) pairs whose window's history keys [L - w + 1, L - 1] hold
+    a run start past their first key at the first step."""
     out = []
     for (b, j), ks in lds_run_starts(lens, S, hint).items():
         lo = max(0, lens[b] - w + 1)
-        if any(lo < k <= lens[b] for k in ks):
+        if any(lo < k <= lens[b] - 1 for k in ks):
             out.append((b, j))
     return out
 
