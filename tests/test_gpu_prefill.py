@@ -223,11 +223,13 @@ def test_fused_copy_positions_at_segment_edges():
     run_case(cfg, 5000, seed=18, out_pos=[0, 31, 32, 159, 160, 161, 2501, 4999])
 
 
-def test_fused_more_sequences_than_one_launch():
-    """67 sequences: the fused kernel takes copy positions 64 per launch."""
-    cfg = make_cfg(67, 4, 1, 64, 16, torch.bfloat16)
+@pytest.mark.parametrize("Hq,Hkv", [(4, 1), (2, 1), (2, 2)], ids=["G4", "G2", "G1"])
+def test_fused_more_sequences_than_one_launch(Hq, Hkv):
+    """67 sequences: the fused kernel takes copy positions 64 per launch
+    (blocks of 4, 2 and 1 heads)."""
+    cfg = make_cfg(67, Hq, Hkv, 64, 16, torch.bfloat16)
     g = torch.Generator().manual_seed(19)
-    run_case(cfg, 70, seed=19, out_pos=torch.randint(0, 70, (67,), generator=g).tolist())
+    run_case(cfg, 70, seed=19 + Hq + Hkv, out_pos=torch.randint(0, 70, (67,), generator=g).tolist())
 
 
 def test_explicit_softmax_scale():
