@@ -32,7 +32,7 @@
 // Workgroup ids are remapped so each XCD walks a contiguous run of tiles
 // and the 127-key halo of the next tile is still in its L2.
 //
-// fp32 kernel: a VALU variant (8 lanes per row, 32 rows of one head per
+// fp32 kernel: a VALU variant (16 lanes per row, 16 rows of one head per
 // workgroup) for fp32 storage, where the tolerance is 1e-4.
 
 #include "device.h"
@@ -276,32 +276,34 @@ __global__ __launch_bounds__(256, 2) void swa_bf16_kernel(SwaParams a, int n_til
 // ------------------------------------------------------------------- fp32
 
 // fp32 storage (tolerance 1e-4): fp32 FMAs on the VALU.  A workgroup takes
-// 32 rows of one query head; each row is served by 8 lanes, lane e of the
-// row holding head dims [D/8 e, D/8 (e+1)) of the query and of the output
-// accumulator.  The key band [q0 - w + 1, q0 + 31] streams through LDS in
+// 16 rows of one query head; each row is served by 16 lanes, lane e of the
+// row holding head dims [D/16 e, D/16 (e+1)) of the query and of the output
+// accumulator.  The key band [q0 - w + 1, q0 + 15] streams through LDS in
 // 32-key blocks (the next block's rows are loaded into registers while the
-// current one is used); per key the 8 lanes' partial dot products meet in a
-// DPP reduction, so every lane of the row has the score and updates its
-// slice of the online softmax state.  The workgroup of the KV group's first
-// query head writes the K/V rows it owns ([q0, q0 + 32)) to the cache.
+// current one is used); per key the 16 lanes' partial dot products meet in
+// a DPP reduction, so every lane of the row has the score; the block's
+// scores are taken first and the online softmax advances once per block.
+// The workgroup of the KV group's first query head writes the K/V rows it
+// owns ([q0, q0 + 16)) to the cache.
 template <int D>
 __global__ __launch_bounds__(256) void swa_f32_kernel(SwaParams a, int n_tiles)
 {
     constexpr int KB = 32;                  // keys per LDS block
-    constexpr int DL = D / 8;               // head dims per lane
+    constexpr int LPR = 16, RW = 256 / LPR; // lanes per row, rows per workgroup
+    constexpr int DL = D / LPR;             // head dims per lane
     constexpr int F4 = KB * D / 4 / 256;    // float4 of a K (or V) block per thread
     __shared__ __align__(16) float Ks[KB][D];
     __shared__ __align__(16) float Vs[KB][D];
 
     const int tid = threadIdx.x;
-    const int row = tid >> 3, e = tid & 7;
+    const int row = tid / LPR, e = tid % LPR;
     const int tile = blockIdx.x % n_tiles;
     const int h = (blockIdx.x / n_tiles) % a.Hq;
     const int b = blockIdx.x / n_tiles / a.Hq;
     const int G = a.Hq / a.Hkv, g = h / G;
     const int64_t T = a.T;
     const int W = a.window;
-    const int64_t q0 = (int64_t)tile * 32, t = q0 + row;
+    const int64_t q0 = (int64_t)tile * RW, t = q0 + row;
     const float* kg = (const float*)a.k;
     const float* vg = (const float*)a.v;
 
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(256) void swa_f32_kernel(SwaParams a, int n_tiles)
     float m_run = kNegBig, l_run = 0.f;
 
     const int64_t klo = q0 - W + 1 > 0 ? q0 - W + 1 : 0;
-    const int64_t khi = (q0 + 32 < T ? q0 + 32 : T) - 1;
+    const int64_t khi = (q0 + RW < T ? q0 + RW : T) - 1;
     const bool writer = (h % G) == 0;
     const int64_t kb0 = klo & ~(int64_t)(KB - 1);
     // rows of one block: thread tid holds float4 i of K and V, i = tid + 256 f
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(256) void swa_f32_kernel(SwaParams a, int n_tiles)
             *(float4*)&Ks[kk][4 * d4] = kr[f];
             *(float4*)&Vs[kk][4 * d4] = vr[f];
             const int64_t j = kbase + kk;
-            if (writer && j >= q0 && j < T) {
+            if (writer && j >= q0 && j <= khi) {
                 const int64_t coff = (((int64_t)b * a.Hkv + g) * a.cap + j) * D + 4 * d4;
                 *(float4*)((float*)a.k_cache + coff) = kr[f];
                 *(float4*)((float*)a.v_cache + coff) = vr[f];
@@ -354,22 +356,48 @@ __global__ __launch_bounds__(256) void swa_f32_kernel(SwaParams a, int n_tiles)
         }
         __syncthreads();
         if (kbase + KB <= khi) load_block(kbase + KB);
-        // keys of this block in the row's window [t - w + 1, t]
-        const int64_t lo = t - W + 1 > kbase ? t - W + 1 : kbase;
-        const int64_t hi = t < kbase + KB - 1 ? t : kbase + KB - 1;
-        for (int64_t j = kbase; j < kbase + KB; ++j) {
+        // keys of this block in the row's window [t - w + 1, t]: the block's
+        // scores first (independent of one another), one maximum and one
+        // rescale per block, then the weighted values into two interleaved
+        // accumulator sets (short dependency chains)
+        const int lo = (int)((t - W + 1 > kbase ? t - W + 1 : kbase) - kbase);
+        const int hi = (int)((t < kbase + KB - 1 ? t : kbase + KB - 1) - kbase);
+        float sc[KB];
+        float mb = kNegBig;
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
             float sp = 0.f;
 #pragma unroll
-            for (int d = 0; d < DL; ++d) sp += qh[d] * Ks[j - kbase][DL * e + d];
-            const float s = group_sum<8>(sp);
-            if (j < lo || j > hi || t >= T) continue;   // uniform over the row's 8 lanes
-            const float m_new = fmaxf(m_run, s);
+            for (int d = 0; d < DL; ++d) sp += qh[d] * Ks[j][DL * e + d];
+            const float sj = group_sum<LPR>(sp);
+            const bool ok = j >= lo && j <= hi && t < T;   // uniform over the row's lanes
+            sc[j] = ok ? sj : -INFINITY;
+            mb = fmaxf(mb, sc[j]);
+        }
+        if (mb > kNegBig) {
+            const float m_new = fmaxf(m_run, mb);
             const float corr = fast_exp2(m_run - m_new);
-            const float p = fast_exp2(s - m_new);
             m_run = m_new;
-            l_run = l_run * corr + p;
+            float l0 = l_run * corr, l1 = 0.f, acc1[DL];
 #pragma unroll
-            for (int d = 0; d < DL; ++d) acc[d] = acc[d] * corr + p * Vs[j - kbase][DL * e + d];
+            for (int d = 0; d < DL; ++d) {
+                acc[d] *= corr;
+                acc1[d] = 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < KB; j += 2) {
+                const float p0 = fast_exp2(sc[j] - m_new), p1 = fast_exp2(sc[j + 1] - m_new);
+                l0 += p0;
+                l1 += p1;
+#pragma unroll
+                for (int d = 0; d < DL; ++d) {
+                    acc[d] += p0 * Vs[j][DL * e + d];
+                    acc1[d] += p1 * Vs[j + 1][DL * e + d];
+                }
+            }
+            l_run = l0 + l1;
+#pragma unroll
+            for (int d = 0; d < DL; ++d) acc[d] += acc1[d];
         }
     }
     if (t < T) {
@@ -396,7 +424,7 @@ hipError_t launch_bf16(const SwaParams& p, hipStream_t s)
 template <int D>
 hipError_t launch_f32(const SwaParams& p, hipStream_t s)
 {
-    const int n_tiles = (int)((p.T + 31) / 32);
+    const int n_tiles = (int)((p.T + 15) / 16);             // 16 rows per workgroup
     const int64_t n_wg = (int64_t)p.B * p.Hq * n_tiles;
     hipLaunchKernelGGL((swa_f32_kernel<D>), dim3((unsigned)n_wg), dim3(256), 0, s, p, n_tiles);
     return hipGetLastError();
