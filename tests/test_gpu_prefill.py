@@ -162,6 +162,50 @@ def test_mask_probe_bit_exact():
     assert torch.equal(run.o_out.cpu().float(), torch.full((1, 4, d), 1 / 128))
 
 
+@pytest.mark.parametrize("Hq,Hkv,w", [(4, 4, 1), (4, 4, 3), (4, 2, 16), (4, 4, 128), (2, 1, 129), (4, 2, 300)],
+                         ids=["G1-w1", "G1-w3", "G2-w16", "G1-w128", "G2-w129", "G2-w300"])
+def test_fp32_moment_probe(Hq, Hkv, w):
+    """The fp32 path's mask placement.  alpha = beta = 0 gives every admissible
+    key the same weight; V rows [1, j, j^2, 0, ...] (j <= 299, so every sum
+    of the row's weighted values is an integer below 2^24, exact in fp32)
+    make each output the mean of 1, j and j^2 over the row's key set.  The
+    count n and the first index lo of that set then follow exactly after
+    rounding: n^2 = 12 (mean j^2 - mean j^2) + 1, lo = mean j - (n - 1) / 2.
+    Every base row's set must be [max(0, t - w + 1), t]; the copy at 157
+    must see [0, 157]."""
+    T, d = 300, 64
+    cfg = make_cfg(1, Hq, Hkv, d, w, torch.float32)
+    say("fp32 moment probe", cfg)
+    xc = inputs.prefill_inputs(T=T, seed=21, **cfg)
+    for key in ("alpha", "beta", "alpha_out", "beta_out"):
+        xc[key].zero_()
+    j = torch.arange(T, dtype=torch.float32)
+    xc["v"].zero_()
+    xc["v"][0, :, :, 0] = 1.0
+    xc["v"][0, :, :, 1] = j[:, None]
+    xc["v"][0, :, :, 2] = (j * j)[:, None]
+    xc["out_pos"] = [157]
+    run = Prefill(cfg, to_dev(xc))
+    run.run()
+    torch.cuda.synchronize()
+
+    def key_set(m):
+        m = m.double()
+        n = torch.round(torch.sqrt(12 * (m[..., 2] - m[..., 1] ** 2) + 1))
+        lo = torch.round(m[..., 1] - (n - 1) / 2)
+        return n, lo
+
+    o = run.o.cpu()[0]                                   # [T, Hq, d]
+    assert torch.allclose(o[..., 0], torch.ones_like(o[..., 0]), rtol=0, atol=1e-6)
+    n, lo = key_set(o)
+    t = torch.arange(T, dtype=torch.float64)[:, None].expand(T, Hq)
+    lo_exp = torch.clamp(t - w + 1, min=0)
+    assert torch.equal(lo, lo_exp), "first keys of the windows"
+    assert torch.equal(n, t - lo_exp + 1), "window sizes"
+    n_c, lo_c = key_set(run.o_out.cpu()[0])
+    assert torch.equal(n_c, torch.full((Hq,), 158.0, dtype=torch.float64)) and torch.equal(lo_c, torch.zeros(Hq, dtype=torch.float64))
+
+
 def test_base_stream_isolated_from_output_stream():
     """Perturbing q_out, alpha', beta' leaves the cache and o bit-identical."""
     cfg = make_cfg(2, 8, 2, 128, 128, torch.bfloat16)
