@@ -62,6 +62,8 @@ CASES = [
     (1, 4, 2, 64, 128, 1000),
     (1, 12, 2, 128, 128, 700),
     (2, 3, 3, 64, 129, 333),
+    (1, 4, 4, 128, 128, 40000),
+    (1, 8, 4, 64, 100, 20000),
     # groups of 1 and 3 past w = 129 (the generic kernel)
     (1, 4, 4, 128, 200, 700),
     (2, 6, 2, 128, 130, 500),
