@@ -38,7 +38,6 @@
 namespace orthros {
 namespace {
 
-constexpr int kSlots = 5;
 constexpr float kRescaleMargin = 8.0f;   // log2 units
 
 // 16x16x32 form: the window of a 32-row tile spans 10 blocks of 16 keys =

@@ -119,15 +119,18 @@ def test_decode_short_kernel_edge(keys):
 @pytest.mark.parametrize("B,Hq,len_lo,len_hi,steps,w", [(32, 32, 66000, 70000, 2, 128),
                                                       (80, 32, 20000, 24000, 1, 128),
                                                       (32, 32, 66000, 70000, 1, 5000),
-                                                      (16, 64, 66000, 70000, 1, 128)],
+                                                      (16, 64, 66000, 70000, 1, 128),
+                                                      (80, 16, 20000, 24000, 1, 128),
+                                                      (80, 8, 20000, 24000, 2, 300)],
                          ids=["B32-70K", "B80-24K-two-launches", "B32-70K-window-5000",
-                              "B16-70K-G8-two-head-blocks"])
+                              "B16-70K-G8-two-head-blocks", "B80-24K-G2-two-launches",
+                              "B80-24K-MHA-two-launches-w300"])
 def test_decode_lds_kernel_long_histories(B, Hq, len_lo, len_hi, steps, w):
     """bf16, 8 KV heads, d128: 32 sequences (32 query heads) with histories
     up to 70K keys, 16 with 64 query heads (two 4-head blocks per KV head),
-    or 80 (two launches of 64 and 16 sequences) up to 24K -- large enough
-    that the step runs on the LDS-streamed kernel (equal runs of the step's
-    keys per workgroup).  Lengths include 0 and the edges of a 128-key
+    or 80 (two launches of 64 and 16 sequences) up to 24K, with groups of 4,
+    2 (2-head streams) and 1 -- large enough that the step runs on the
+    LDS-streamed kernel (equal runs of the step's keys per workgroup).  Lengths include 0 and the edges of a 128-key
     stage; windows of 128 and 5000 keys.  Unused cache slots hold the NaN
     sentinel, and one sequence's length is past the hint.  Every step
     against the oracle, caches and lengths in full."""
@@ -157,7 +160,8 @@ def test_decode_lds_kernel_long_histories(B, Hq, len_lo, len_hi, steps, w):
     # streams): counters, lengths, 3 record ids per stream, then 2 x 4
     # records of d + 32 floats per id (every stream of a launch of up to 64
     # sequences, plus 512)
-    S = Hkv * (Hq // Hkv // 4)
+    G = Hq // Hkv
+    S = Hkv * (G // (4 if G % 4 == 0 else 2 if G % 2 == 0 else 1))
     assert (max_hint + 1) * B * S >= 12 << 20
     len_bytes = -(-B * 4 // 256) * 256         # the per-sequence lengths, 256-byte aligned
     cnt_bytes = -(-B * (S + 1) * 4 // 256) * 256     # arrival counters
