@@ -22,9 +22,9 @@ of its row, compared bit for bit (tests/probe_util.py).  Kernels covered:
     token's window straddling run boundaries at w = 128 and spanning several
     runs at w = 4096 and 5000, and the copy over ~64K-key histories with
     marked keys on both sides of every run boundary;
-  decode, one-launch short-history kernel (groups of 2, 4 and 8, d 128
-    and 64, windows 1, 128 and 300), and the LDS-streamed kernel past
-    4096 keys with groups of 2 and d = 64.
+  decode, one-launch short-history kernel (groups of 1, 2, 3, 4 and 8,
+    d 128 and 64, windows 1, 128 and 300), and the LDS-streamed kernel past
+    4096 keys with groups of 1, 2 and 3 and d = 64.
 (MI355X only.)"""
 import pytest
 import torch
@@ -373,9 +373,11 @@ def test_probe_decode_lds_copy_marked_run_edges():
                           (4, 2, 128, 128, 9000, 65535, True), (2, 2, 64, 128, 9000, 65535, True),
                           (8, 2, 64, 128, 9000, None, True), (4, 1, 128, 128, 4095, None, False),
                           (4, 1, 64, 300, 4095, None, False), (2, 1, 128, 1, 4095, None, False),
-                          (1, 1, 128, 128, 4095, None, False)],
+                          (1, 1, 128, 128, 4095, None, False), (6, 2, 128, 128, 4095, None, False),
+                          (6, 2, 128, 300, 9000, 65535, True)],
                          ids=["G4", "G4-w1", "G4-d64-w300", "G2", "G8", "G2-lane", "G2-lds", "MHA-d64-lds",
-                              "G4-d64-lds", "G4-Hkv1", "G4-d64-w300-Hkv1", "G2-w1-Hkv1", "MHA-Hkv1"])
+                              "G4-d64-lds", "G4-Hkv1", "G4-d64-w300-Hkv1", "G2-w1-Hkv1", "MHA-Hkv1", "G3",
+                              "G3-w300-lds"])
 def test_probe_decode_short_kernel(Hq, Hkv, d, w, longest, hint, lds):
     """Short histories: lengths 0, 1, around the window, and on the edges of
     128- and 256-key chunks; three steps.  Up to 4096 keys the step is one
